@@ -1,0 +1,303 @@
+"""Plain, slow fp64 CPU oracle of the Mixture-of-Experts FFN layer.
+
+TEST INFRASTRUCTURE.  Only the test suite, the smoke check of the package
+entry module and the CPU-baseline leg of the benchmark may import this
+module.  It shares no code with the HIP path and imports nothing from it.
+
+What the layer computes (Gemma-4-26B-A4B optimisation report, section 1 model
+overview: every decoder block has an MoE with 128 experts, top-8 routing,
+expert intermediate 704 and a GEGLU activation; section 5 names the fused
+router op that does top-k + softmax over the router logits; section 6.1
+describes the dispatch of tokens grouped by expert and the weighted combine
+of the expert outputs; Gemma-4-26B-A4B-NVFP4 Ascend verification report,
+section 2.1 model architecture parameters: hidden 2816, activation
+gelu_pytorch_tanh):
+
+  O1  decode every bf16 input exactly to fp64
+  O2  router logits L = x W_r^T (+ b)
+  O3  per token, the k experts with the largest logits; ties go to the lower
+      expert index; slots ordered by (logit descending, index ascending)
+  O4  routing weights: softmax over the k selected logits (renormalised top-k)
+  O5  per-expert counts and their exclusive prefix sum (offsets)
+  O6  the expert-grouped order of the flat assignments a = t*k + j, stable in t
+  O7  per expert: G = X W_gu^T, h = gelu_tanh(G[:, :I]) * G[:, I:], Y = h W_d^T
+  O8  out[t] = sum_j w[t, j] * Y[inv[t*k + j]]
+  O9  MXFP4 expert weights decoded to fp64 before O7
+
+Readings of points the pages leave open (renormalised top-k softmax,
+lowest-index tie-break, gate = first I rows of the concatenated gate/up
+weight, the tanh GELU constants, no capacity limit) are listed with the
+design notes of the repository.
+
+Parity status: O2-O8 are pinned by the dense brute force (`dense_forward`) and
+by closed-form special cases in the CPU test suite; O9 is pinned by the E2M1
+table of the OCP Microscaling Formats v1.0 specification.  Against the real
+Gemma-4 layer parity is unpinned: the pages print no activations or weights.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "bf16_to_f64", "mxfp4_to_f64", "router_logits", "topk_softmax",
+    "counts_offsets", "permutation", "gelu_tanh", "gateup_geglu",
+    "down_proj", "combine", "expert_weights", "forward", "forward_tokens",
+    "dense_forward", "routing_margin",
+]
+
+
+# ---------------------------------------------------------------- O1 / O9
+def bf16_to_f64(bits) -> np.ndarray:
+    """Exact value of bfloat16 bit patterns (uint16) as float64 (O1)."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+# FP4 E2M1 element values by code (OCP Microscaling Formats v1.0): bit 3 is
+# the sign, bits 2..1 the exponent (bias 1), bit 0 the mantissa; code 1 is
+# the subnormal 0.5.
+_E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0,
+                  -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0], dtype=np.float64)
+
+
+def mxfp4_to_f64(packed, scales) -> np.ndarray:
+    """Decode MXFP4 weights to fp64 (O9).
+
+    packed [..., K/2] holds two E2M1 codes per byte, the even K index in the
+    low nibble; scales [..., K/32] holds one E8M0 byte per 32 consecutive K
+    elements, meaning 2^(byte - 127).  MXFP4 checkpoints of this model are
+    named by the vLLM-Ascend Gemma4 tutorial (section 3.1 model weight); the
+    element and scale encodings are those of the OCP MX v1.0 specification.
+    """
+    packed = np.asarray(packed, dtype=np.uint8)
+    lo = packed & 0x0F
+    hi = packed >> 4
+    codes = np.stack([lo, hi], axis=-1).reshape(*packed.shape[:-1], packed.shape[-1] * 2)
+    vals = _E2M1[codes]
+    s = np.asarray(scales, dtype=np.int64)
+    if np.any(s == 255):
+        raise ValueError("E8M0 byte 0xFF is NaN and not a valid scale")
+    factor = np.ldexp(1.0, s - 127)                     # [..., K/32]
+    K = codes.shape[-1]
+    vals = vals.reshape(*codes.shape[:-1], K // 32, 32) * factor[..., None]
+    return vals.reshape(*codes.shape[:-1], K)
+
+
+def expert_weights(inp, e: int):
+    """fp64 gate/up [2I, H] and down [H, I] weights of expert e."""
+    if inp.shape.mxfp4:
+        wgu = mxfp4_to_f64(inp.w_gate_up[e], inp.gu_scales[e])
+        wd = mxfp4_to_f64(inp.w_down[e], inp.d_scales[e])
+    else:
+        wgu = bf16_to_f64(inp.w_gate_up[e])
+        wd = bf16_to_f64(inp.w_down[e])
+    return wgu, wd
+
+
+# ---------------------------------------------------------------- O2
+def router_logits(x64: np.ndarray, wr64: np.ndarray, bias=None) -> np.ndarray:
+    """L[t, e] = sum_h x[t, h] W_r[e, h] (+ b[e]) in fp64 (O2).
+
+    The router linear layer ahead of the fused gating op (optimisation report,
+    section 5, MoE Router row)."""
+    L = x64 @ wr64.T
+    if bias is not None:
+        L = L + np.asarray(bias, dtype=np.float64)[None, :]
+    return L
+
+
+# ---------------------------------------------------------------- O3 / O4
+def topk_softmax(L: np.ndarray, k: int):
+    """Top-k selection and renormalised softmax weights (O3, O4).
+
+    For each token the experts are ordered by the key (-L[t, e], e): largest
+    logit first, the lower expert index first among equal logits.  The first
+    k are the selection, in slot order.  w[t, j] = exp(L_j - L_0) / sum over
+    the k selected of exp(L_i - L_0), which equals the softmax over all
+    experts renormalised over the selected ones (optimisation report, section
+    5: the router is fused as a gating top-k softmax op).
+
+    Returns ids int32 [T, k], w float64 [T, k]."""
+    L = np.asarray(L, dtype=np.float64)
+    T, E = L.shape
+    ids = np.empty((T, k), dtype=np.int32)
+    w = np.empty((T, k), dtype=np.float64)
+    idx = np.arange(E)
+    for t in range(T):
+        order = np.lexsort((idx, -L[t]))     # primary -L, then index
+        sel = order[:k]
+        ids[t] = sel
+        z = L[t, sel] - L[t, sel[0]]
+        ez = np.exp(z)
+        w[t] = ez / ez.sum()
+    return ids, w
+
+
+def routing_margin(L: np.ndarray, k: int) -> np.ndarray:
+    """Per token, the gap between the k-th and (k+1)-th largest logit
+    (infinite when k equals the expert count)."""
+    L = np.asarray(L, dtype=np.float64)
+    if k >= L.shape[1]:
+        return np.full(L.shape[0], np.inf)
+    s = -np.sort(-L, axis=1)
+    return s[:, k - 1] - s[:, k]
+
+
+# ---------------------------------------------------------------- O5 / O6
+def counts_offsets(ids: np.ndarray, E: int):
+    """counts[e] = number of (t, j) with ids[t, j] == e; offsets = exclusive
+    prefix sum with offsets[E] = T*k (O5).  These are the data-dependent split
+    sizes of the dispatch (optimisation report, section 6.1)."""
+    flat = np.asarray(ids).reshape(-1)
+    counts = np.zeros(E, dtype=np.int64)
+    for e in flat:
+        counts[int(e)] += 1
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    for e in range(E):
+        offsets[e + 1] = offsets[e] + counts[e]
+    return counts.astype(np.int32), offsets.astype(np.int32)
+
+
+def permutation(ids: np.ndarray):
+    """Expert-grouped order of the flat assignments (O6).
+
+    sorted_ids[p] = a = t*k + j, ordered by (ids[t, j], t); a token never
+    picks an expert twice, so the order is unique.  inv[a] = p."""
+    ids = np.asarray(ids)
+    T, k = ids.shape
+    flat = ids.reshape(-1)
+    tok = np.arange(T * k) // k
+    sorted_ids = np.lexsort((tok, flat)).astype(np.int32)
+    inv = np.empty(T * k, dtype=np.int32)
+    inv[sorted_ids] = np.arange(T * k, dtype=np.int32)
+    return sorted_ids, inv
+
+
+# ---------------------------------------------------------------- O7
+_SQRT_2_OVER_PI = math.sqrt(2.0 / math.pi)
+
+
+def gelu_tanh(z):
+    """gelu_pytorch_tanh (verification report, section 2.1): the tanh form of
+    the Gaussian error linear unit of Hendrycks and Gimpel,
+    0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3)))."""
+    z = np.asarray(z, dtype=np.float64)
+    return 0.5 * z * (1.0 + np.tanh(_SQRT_2_OVER_PI * (z + 0.044715 * z ** 3)))
+
+
+def gateup_geglu(X: np.ndarray, wgu64: np.ndarray) -> np.ndarray:
+    """h = gelu_tanh(X W_gate^T) * (X W_up^T) for one expert (O7, first half).
+
+    wgu64 is [2I, H]: rows 0..I-1 the gate, rows I..2I-1 the up projection
+    (the GEGLU of the optimisation report, section 1)."""
+    I = wgu64.shape[0] // 2
+    G = X @ wgu64.T
+    return gelu_tanh(G[:, :I]) * G[:, I:]
+
+
+def down_proj(h: np.ndarray, wd64: np.ndarray) -> np.ndarray:
+    """Y = h W_d^T for one expert, W_d [H, I] (O7, second half)."""
+    return h @ wd64.T
+
+
+# ---------------------------------------------------------------- O8
+def combine(Y: np.ndarray, inv: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """out[t] = sum_j w[t, j] Y[inv[t*k + j]] (O8): the weighted sum of each
+    token's expert outputs (the local-expert sum before the all-reduce of the
+    decode path, optimisation report, section 6.1)."""
+    T, k = w.shape
+    out = np.zeros((T, Y.shape[1]), dtype=np.float64)
+    for t in range(T):
+        for j in range(k):
+            out[t] += w[t, j] * Y[inv[t * k + j]]
+    return out
+
+
+# ---------------------------------------------------------------- whole layer
+def forward(inp, logits_fp32: np.ndarray | None = None) -> dict:
+    """The routed layer, step by step (O1-O9).
+
+    If logits_fp32 is given, routing uses those float32 values (widened
+    exactly) instead of O2; this is how the routing decision is taken in the
+    same precision as a float32 kernel."""
+    s = inp.shape
+    T, H, E, k, I = s.T, s.H, s.E, s.k, s.I
+    x64 = bf16_to_f64(inp.x)
+    L = router_logits(x64, bf16_to_f64(inp.w_router), inp.router_bias)
+    Lr = L if logits_fp32 is None else np.asarray(logits_fp32, dtype=np.float32).astype(np.float64)
+    ids, w = topk_softmax(Lr, k)
+    counts, offsets = counts_offsets(ids, E)
+    sorted_ids, inv = permutation(ids)
+    Y = np.zeros((T * k, H), dtype=np.float64)
+    Hh = np.zeros((T * k, I), dtype=np.float64)
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue                      # empty expert: its weights are never read
+        rows = sorted_ids[lo:hi]
+        X = x64[rows // k]
+        wgu, wd = expert_weights(inp, e)
+        h = gateup_geglu(X, wgu)
+        Hh[lo:hi] = h
+        Y[lo:hi] = down_proj(h, wd)
+    out = combine(Y, inv, w)
+    return dict(logits=L, route_logits=Lr, ids=ids, w=w, counts=counts,
+                offsets=offsets, sorted_ids=sorted_ids, inv=inv, h=Hh, y=Y,
+                out=out, margin=routing_margin(Lr, k))
+
+
+def forward_tokens(inp, tokens) -> dict:
+    """The layer evaluated one token at a time for the listed tokens (the
+    output of a token depends only on its own row).  Used to sample the
+    output of large problems."""
+    s = inp.shape
+    k = s.k
+    tokens = np.asarray(tokens, dtype=np.int64)
+    x64 = bf16_to_f64(inp.x[tokens])
+    L = router_logits(x64, bf16_to_f64(inp.w_router), inp.router_bias)
+    ids, w = topk_softmax(L, k)
+    out = np.zeros((len(tokens), s.H), dtype=np.float64)
+    cache = {}
+    for i in range(len(tokens)):
+        for j in range(k):
+            e = int(ids[i, j])
+            if e not in cache:
+                cache[e] = expert_weights(inp, e)
+            wgu, wd = cache[e]
+            h = gateup_geglu(x64[i:i + 1], wgu)
+            out[i] += w[i, j] * down_proj(h, wd)[0]
+    return dict(logits=L, ids=ids, w=w, out=out, margin=routing_margin(L, k))
+
+
+def dense_forward(inp) -> np.ndarray:
+    """Brute force: every expert on every token, masked to the top-k.
+
+    mask[t, e] = 1 iff fewer than k experts e' beat e, where e' beats e when
+    L[t, e'] > L[t, e], or L[t, e'] == L[t, e] and e' < e (a rank count that
+    does not sort).  out[t] = sum_e mask * p_hat * F_e(x_t), p_hat the softmax
+    over the masked set.  Only for small problems."""
+    s = inp.shape
+    T, E, k = s.T, s.E, s.k
+    x64 = bf16_to_f64(inp.x)
+    L = router_logits(x64, bf16_to_f64(inp.w_router), inp.router_bias)
+    mask = np.zeros((T, E), dtype=bool)
+    for t in range(T):
+        for e in range(E):
+            beats = 0
+            for e2 in range(E):
+                if L[t, e2] > L[t, e] or (L[t, e2] == L[t, e] and e2 < e):
+                    beats += 1
+            mask[t, e] = beats < k
+    out = np.zeros((T, s.H), dtype=np.float64)
+    for t in range(T):
+        m = max(L[t, e] for e in range(E) if mask[t, e])
+        den = sum(math.exp(L[t, e] - m) for e in range(E) if mask[t, e])
+        for e in range(E):
+            if not mask[t, e]:
+                continue
+            wgu, wd = expert_weights(inp, e)
+            F = down_proj(gateup_geglu(x64[t:t + 1], wgu), wd)[0]
+            out[t] += (math.exp(L[t, e] - m) / den) * F
+    return out

@@ -1,0 +1,24 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: full-size case, minutes of CPU work")
+
+
+@pytest.fixture(scope="session")
+def gpu():
+    """The HIP library bound to cuda:0; fails (does not skip) without a GPU."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test run without a visible GPU")
+    import mixture_experts_router_amd as moe
+    moe.load()
+    return moe

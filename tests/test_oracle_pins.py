@@ -1,0 +1,323 @@
+"""Pins of the fp64 oracle against facts it does not compute itself: a dense
+brute force that never sorts, closed forms, special cases that reduce to
+textbook routines, library implementations of the same functions and the
+published E2M1 table.  CPU only."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from hypothesis import given, settings, strategies as st, HealthCheck
+
+import moe_inputs as mi
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _inputs(T, H, E, k, I, seed=0, skew=False):
+    return mi.make(mi.Shape(T=T, H=H, E=E, k=k, I=I, skew=skew), seed=seed)
+
+
+def _rel(a, b):
+    return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
+
+
+# ------------------------------------------------------------------ shape
+def test_golden_layer_shape_matches_configs():
+    g = json.load(open(os.path.join(GOLDEN, "gemma4_moe_layer.json")))
+    for name in ("decode", "prefill", "skew", "mxfp4"):
+        s = mi.CONFIGS[name]
+        assert (s.H, s.E, s.k, s.I) == (g["hidden_size"], g["num_experts"],
+                                        g["top_k"], g["moe_intermediate_size"])
+    assert mi.CONFIGS["prefill"].T == g["prefill_batch"] * g["prefill_seq_len"]
+    assert mi.CONFIGS["decode"].T == g["decode_batch"]
+    assert g["activation"] == "gelu_pytorch_tanh"
+
+
+# ------------------------------------------------------------------ brute force
+def test_dense_brute_force_tiny_config():
+    inp = mi.make("tiny")
+    r = oracle.forward(inp)
+    d = oracle.dense_forward(inp)
+    assert _rel(r["out"], d) <= 1e-12
+
+
+def test_dense_brute_force_skewed_bias():
+    inp = _inputs(24, 64, 12, 3, 32, seed=3, skew=True)
+    r = oracle.forward(inp)
+    assert _rel(r["out"], oracle.dense_forward(inp)) <= 1e-12
+
+
+@settings(max_examples=12, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(T=st.integers(1, 40), E=st.integers(1, 16), kf=st.floats(0, 1),
+       H=st.sampled_from([32, 64, 128]), I=st.sampled_from([32, 64, 128]),
+       seed=st.integers(0, 1000))
+def test_dense_brute_force_random_shapes(T, E, kf, H, I, seed):
+    k = 1 + int(kf * (E - 1))
+    inp = _inputs(T, H, E, k, I, seed=seed)
+    r = oracle.forward(inp)
+    assert _rel(r["out"], oracle.dense_forward(inp)) <= 1e-12
+
+
+# ------------------------------------------------------------------ top-k
+def _rank_count_topk(L, k):
+    """Selection by counting, per expert, the experts that beat it."""
+    T, E = L.shape
+    sel = []
+    for t in range(T):
+        chosen = []
+        for e in range(E):
+            beats = sum(1 for e2 in range(E)
+                        if L[t, e2] > L[t, e] or (L[t, e2] == L[t, e] and e2 < e))
+            if beats < k:
+                chosen.append((beats, e))
+        sel.append([e for _, e in sorted(chosen)])
+    return np.array(sel)
+
+
+def test_topk_matches_rank_count_with_many_ties():
+    rng = np.random.default_rng(5)
+    L = rng.integers(-3, 4, size=(50, 16)).astype(np.float64)   # heavy ties
+    for k in (1, 3, 8, 16):
+        ids, w = oracle.topk_softmax(L, k)
+        assert (ids == _rank_count_topk(L, k)).all()
+
+
+def test_all_equal_logits_pick_lowest_indices_with_equal_weights():
+    L = np.full((4, 128), 0.37)
+    ids, w = oracle.topk_softmax(L, 8)
+    assert (ids == np.arange(8)).all()
+    assert (w == 1.0 / 8).all()
+
+
+def test_negative_zero_ties_with_zero():
+    L = np.array([[-0.0, 0.0, -1.0]])
+    ids, _ = oracle.topk_softmax(L, 1)
+    assert ids[0, 0] == 0
+
+
+def test_k_equals_E_gives_full_softmax():
+    rng = np.random.default_rng(1)
+    L = rng.standard_normal((10, 12))
+    ids, w = oracle.topk_softmax(L, 12)
+    full = torch.softmax(torch.from_numpy(L), dim=1).numpy()
+    for t in range(10):
+        assert np.allclose(w[t], full[t, ids[t]], rtol=0, atol=1e-15)
+        assert (np.diff(L[t, ids[t]]) <= 0).all()
+
+
+def test_topk_weights_are_renormalised_full_softmax():
+    rng = np.random.default_rng(2)
+    L = rng.standard_normal((20, 128)) * 3
+    ids, w = oracle.topk_softmax(L, 8)
+    full = torch.softmax(torch.from_numpy(L), dim=1).numpy()
+    for t in range(20):
+        p = full[t, ids[t]]
+        assert np.allclose(w[t], p / p.sum(), rtol=1e-13, atol=0)
+
+
+def test_shift_invariance_and_weight_invariants():
+    rng = np.random.default_rng(3)
+    L = rng.standard_normal((64, 128))
+    ids, w = oracle.topk_softmax(L, 8)
+    ids2, w2 = oracle.topk_softmax(L + 11.5, 8)
+    assert (ids == ids2).all()
+    assert np.allclose(w, w2, rtol=1e-12, atol=0)
+    assert np.allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-15)
+    assert (np.diff(w, axis=1) <= 0).all()
+    assert all(len(set(r)) == 8 for r in ids)
+
+
+def test_margin():
+    L = np.array([[5.0, 1.0, 3.0, 2.0]])
+    assert oracle.routing_margin(L, 2)[0] == 1.0
+    assert np.isinf(oracle.routing_margin(L, 4)[0])
+
+
+# ------------------------------------------------------------------ permutation
+def test_permutation_invariants_and_round_trip():
+    T, E, k, H = 300, 16, 4, 48
+    ids = mi.random_ids(T, E, k, seed=4, p=np.arange(1, E + 1)[::-1] / np.arange(1, E + 1).sum())
+    counts, offsets = oracle.counts_offsets(ids, E)
+    sorted_ids, inv = oracle.permutation(ids)
+    A = T * k
+    assert counts.sum() == A and offsets[0] == 0 and offsets[E] == A
+    assert (np.diff(offsets) == counts).all()
+    assert (np.bincount(ids.reshape(-1), minlength=E) == counts).all()
+    assert sorted(sorted_ids.tolist()) == list(range(A))
+    assert (inv[sorted_ids] == np.arange(A)).all()
+    flat = ids.reshape(-1)
+    for e in range(E):
+        seg = sorted_ids[offsets[e]:offsets[e + 1]]
+        assert (flat[seg] == e).all()
+        assert (np.diff(seg // k) > 0).all()          # stable in token order
+    tok_count = np.bincount(sorted_ids // k, minlength=T)
+    assert (tok_count == k).all()                      # each token exactly k times
+    x = mi.random_bf16((T, H), seed=9)
+    x_perm = x[sorted_ids // k]
+    back = x_perm[inv].reshape(T, k, H)
+    assert (back == x[:, None, :]).all()               # bitwise round trip
+
+
+def test_empty_experts_and_single_hot_expert():
+    ids = np.tile(np.array([[0, 5]], dtype=np.int32), (7, 1))
+    counts, offsets = oracle.counts_offsets(ids, 8)
+    assert counts.tolist() == [7, 0, 0, 0, 0, 7, 0, 0]
+    assert offsets.tolist() == [0, 7, 7, 7, 7, 7, 14, 14, 14]
+
+
+# ------------------------------------------------------------------ GELU
+def test_gelu_tanh_matches_torch_and_limits():
+    z = np.linspace(-12, 12, 4001)
+    ref = torch.nn.functional.gelu(torch.from_numpy(z), approximate="tanh").numpy()
+    assert np.abs(oracle.gelu_tanh(z) - ref).max() <= 1e-14
+    assert oracle.gelu_tanh(0.0) == 0.0
+    assert oracle.gelu_tanh(40.0) == 40.0             # tanh saturates to 1
+    assert oracle.gelu_tanh(-40.0) == 0.0
+    exact = 0.5 * z * (1 + np.vectorize(math.erf)(z / math.sqrt(2)))
+    assert np.abs(oracle.gelu_tanh(z) - exact).max() < 1e-3   # tanh form approximates erf form
+
+
+# ------------------------------------------------------------------ layer special cases
+def test_zero_input_gives_zero_output():
+    inp = _inputs(5, 64, 6, 2, 32)
+    inp.x[:] = 0
+    assert (oracle.forward(inp)["out"] == 0).all()
+
+
+def test_single_expert_is_a_dense_geglu_ffn():
+    inp = _inputs(9, 64, 1, 1, 32, seed=7)
+    r = oracle.forward(inp)
+    x = torch.from_numpy(mi.bf16_bits_to_f32(inp.x).astype(np.float64))
+    wgu = torch.from_numpy(mi.bf16_bits_to_f32(inp.w_gate_up[0]).astype(np.float64))
+    wd = torch.from_numpy(mi.bf16_bits_to_f32(inp.w_down[0]).astype(np.float64))
+    gate = torch.nn.functional.linear(x, wgu[:32])
+    up = torch.nn.functional.linear(x, wgu[32:])
+    ref = torch.nn.functional.linear(torch.nn.functional.gelu(gate, approximate="tanh") * up, wd)
+    assert (r["w"] == 1.0).all()
+    assert _rel(r["out"], ref.numpy()) <= 1e-13
+
+
+def _bits(v):
+    return mi.f32_to_bf16_bits(np.asarray(v, dtype=np.float32))
+
+
+def test_gate_is_first_half_closed_form():
+    """One token, H=2, two experts, k=2, I=1, weights chosen so every step has
+    an exact closed form.  x = (8, 1).  Router rows make the logits (1, 0).
+    Expert e: gate row (4, 0) -> gate pre-activation 32, gelu_tanh(32) = 32
+    exactly in fp64; up row (0, u_e) -> up = u_e; down column d_e.  So
+    Y_e = 32 u_e d_e and out = w0 Y_0 + w1 Y_1 with w0 = 1/(1+e^-1).
+    Swapping gate and up would give gelu_tanh(u_e) * 32 instead."""
+    s = mi.Shape(T=1, H=2, E=2, k=2, I=1)
+    u = [0.5, -2.0]
+    d = [[1.0, 0.25], [-0.5, 2.0]]
+    inp = mi.Inputs(
+        shape=s, seed=0,
+        x=_bits([[8.0, 1.0]]),
+        w_router=_bits([[0.125, 0.0], [0.0, 0.0]]),
+        router_bias=None,
+        w_gate_up=_bits([[[4.0, 0.0], [0.0, u[0]]], [[4.0, 0.0], [0.0, u[1]]]]),
+        w_down=_bits([[[d[0][0]], [d[0][1]]], [[d[1][0]], [d[1][1]]]]),
+    )
+    r = oracle.forward(inp)
+    w0 = 1.0 / (1.0 + math.exp(-1.0))
+    w1 = 1.0 - w0
+    expect = np.array([w0 * 32 * u[0] * d[0][0] + w1 * 32 * u[1] * d[1][0],
+                       w0 * 32 * u[0] * d[0][1] + w1 * 32 * u[1] * d[1][1]])
+    assert r["ids"].tolist() == [[0, 1]]
+    assert np.allclose(r["w"][0], [w0, w1], rtol=1e-15, atol=0)
+    assert np.allclose(r["out"][0], expect, rtol=1e-14, atol=0)
+
+
+def test_forward_tokens_matches_forward():
+    inp = _inputs(40, 64, 10, 3, 32, seed=11)
+    r = oracle.forward(inp)
+    sample = [0, 7, 39, 21]
+    f = oracle.forward_tokens(inp, sample)
+    assert (f["ids"] == r["ids"][sample]).all()
+    assert _rel(f["out"], r["out"][sample]) <= 1e-13
+
+
+def test_fp32_routing_override():
+    inp = _inputs(30, 64, 10, 3, 32, seed=12)
+    r = oracle.forward(inp)
+    L32 = r["logits"].astype(np.float32)
+    r32 = oracle.forward(inp, logits_fp32=L32)
+    assert (r32["route_logits"] == L32.astype(np.float64)).all()
+
+
+# ------------------------------------------------------------------ MXFP4
+def _golden_e2m1():
+    vals = {}
+    for line in open(os.path.join(GOLDEN, "ocp_mx_e2m1.txt")):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        c, v = line.split()
+        vals[int(c, 16)] = float(v)
+    return vals
+
+
+def test_mxfp4_decodes_every_code_to_the_published_table():
+    table = _golden_e2m1()
+    assert len(table) == 16
+    for s in (127, 100, 140, 120):
+        codes = np.arange(16, dtype=np.uint8)
+        packed = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
+        packed = np.tile(packed, 4)                     # 32 elements, one block
+        scales = np.array([s], dtype=np.uint8)
+        v = oracle.mxfp4_to_f64(packed, scales)
+        for c in range(16):
+            expect = table[c] * 2.0 ** (s - 127)
+            assert v[c] == expect and np.signbit(v[c]) == (c >= 8)
+    with pytest.raises(ValueError):
+        oracle.mxfp4_to_f64(np.zeros(16, np.uint8), np.array([255], np.uint8))
+
+
+def test_mxfp4_quantiser_round_trip_and_bf16_exactness():
+    w = mi.random_bf16((6, 128), sigma=0.02, seed=8)
+    packed, scales = mi.mxfp4_quantize(w)
+    deq = oracle.mxfp4_to_f64(packed, scales)
+    wf = mi.bf16_bits_to_f32(w).astype(np.float64)
+    step = np.repeat(np.ldexp(1.0, scales.astype(np.int64) - 127), 32, axis=1)
+    # every element within half a grid step of the largest spacing (2 * scale)
+    # unless saturated at 6 * scale
+    sat = np.abs(wf) > 6 * step
+    assert (np.abs(deq - wf)[~sat] <= step[~sat] + 0).all()
+    assert (np.abs(deq[sat]) == 6 * step[sat]).all()
+    # every decoded weight is exactly a bf16 value
+    assert (mi.bf16_bits_to_f32(mi.f32_to_bf16_bits(deq.astype(np.float32))) == deq).all()
+    # re-quantising the decoded weights reproduces the codes
+    p2, s2 = mi.mxfp4_quantize(mi.f32_to_bf16_bits(deq.astype(np.float32)))
+    assert (oracle.mxfp4_to_f64(p2, s2) == deq).all()
+
+
+def test_mxfp4_tie_rounding_is_nearest_even():
+    table = _golden_e2m1()
+    # block max 4.0 -> scale 2^0; the midpoints 0.25, .75, 1.25, 1.75, 2.5, 3.5, 5
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    expect = [0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0]
+    row = np.zeros(32, dtype=np.float32)
+    row[0] = 4.0
+    row[1:8] = mids
+    row[8:15] = [-m for m in mids]
+    p, s = mi.mxfp4_quantize(mi.f32_to_bf16_bits(row)[None, :])
+    v = oracle.mxfp4_to_f64(p, s)[0]
+    assert s[0, 0] == 127
+    assert v[1:8].tolist() == expect
+    assert v[8:15].tolist() == [-e for e in expect]
+    assert set(table.values()) >= set(abs(x) for x in expect)
+
+
+def test_router_logits_match_torch_linear_with_bias():
+    inp = _inputs(12, 64, 10, 3, 32, seed=13, skew=True)
+    x = torch.from_numpy(mi.bf16_bits_to_f32(inp.x).astype(np.float64))
+    W = torch.from_numpy(mi.bf16_bits_to_f32(inp.w_router).astype(np.float64))
+    b = torch.from_numpy(inp.router_bias.astype(np.float64))
+    ref = torch.nn.functional.linear(x, W, b).numpy()
+    got = oracle.router_logits(oracle.bf16_to_f64(inp.x), oracle.bf16_to_f64(inp.w_router), inp.router_bias)
+    assert np.allclose(got, ref, rtol=1e-14, atol=1e-14)
