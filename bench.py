@@ -1,0 +1,247 @@
+"""Benchmark of the MoE FFN layer (moe_forward) on one MI355X.
+
+A step is one moe_forward call over one batch of synthetic tokens: router
+GEMM + top-k softmax, permutation, grouped gate/up GEMM + GEGLU, grouped
+down GEMM, weighted combine.  The default workload is the Gemma-4-26B-A4B MoE
+layer at decode size (T=8 tokens, hidden 2816, 128 experts, top-8,
+intermediate 704, bf16).  Inputs are resident in HBM before timing; expert
+weights rotate over several device copies so the 256 MB Infinity Cache
+cannot serve them from a previous step.
+
+Prints one JSON line:  value = tokens/s of the whole layer; roofline = the
+dominant kernel (grouped gate/up GEMM) against the HBM or MFMA peak, its
+duration from HIP events the library records on the launch stream;
+cpu_baseline = the fp64 numpy oracle timed on this host on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + % HBM roofline (decode) / % bf16 MFMA peak (prefill)"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+STAGES = ["route", "permute", "gateup", "down", "combine"]
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--config", default="decode", help="tiny|decode|prefill|skew|mxfp4")
+    p.add_argument("--rotate", type=int, default=4, help="device copies of the weights cycled per step")
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle timing")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run a device copy of MIB mebibytes (counter calibration) and exit")
+    return p.parse_args()
+
+
+def algorithmic(inp, ids):
+    """Bytes and flops the method must move/do (touched experts' weights once,
+    router weight, x and out) for the layer and for the gate/up kernel."""
+    s = inp.shape
+    T, H, E, k, I = s.T, s.H, s.E, s.k, s.I
+    U = int(np.unique(ids).size)
+    if s.mxfp4:
+        gu_bytes = 2 * I * (H // 2 + H // 32)
+        d_bytes = H * (I // 2 + I // 32)
+    else:
+        gu_bytes = 2 * I * H * 2
+        d_bytes = H * I * 2
+    A = T * k
+    layer_bytes = U * (gu_bytes + d_bytes) + E * H * 2 + 2 * T * H * 2
+    layer_flops = T * (2 * H * E + k * (2 * H * 2 * I + 2 * I * H))
+    gateup_bytes = U * gu_bytes + T * H * 2 + A * I * 2
+    gateup_flops = A * 2 * H * 2 * I
+    return dict(U=U, layer_bytes=layer_bytes, layer_flops=layer_flops, gateup_bytes=gateup_bytes,
+                gateup_flops=gateup_flops, gu_bytes_per_expert=gu_bytes)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("grouped_gemm.hip", "moe_common.h"):
+        h.update(open(os.path.join(ROOT, "mixture_experts_router_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(config):
+    """HBM bytes per gate/up launch from a committed counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"gateup_{config}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, budget_s):
+    """The oracle as it stands, on this host, on a bounded sample."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:                                          # pragma: no cover
+        threads = 1
+    s = inp.shape
+    if s.T <= 64:
+        t0 = time.perf_counter()
+        n = 0
+        while True:
+            oracle.forward(inp)
+            n += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        el = time.perf_counter() - t0
+        tokens = n * s.T
+        sample = f"{n} full oracle.forward calls on the T={s.T} workload"
+    else:
+        rng = np.random.default_rng(0)
+        t0 = time.perf_counter()
+        tokens = 0
+        while time.perf_counter() - t0 < budget_s:
+            tok = rng.choice(s.T, size=16, replace=False)
+            oracle.forward_tokens(inp, tok)
+            tokens += 16
+        el = time.perf_counter() - t0
+        sample = f"{tokens} tokens of the T={s.T} workload through oracle.forward_tokens (16 per call)"
+    return {"value": tokens / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": sample, "seconds": round(el, 2),
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the layer holds all experts on one device and this "
+              f"build has no multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import moe_inputs as mi
+    import mixture_experts_router_amd as moe
+    from mixture_experts_router_amd import device as dev
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
+        return
+
+    t_gen = time.perf_counter()
+    inp = mi.make(args.config, seed=0)
+    s = inp.shape
+    sh = moe.shape(s.T, s.H, s.E, s.k, s.I, mxfp4=s.mxfp4)
+    x = dev.to_device(inp.x)
+    wr = dev.to_device(inp.w_router)
+    bias = dev.to_device(inp.router_bias) if inp.router_bias is not None else None
+    gu0 = dev.to_device(inp.w_gate_up)
+    d0 = dev.to_device(inp.w_down)
+    gus = dev.to_device(inp.gu_scales) if s.mxfp4 else None
+    ds = dev.to_device(inp.d_scales) if s.mxfp4 else None
+    copies = [(gu0, d0)] + [(gu0.clone(), d0.clone()) for _ in range(max(0, args.rotate - 1))]
+    out = torch.empty((s.T, s.H), dtype=torch.bfloat16, device="cuda")
+    ids = torch.empty((s.T, s.k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((s.T, s.k), dtype=torch.float32, device="cuda")
+    ws = dev.workspace(sh)
+    torch.cuda.synchronize()
+    gen_s = time.perf_counter() - t_gen
+    print(f"# inputs ready in {gen_s:.1f}s: {args.config} {s}", file=sys.stderr, flush=True)
+
+    def step(i, events=None):
+        gu, d = copies[i % len(copies)]
+        moe.forward(sh, x, wr, bias, gu, gus, d, ds, out, ids, wts, ws, stage_events=events)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ids_np = ids.cpu().numpy()
+    alg = algorithmic(inp, ids_np)
+
+    K = args.steps
+    ev = dev.StageEvents(K)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(K):
+        step(i, ev.arrays[i])
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / K
+    stage_ms = np.array([ev.stage_ms(i) for i in range(K)])      # [K, 5]
+    ev.close()
+    stage_avg_us = {n: float(v) * 1e3 for n, v in zip(STAGES, stage_ms.mean(axis=0))}
+    print(f"# {K} steps: {ms * 1e3:.1f} us/step; stages (us) " +
+          " ".join(f"{n}={v:.1f}" for n, v in stage_avg_us.items()), file=sys.stderr, flush=True)
+
+    tokens_per_s = s.T / (ms * 1e-3)
+    gu_s = stage_avg_us["gateup"] * 1e-6
+    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if alg["gateup_flops"] / alg["gateup_bytes"] > ridge:
+        bound, unit, peak = "mfma", "TFLOP/s", BF16_PEAK_TFLOPS
+        achieved = alg["gateup_flops"] / gu_s / 1e12
+    else:
+        bound, unit, peak = "hbm", "GB/s", HBM_PEAK_GBS
+        achieved = alg["gateup_bytes"] / gu_s / 1e9
+    t_layer = ms * 1e-3
+    layer = {
+        "touched_experts": alg["U"],
+        "alg_bytes": alg["layer_bytes"], "alg_flops": alg["layer_flops"],
+        "hbm_frac": alg["layer_bytes"] / t_layer / (HBM_PEAK_GBS * 1e9),
+        "mfma_frac": alg["layer_flops"] / t_layer / (BF16_PEAK_TFLOPS * 1e12),
+    }
+    res = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"Gemma-4-26B-A4B MoE FFN layer, {args.config}: T={s.T} tokens, "
+                               f"hidden {s.H}, {s.E} experts, top-{s.k}, intermediate {s.I}, "
+                               f"GEGLU, {'MXFP4' if s.mxfp4 else 'bf16'} expert weights"
+                               f"{', Zipf(1.2) router bias' if s.skew else ''}",
+                   "T": s.T, "H": s.H, "E": s.E, "k": s.k, "I": s.I,
+                   "weights": "mxfp4" if s.mxfp4 else "bf16", "weight_copies": len(copies)},
+        "roofline": {
+            "kernel": "grouped_gemm gate/up + GEGLU",
+            "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+            "frac": achieved / peak,
+            "traffic": traffic_from_profiles(args.config),
+            "alg_bytes_per_launch": alg["gateup_bytes"], "alg_flops_per_launch": alg["gateup_flops"],
+            "avg_launch_us": stage_avg_us["gateup"],
+        },
+        "layer": layer,
+        "stages_us": stage_avg_us,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

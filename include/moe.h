@@ -1,0 +1,196 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) Mixture-of-Experts FFN layer.
+ *
+ * The layer (Gemma-4-26B-A4B optimisation report, section 1 model overview:
+ * each decoder block has an MoE of 128 experts with top-8 routing, expert
+ * intermediate 704 and a GEGLU activation; Gemma-4-26B-A4B-NVFP4 Ascend
+ * verification report, section 2.1: hidden 2816, gelu_pytorch_tanh, bf16):
+ *
+ *   route    logits = x W_r^T (+ b); per token the top-k experts and their
+ *            renormalised softmax weights         (report, section 5, router op)
+ *   permute  per-expert counts, offsets and the expert-grouped order of the
+ *            (token, slot) assignments; optional gathered copy of x
+ *                                                 (report, section 6.1, dispatch)
+ *   gate/up  per expert, h = gelu_tanh(X W_gate^T) * (X W_up^T)    (GEGLU)
+ *   down     per expert, y = h W_down^T
+ *   combine  out[t] = sum_j w[t, j] y[inv[t*k + j]]  (report, section 6.1,
+ *            the local-expert weighted sum)
+ *
+ * Conventions shared by every entry point
+ *   - All array arguments are DEVICE pointers on the current HIP device,
+ *     row-major, densely packed.  bf16 values travel as uint16_t bit patterns.
+ *   - Weights are K-contiguous: w_router [E][H]; w_gate_up [E][2I][H] whose
+ *     rows 0..I-1 are the gate and rows I..2I-1 the up projection; w_down
+ *     [E][H][I].  MXFP4 weights (w_format MOE_W_MXFP4) replace a bf16 row of
+ *     K values by K/2 bytes of E2M1 codes (two per byte, the even K index in
+ *     the low nibble) plus K/32 E8M0 scale bytes (value 2^(byte-127)); the
+ *     E2M1/E8M0 encodings are the OCP Microscaling Formats v1.0 ones.  The
+ *     router weight is always bf16.  Decoded weights must be normal bf16
+ *     numbers (scale bytes 2..250 guarantee it); 0xFF scales are undefined.
+ *   - Assignment a = t*k + j is slot j of token t.  A = T*k.
+ *   - Routing: the k largest logits, ties to the lower expert index, slots in
+ *     (logit descending, index ascending) order; w = softmax over the k
+ *     selected logits.  Non-finite logits give undefined routing.
+ *   - Expert-grouped order: position p of sorted_ids holds the assignment a;
+ *     assignments of expert e occupy [offsets[e], offsets[e+1]) in ascending
+ *     token order.  inv[a] = p.  Every token has exactly k assignments; no
+ *     capacity limit, nothing dropped.  Empty experts read no weight bytes.
+ *   - Arithmetic: bf16 inputs, fp32 accumulation; h, y and out are rounded
+ *     to bf16 (nearest-even); the combine sums in fp32 in ascending j.  The
+ *     router accumulates in fp32 over blocks of 256 products and adds the
+ *     block sums in fp64 before the single rounding of each logit to fp32.
+ *   - Ownership: the caller allocates and frees every buffer, including the
+ *     workspace.  The library allocates nothing and keeps no pointer after a
+ *     call returns.  Inputs are never written.
+ *   - Execution: every call only enqueues kernels on `stream` (a hipStream_t;
+ *     NULL is the null stream).  None synchronises or copies data to the
+ *     host.  The entry points hold no global mutable state; calls on
+ *     different streams with disjoint outputs may overlap.
+ *   - Errors: the return value is a status.  Shape, pointer, alignment and
+ *     workspace checks run on the host before any HIP call; a failing check
+ *     launches nothing.  MOE_ERR_HIP reports a launch failure; faults during
+ *     execution surface at the caller's next synchronisation.  No C++
+ *     exception crosses this interface.
+ *   - Supported sizes: H % 64 == 0, I % 64 == 0, 1 <= k <= min(E, 32),
+ *     E <= 1024, T*k < 2^30.  Pointers to bf16 arrays, x_perm, h and y must
+ *     be 16-byte aligned, the other arrays 4-byte aligned.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct moe_shape {
+    int32_t T;        /* tokens */
+    int32_t H;        /* hidden size */
+    int32_t E;        /* experts */
+    int32_t k;        /* experts per token */
+    int32_t I;        /* expert intermediate size */
+    int32_t w_format; /* MOE_W_BF16 or MOE_W_MXFP4 (expert weights only) */
+} moe_shape;
+
+enum { MOE_W_BF16 = 0, MOE_W_MXFP4 = 1 };
+
+enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARGUMENT = -1, /* NULL pointer, T/H/E/I < 1, k < 1, k > E, misalignment */
+    MOE_ERR_UNSUPPORTED = -2,      /* a size outside the supported set above */
+    MOE_ERR_WORKSPACE = -3,        /* workspace NULL or smaller than required */
+    MOE_ERR_HIP = -4               /* a HIP launch or event call failed */
+};
+
+typedef void *moe_stream_t; /* hipStream_t */
+typedef void *moe_event_t;  /* hipEvent_t */
+
+/* Number of stages moe_forward times when given stage events. */
+#define MOE_FORWARD_STAGES 5
+
+/*
+ * moe_route -- router GEMM, top-k and softmax weights (report, section 5:
+ * the router op fused as gating top-k softmax).
+ *   x            [T][H] bf16, or NULL: then `logits` is an INPUT [T][E] fp32
+ *                and w_router / router_bias are ignored
+ *   w_router     [E][H] bf16 (required when x != NULL)
+ *   router_bias  [E] fp32 or NULL
+ *   logits       [T][E] fp32: output when x != NULL, input when x == NULL
+ *   topk_ids     [T][k] int32 out;  topk_w [T][k] fp32 out (rows sum to 1)
+ */
+int moe_route(const moe_shape *s, const uint16_t *x, const uint16_t *w_router,
+              const float *router_bias, float *logits, int32_t *topk_ids,
+              float *topk_w, moe_stream_t stream);
+
+/*
+ * moe_permute -- expert histogram, prefix scan and stable scatter: the
+ * data-dependent split sizes and order of the dispatch (report, section 6.1).
+ *   topk_ids     [T][k] int32 in, each in [0, E)
+ *   counts       [E] int32 out;  offsets [E+1] int32 out (offsets[E] = T*k)
+ *   sorted_ids   [T*k] int32 out; inv [T*k] int32 out
+ *   x, x_perm    both NULL, or x [T][H] bf16 in and x_perm [T*k][H] bf16 out
+ *                with x_perm[p] = x[sorted_ids[p] / k] (bitwise copy)
+ *   ws           device scratch of at least moe_permute_workspace_bytes(s)
+ */
+int moe_permute(const moe_shape *s, const int32_t *topk_ids, const uint16_t *x,
+                int32_t *counts, int32_t *offsets, int32_t *sorted_ids,
+                int32_t *inv, uint16_t *x_perm, void *ws, size_t ws_bytes,
+                moe_stream_t stream);
+
+/*
+ * moe_grouped_gemm_gateup -- per expert e with rows [offsets[e],
+ * offsets[e+1]): G = X_e W_gu[e]^T (fp32), h = gelu_tanh(G[:, :I]) * G[:, I:]
+ * rounded to bf16 (GEGLU, report, section 1; gelu_pytorch_tanh, verification
+ * report, section 2.1).  gelu_tanh(z) = 0.5 z (1 + tanh(sqrt(2/pi)(z + 0.044715 z^3))).
+ *   x            sorted_ids == NULL: x_perm [T*k][H] bf16, row p = assignment p
+ *                sorted_ids != NULL: x [T][H] bf16, row p = x[sorted_ids[p] / k]
+ *   sorted_ids   [T*k] int32 or NULL (see x)
+ *   offsets      [E+1] int32
+ *   w_gate_up    bf16 [E][2I][H], or MXFP4 codes [E][2I][H/2]
+ *   gu_scales    NULL for bf16; MXFP4 scales [E][2I][H/32]
+ *   h            [T*k][I] bf16 out
+ */
+int moe_grouped_gemm_gateup(const moe_shape *s, const uint16_t *x,
+                            const int32_t *sorted_ids, const int32_t *offsets,
+                            const void *w_gate_up, const uint8_t *gu_scales,
+                            uint16_t *h, moe_stream_t stream);
+
+/*
+ * moe_grouped_gemm_down -- per expert: y rows = h rows W_d[e]^T, fp32
+ * accumulation, bf16 out.
+ *   h            [T*k][I] bf16;  offsets [E+1] int32
+ *   w_down       bf16 [E][H][I], or MXFP4 codes [E][H][I/2]
+ *   d_scales     NULL for bf16; MXFP4 scales [E][H][I/32]
+ *   y            [T*k][H] bf16 out
+ */
+int moe_grouped_gemm_down(const moe_shape *s, const uint16_t *h,
+                          const int32_t *offsets, const void *w_down,
+                          const uint8_t *d_scales, uint16_t *y,
+                          moe_stream_t stream);
+
+/*
+ * moe_combine -- out[t] = sum_{j<k} topk_w[t][j] * y[inv[t*k+j]], fp32 sum
+ * in ascending j, one bf16 rounding; no atomics, so bitwise reproducible.
+ *   y [T*k][H] bf16; inv [T*k] int32; topk_w [T][k] fp32; out [T][H] bf16
+ */
+int moe_combine(const moe_shape *s, const uint16_t *y, const int32_t *inv,
+                const float *topk_w, uint16_t *out, moe_stream_t stream);
+
+/*
+ * moe_forward -- the whole layer: route, permute (without materialising
+ * x_perm: the gate/up GEMM gathers x rows itself), gate/up + GEGLU, down,
+ * combine, all on `stream`, with a launch grid that depends only on the
+ * shape (never on routing counts), no host synchronisation and no
+ * device-to-host copy.
+ *   weights and scales as for the steps above
+ *   out           [T][H] bf16 out
+ *   topk_ids_out  [T][k] int32 out or NULL;  topk_w_out [T][k] fp32 out or NULL
+ *   ws            device scratch of at least moe_workspace_bytes(s)
+ *   stage_events  NULL, or MOE_FORWARD_STAGES + 1 hipEvent_t recorded on
+ *                 `stream` before the first stage and after each stage
+ *                 (route, permute, gate/up, down, combine)
+ */
+int moe_forward(const moe_shape *s, const uint16_t *x, const uint16_t *w_router,
+                const float *router_bias, const void *w_gate_up,
+                const uint8_t *gu_scales, const void *w_down,
+                const uint8_t *d_scales, uint16_t *out, int32_t *topk_ids_out,
+                float *topk_w_out, void *ws, size_t ws_bytes,
+                moe_stream_t stream, const moe_event_t *stage_events);
+
+/* Workspace bytes moe_forward needs for this shape; 0 for an invalid or
+ * unsupported shape.  Monotone in T. */
+size_t moe_workspace_bytes(const moe_shape *s);
+
+/* Workspace bytes moe_permute needs for this shape; 0 if invalid. */
+size_t moe_permute_workspace_bytes(const moe_shape *s);
+
+/* Static description of a status code; never NULL. */
+const char *moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,12 @@
+"""MI355X (gfx950) Mixture-of-Experts FFN layer: router -> top-k softmax ->
+expert-grouped dispatch -> grouped GEGLU expert GEMMs -> weighted combine.
+
+The layer runs in hand-written HIP kernels behind the C ABI of include/moe.h
+(libmoe.so in this directory).  This package only marshals arguments; every
+call raises if the library is missing.
+"""
+from ._lib import (  # noqa: F401
+    EXPORTS, LIB_PATH, MOE_FORWARD_STAGES, MOE_W_BF16, MOE_W_MXFP4, MoeError, MoeShape,
+    combine, forward, gemm_down, gemm_gateup, load, permute, permute_workspace_bytes, route,
+    shape, workspace_bytes,
+)

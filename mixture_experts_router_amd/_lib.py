@@ -1,0 +1,156 @@
+"""ctypes binding of libmoe.so (include/moe.h).  Argument marshalling only:
+every step of the layer runs in the library's HIP kernels.  torch provides
+device memory and the current stream."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe.so")
+
+MOE_W_BF16, MOE_W_MXFP4 = 0, 1
+MOE_FORWARD_STAGES = 5
+STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARGUMENT", -2: "MOE_ERR_UNSUPPORTED",
+          -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP"}
+
+# Entry points declared in include/moe.h.
+EXPORTS = ("moe_route", "moe_permute", "moe_grouped_gemm_gateup", "moe_grouped_gemm_down",
+           "moe_combine", "moe_forward", "moe_workspace_bytes", "moe_permute_workspace_bytes",
+           "moe_status_string")
+
+
+class MoeShape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("I", ctypes.c_int32), ("w_format", ctypes.c_int32)]
+
+    def __repr__(self):
+        return (f"MoeShape(T={self.T}, H={self.H}, E={self.E}, k={self.k}, I={self.I}, "
+                f"w_format={self.w_format})")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({msg})")
+        self.status = status
+
+
+_lib = None
+_P = ctypes.c_void_p
+_S = ctypes.POINTER(MoeShape)
+
+
+def load(path: str = LIB_PATH):
+    """Load libmoe.so.  torch is imported first so that the library binds to
+    the HIP runtime torch already uses (one runtime per process)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with mixture_experts_router_amd.build.build()")
+    import torch  # noqa: F401  (loads torch's libamdhip64 before ours)
+    lib = ctypes.CDLL(path)
+    c_int, c_size = ctypes.c_int, ctypes.c_size_t
+    sig = {
+        "moe_route": [_S, _P, _P, _P, _P, _P, _P, _P],
+        "moe_permute": [_S, _P, _P, _P, _P, _P, _P, _P, _P, c_size, _P],
+        "moe_grouped_gemm_gateup": [_S, _P, _P, _P, _P, _P, _P, _P],
+        "moe_grouped_gemm_down": [_S, _P, _P, _P, _P, _P, _P],
+        "moe_combine": [_S, _P, _P, _P, _P, _P],
+        "moe_forward": [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, c_size, _P, _P],
+    }
+    for name, args in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = c_int
+    for name in ("moe_workspace_bytes", "moe_permute_workspace_bytes"):
+        f = getattr(lib, name)
+        f.argtypes = [_S]
+        f.restype = c_size
+    lib.moe_status_string.argtypes = [c_int]
+    lib.moe_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def shape(T, H, E, k, I, mxfp4=False) -> MoeShape:
+    return MoeShape(T, H, E, k, I, MOE_W_MXFP4 if mxfp4 else MOE_W_BF16)
+
+
+def _ptr(t):
+    """Device address of a contiguous CUDA tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(fn, st):
+    if st != 0:
+        raise MoeError(fn, st, _lib.moe_status_string(st).decode())
+
+
+def workspace_bytes(s: MoeShape) -> int:
+    return load().moe_workspace_bytes(ctypes.byref(s))
+
+
+def permute_workspace_bytes(s: MoeShape) -> int:
+    return load().moe_permute_workspace_bytes(ctypes.byref(s))
+
+
+def route(s, x, w_router, router_bias, logits, topk_ids, topk_w, stream=None):
+    lib = load()
+    _check("moe_route", lib.moe_route(ctypes.byref(s), _ptr(x), _ptr(w_router), _ptr(router_bias),
+                                      _ptr(logits), _ptr(topk_ids), _ptr(topk_w), _stream(stream)))
+
+
+def permute(s, topk_ids, x, counts, offsets, sorted_ids, inv, x_perm, ws, stream=None):
+    lib = load()
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check("moe_permute", lib.moe_permute(ctypes.byref(s), _ptr(topk_ids), _ptr(x), _ptr(counts),
+                                          _ptr(offsets), _ptr(sorted_ids), _ptr(inv), _ptr(x_perm),
+                                          _ptr(ws), nbytes, _stream(stream)))
+
+
+def gemm_gateup(s, x, sorted_ids, offsets, w_gate_up, gu_scales, h, stream=None):
+    lib = load()
+    _check("moe_grouped_gemm_gateup",
+           lib.moe_grouped_gemm_gateup(ctypes.byref(s), _ptr(x), _ptr(sorted_ids), _ptr(offsets),
+                                       _ptr(w_gate_up), _ptr(gu_scales), _ptr(h), _stream(stream)))
+
+
+def gemm_down(s, h, offsets, w_down, d_scales, y, stream=None):
+    lib = load()
+    _check("moe_grouped_gemm_down",
+           lib.moe_grouped_gemm_down(ctypes.byref(s), _ptr(h), _ptr(offsets), _ptr(w_down),
+                                     _ptr(d_scales), _ptr(y), _stream(stream)))
+
+
+def combine(s, y, inv, topk_w, out, stream=None):
+    lib = load()
+    _check("moe_combine", lib.moe_combine(ctypes.byref(s), _ptr(y), _ptr(inv), _ptr(topk_w),
+                                          _ptr(out), _stream(stream)))
+
+
+def forward(s, x, w_router, router_bias, w_gate_up, gu_scales, w_down, d_scales, out,
+            topk_ids_out=None, topk_w_out=None, ws=None, stream=None, stage_events=None):
+    """stage_events: None or a ctypes array of MOE_FORWARD_STAGES + 1 hipEvent_t handles."""
+    lib = load()
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    ev = ctypes.cast(stage_events, _P) if stage_events is not None else None
+    _check("moe_forward",
+           lib.moe_forward(ctypes.byref(s), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w_gate_up),
+                           _ptr(gu_scales), _ptr(w_down), _ptr(d_scales), _ptr(out), _ptr(topk_ids_out),
+                           _ptr(topk_w_out), _ptr(ws), nbytes, _stream(stream), ev))

@@ -1,0 +1,226 @@
+// C ABI of the MoE layer: argument checks (host only, before any HIP call),
+// workspace layout and the kernel sequence of moe_forward.
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+#include "moe_launch.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool al16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool al4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int check_shape(const moe_shape *s) {
+    if (!s) return MOE_ERR_INVALID_ARGUMENT;
+    if (s->T < 1 || s->H < 1 || s->E < 1 || s->k < 1 || s->I < 1) return MOE_ERR_INVALID_ARGUMENT;
+    if (s->k > s->E) return MOE_ERR_INVALID_ARGUMENT;
+    if (s->w_format != MOE_W_BF16 && s->w_format != MOE_W_MXFP4) return MOE_ERR_UNSUPPORTED;
+    if (s->H % 64 != 0 || s->I % 64 != 0) return MOE_ERR_UNSUPPORTED;
+    if (s->E > 1024 || s->k > 32) return MOE_ERR_UNSUPPORTED;
+    if ((int64_t)s->T * s->k >= (int64_t{1} << 30)) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+int num_blocks(const moe_shape *s) {
+    const int64_t A = (int64_t)s->T * s->k;
+    return (int)((A + moe::kChunk - 1) / moe::kChunk);
+}
+
+size_t permute_ws(const moe_shape *s) { return round_up((size_t)num_blocks(s) * s->E * sizeof(int32_t)); }
+
+// Weight pointers: bf16 weights must be 16-byte aligned and come without
+// scales; MXFP4 codes must be 4-byte aligned and come with scales.
+int check_weights(const moe_shape *s, const void *w, const uint8_t *scales) {
+    if (!w) return MOE_ERR_INVALID_ARGUMENT;
+    if (s->w_format == MOE_W_BF16) {
+        if (scales || !al16(w)) return MOE_ERR_INVALID_ARGUMENT;
+    } else {
+        if (!scales || !al4(w)) return MOE_ERR_INVALID_ARGUMENT;
+    }
+    return MOE_OK;
+}
+
+struct Workspace {
+    float *logits;
+    int32_t *ids;
+    float *w;
+    int32_t *counts, *offsets, *block_hist, *sorted_ids, *inv;
+    uint16_t *h, *y;
+    size_t bytes;
+};
+
+Workspace carve(const moe_shape *s, void *base) {
+    const size_t T = s->T, E = s->E, A = T * s->k;
+    char *p = static_cast<char *>(base);
+    size_t off = 0;
+    Workspace w{};
+    auto take = [&](size_t bytes) {
+        char *q = p ? p + off : nullptr;
+        off += round_up(bytes);
+        return q;
+    };
+    w.logits = reinterpret_cast<float *>(take(T * E * sizeof(float)));
+    w.ids = reinterpret_cast<int32_t *>(take(A * sizeof(int32_t)));
+    w.w = reinterpret_cast<float *>(take(A * sizeof(float)));
+    w.counts = reinterpret_cast<int32_t *>(take(E * sizeof(int32_t)));
+    w.offsets = reinterpret_cast<int32_t *>(take((E + 1) * sizeof(int32_t)));
+    w.block_hist = reinterpret_cast<int32_t *>(take((size_t)num_blocks(s) * E * sizeof(int32_t)));
+    w.sorted_ids = reinterpret_cast<int32_t *>(take(A * sizeof(int32_t)));
+    w.inv = reinterpret_cast<int32_t *>(take(A * sizeof(int32_t)));
+    w.h = reinterpret_cast<uint16_t *>(take(A * s->I * sizeof(uint16_t)));
+    w.y = reinterpret_cast<uint16_t *>(take(A * s->H * sizeof(uint16_t)));
+    w.bytes = off;
+    return w;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_status_string(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported size or format";
+        case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+        case MOE_ERR_HIP: return "HIP launch or event call failed";
+        default: return "unknown status";
+    }
+}
+
+size_t moe_workspace_bytes(const moe_shape *s) {
+    if (check_shape(s) != MOE_OK) return 0;
+    return carve(s, nullptr).bytes;
+}
+
+size_t moe_permute_workspace_bytes(const moe_shape *s) {
+    if (check_shape(s) != MOE_OK) return 0;
+    return permute_ws(s);
+}
+
+int moe_route(const moe_shape *s, const uint16_t *x, const uint16_t *w_router, const float *router_bias,
+              float *logits, int32_t *topk_ids, float *topk_w, moe_stream_t stream) {
+    int st = check_shape(s);
+    if (st != MOE_OK) return st;
+    if (!logits || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARGUMENT;
+    if (!al4(logits) || !al4(topk_ids) || !al4(topk_w)) return MOE_ERR_INVALID_ARGUMENT;
+    if (x) {
+        if (!w_router || !al16(x) || !al16(w_router)) return MOE_ERR_INVALID_ARGUMENT;
+        if (router_bias && !al4(router_bias)) return MOE_ERR_INVALID_ARGUMENT;
+    }
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (x) {
+        st = hip_status(moe::launch_router_gemm(x, w_router, router_bias, logits, s->T, s->H, s->E, hs));
+        if (st != MOE_OK) return st;
+    }
+    return hip_status(moe::launch_topk(logits, topk_ids, topk_w, s->T, s->E, s->k, hs));
+}
+
+int moe_permute(const moe_shape *s, const int32_t *topk_ids, const uint16_t *x, int32_t *counts,
+                int32_t *offsets, int32_t *sorted_ids, int32_t *inv, uint16_t *x_perm, void *ws,
+                size_t ws_bytes, moe_stream_t stream) {
+    int st = check_shape(s);
+    if (st != MOE_OK) return st;
+    if (!topk_ids || !counts || !offsets || !sorted_ids || !inv) return MOE_ERR_INVALID_ARGUMENT;
+    if (!al4(topk_ids) || !al4(counts) || !al4(offsets) || !al4(sorted_ids) || !al4(inv))
+        return MOE_ERR_INVALID_ARGUMENT;
+    if ((x == nullptr) != (x_perm == nullptr)) return MOE_ERR_INVALID_ARGUMENT;
+    if (x && (!al16(x) || !al16(x_perm))) return MOE_ERR_INVALID_ARGUMENT;
+    if (!ws || ws_bytes < permute_ws(s) || !al4(ws)) return MOE_ERR_WORKSPACE;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const int A = s->T * s->k;
+    st = hip_status(moe::launch_permute(topk_ids, counts, offsets, sorted_ids, inv,
+                                        static_cast<int32_t *>(ws), A, s->E, hs));
+    if (st != MOE_OK || !x) return st;
+    return hip_status(moe::launch_gather_rows(x, sorted_ids, x_perm, A, s->H, s->k, hs));
+}
+
+int moe_grouped_gemm_gateup(const moe_shape *s, const uint16_t *x, const int32_t *sorted_ids,
+                            const int32_t *offsets, const void *w_gate_up, const uint8_t *gu_scales,
+                            uint16_t *h, moe_stream_t stream) {
+    int st = check_shape(s);
+    if (st != MOE_OK) return st;
+    if (!x || !offsets || !h) return MOE_ERR_INVALID_ARGUMENT;
+    if (!al16(x) || !al16(h) || !al4(offsets)) return MOE_ERR_INVALID_ARGUMENT;
+    if (sorted_ids && !al4(sorted_ids)) return MOE_ERR_INVALID_ARGUMENT;
+    if ((st = check_weights(s, w_gate_up, gu_scales)) != MOE_OK) return st;
+    return hip_status(moe::launch_gateup(x, sorted_ids, s->k, offsets, w_gate_up, gu_scales, h,
+                                         s->T * s->k, s->H, s->E, s->I, s->w_format == MOE_W_MXFP4,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int moe_grouped_gemm_down(const moe_shape *s, const uint16_t *h, const int32_t *offsets, const void *w_down,
+                          const uint8_t *d_scales, uint16_t *y, moe_stream_t stream) {
+    int st = check_shape(s);
+    if (st != MOE_OK) return st;
+    if (!h || !offsets || !y) return MOE_ERR_INVALID_ARGUMENT;
+    if (!al16(h) || !al16(y) || !al4(offsets)) return MOE_ERR_INVALID_ARGUMENT;
+    if ((st = check_weights(s, w_down, d_scales)) != MOE_OK) return st;
+    return hip_status(moe::launch_down(h, offsets, w_down, d_scales, y, s->T * s->k, s->H, s->E, s->I,
+                                       s->w_format == MOE_W_MXFP4, static_cast<hipStream_t>(stream)));
+}
+
+int moe_combine(const moe_shape *s, const uint16_t *y, const int32_t *inv, const float *topk_w,
+                uint16_t *out, moe_stream_t stream) {
+    int st = check_shape(s);
+    if (st != MOE_OK) return st;
+    if (!y || !inv || !topk_w || !out) return MOE_ERR_INVALID_ARGUMENT;
+    if (!al16(y) || !al16(out) || !al4(inv) || !al4(topk_w)) return MOE_ERR_INVALID_ARGUMENT;
+    return hip_status(moe::launch_combine(y, inv, topk_w, out, s->T, s->H, s->k,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int moe_forward(const moe_shape *s, const uint16_t *x, const uint16_t *w_router, const float *router_bias,
+                const void *w_gate_up, const uint8_t *gu_scales, const void *w_down, const uint8_t *d_scales,
+                uint16_t *out, int32_t *topk_ids_out, float *topk_w_out, void *ws, size_t ws_bytes,
+                moe_stream_t stream, const moe_event_t *stage_events) {
+    int st = check_shape(s);
+    if (st != MOE_OK) return st;
+    if (!x || !w_router || !out) return MOE_ERR_INVALID_ARGUMENT;
+    if (!al16(x) || !al16(w_router) || !al16(out)) return MOE_ERR_INVALID_ARGUMENT;
+    if (router_bias && !al4(router_bias)) return MOE_ERR_INVALID_ARGUMENT;
+    if ((topk_ids_out && !al4(topk_ids_out)) || (topk_w_out && !al4(topk_w_out)))
+        return MOE_ERR_INVALID_ARGUMENT;
+    if ((st = check_weights(s, w_gate_up, gu_scales)) != MOE_OK) return st;
+    if ((st = check_weights(s, w_down, d_scales)) != MOE_OK) return st;
+    if (stage_events)
+        for (int i = 0; i <= MOE_FORWARD_STAGES; ++i)
+            if (!stage_events[i]) return MOE_ERR_INVALID_ARGUMENT;
+    const size_t need = carve(s, nullptr).bytes;
+    if (!ws || ws_bytes < need || !al16(ws)) return MOE_ERR_WORKSPACE;
+
+    Workspace w = carve(s, ws);
+    int32_t *ids = topk_ids_out ? topk_ids_out : w.ids;
+    float *wts = topk_w_out ? topk_w_out : w.w;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const int T = s->T, H = s->H, E = s->E, k = s->k, I = s->I, A = T * k;
+    const bool mx = s->w_format == MOE_W_MXFP4;
+
+    int stage = 0;
+    auto mark = [&]() -> int {
+        if (!stage_events) return MOE_OK;
+        return hip_status(hipEventRecord(static_cast<hipEvent_t>(stage_events[stage++]), hs));
+    };
+    if ((st = mark()) != MOE_OK) return st;
+    st = hip_status(moe::launch_router_gemm(x, w_router, router_bias, w.logits, T, H, E, hs));
+    if (st == MOE_OK) st = hip_status(moe::launch_topk(w.logits, ids, wts, T, E, k, hs));
+    if (st != MOE_OK || (st = mark()) != MOE_OK) return st;
+    st = hip_status(moe::launch_permute(ids, w.counts, w.offsets, w.sorted_ids, w.inv, w.block_hist, A, E, hs));
+    if (st != MOE_OK || (st = mark()) != MOE_OK) return st;
+    st = hip_status(moe::launch_gateup(x, w.sorted_ids, k, w.offsets, w_gate_up, gu_scales, w.h, A, H, E, I, mx, hs));
+    if (st != MOE_OK || (st = mark()) != MOE_OK) return st;
+    st = hip_status(moe::launch_down(w.h, w.offsets, w_down, d_scales, w.y, A, H, E, I, mx, hs));
+    if (st != MOE_OK || (st = mark()) != MOE_OK) return st;
+    st = hip_status(moe::launch_combine(w.y, w.inv, wts, out, T, H, k, hs));
+    if (st != MOE_OK) return st;
+    return mark();
+}
+
+}  // extern "C"

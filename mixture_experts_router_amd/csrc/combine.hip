@@ -1,0 +1,52 @@
+// Weighted combine: out[t] = sum_{j<k} w[t, j] * y[inv[t*k + j]], summed in
+// fp32 in ascending j and rounded to bf16 once.  This is the local-expert sum
+// that the decode path of the pages all-reduces across expert-parallel
+// ranks (Gemma-4-26B-A4B optimisation report, section 6.1, MoE row).  Each
+// output element is owned by one lane, so there are no atomics and the
+// result is bitwise reproducible.
+#include "moe_common.h"
+#include "moe_launch.h"
+
+namespace moe {
+
+// One workgroup per token; each lane owns 8 consecutive outputs (16 bytes).
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict__ y,
+                                                      const int32_t *__restrict__ inv,
+                                                      const float *__restrict__ w,
+                                                      uint16_t *__restrict__ out, int H, int k) {
+    __shared__ int s_row[32];
+    __shared__ float s_w[32];
+    const int t = blockIdx.x;
+    if (threadIdx.x < k) {
+        s_row[threadIdx.x] = inv[(size_t)t * k + threadIdx.x];
+        s_w[threadIdx.x] = w[(size_t)t * k + threadIdx.x];
+    }
+    __syncthreads();
+    const int nchunks = H / 8;
+    for (int c = threadIdx.x; c < nchunks; c += blockDim.x) {
+        float acc[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+        for (int j = 0; j < k; ++j) {
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(y + (size_t)s_row[j] * H + c * 8);
+            const float wj = s_w[j];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc[2 * q] = fmaf(wj, bf16_to_f32(v[q] & 0xFFFFu), acc[2 * q]);
+                acc[2 * q + 1] = fmaf(wj, bf16_to_f32(v[q] >> 16), acc[2 * q + 1]);
+            }
+        }
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+        *reinterpret_cast<u32x4 *>(out + (size_t)t * H + c * 8) = o;
+    }
+}
+
+hipError_t launch_combine(const uint16_t *y, const int32_t *inv, const float *w, uint16_t *out, int T,
+                          int H, int k, hipStream_t st) {
+    combine_kernel<<<T, 256, 0, st>>>(y, inv, w, out, H, k);
+    return hipGetLastError();
+}
+
+}  // namespace moe

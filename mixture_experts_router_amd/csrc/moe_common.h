@@ -1,0 +1,59 @@
+// Shared device helpers for the gfx950 MoE kernels: bf16 conversion, MFMA
+// operand types and the LDS tile swizzle.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t b = __float_as_uint(f);
+    b += 0x7FFFu + ((b >> 16) & 1u);
+    return b >> 16;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// Two bf16 values packed low/high in a 32-bit word.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// A tile row holds 64 bf16 (128 bytes = 8 chunks of 16 bytes).  The chunk
+// index is XORed with a function of the row so that 16 lanes reading the same
+// logical chunk of 16 consecutive rows hit distinct LDS banks, whether the
+// LDS is 32 or 64 banks wide.
+__device__ __forceinline__ int swz(int row, int chunk) {
+    return chunk ^ ((row ^ (row >> 3)) & 7);
+}
+
+// 16x16x32 bf16 MFMA with fp32 accumulation.  Operand layout per lane l:
+// A row (l % 16), k = 8*(l/16) .. +7; B column (l % 16), same k range;
+// result rows 4*(l/16) + r (r = 0..3), column l % 16.
+__device__ __forceinline__ f32x4 mfma16x16x32(const u32x4 &a, const u32x4 &b, f32x4 c) {
+    bf16x8 av = __builtin_bit_cast(bf16x8, a);
+    bf16x8 bv = __builtin_bit_cast(bf16x8, b);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, c, 0, 0, 0);
+}
+
+// gelu_pytorch_tanh: 0.5 z (1 + tanh(u)), u = sqrt(2/pi) (z + 0.044715 z^3),
+// evaluated as z / (1 + exp(-2u)) (the same function: 0.5 (1 + tanh u) is
+// the logistic function of 2u).  Large |u| saturates to z or -0.
+__device__ __forceinline__ float gelu_tanh(float z) {
+    const float k0 = 0.7978845608028654f;   // sqrt(2/pi)
+    const float k1 = 0.044715f;
+    float u = k0 * (z + k1 * z * z * z);
+    return z / (1.0f + __expf(-2.0f * u));
+}
+
+}  // namespace moe

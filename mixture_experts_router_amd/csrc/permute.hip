@@ -1,0 +1,183 @@
+// Dispatch bookkeeping: per-expert counts, their prefix sum and the stable
+// expert-grouped order of the (token, slot) assignments.  These counts are
+// the data-dependent split sizes of the dispatch (Gemma-4-26B-A4B
+// optimisation report, section 6.1, MoE row).
+//
+// Deterministic and free of global atomics: each block of kChunk assignments
+// builds its histogram in LDS, one block scans the block histograms, and each
+// block then ranks its assignments in order (wave ballots give the rank
+// among equal experts inside 64 lanes; a running LDS counter per expert
+// carries it across the block's chunks).
+#include "moe_common.h"
+#include "moe_launch.h"
+
+namespace moe {
+
+// Mask of the lanes (among those with `valid`) holding the same expert id.
+__device__ __forceinline__ uint64_t match_lanes(int e, bool valid, int nbits) {
+    uint64_t m = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+        const uint64_t ones = __ballot(valid && ((e >> b) & 1));
+        m &= ((e >> b) & 1) ? ones : ~ones;
+    }
+    return m;
+}
+
+// Block b counts experts of assignments [b*kChunk, (b+1)*kChunk).
+__global__ __launch_bounds__(256) void hist_kernel(const int32_t *__restrict__ ids,
+                                                   int32_t *__restrict__ block_hist, int A, int E) {
+    extern __shared__ int32_t h[];
+    for (int e = threadIdx.x; e < E; e += blockDim.x) h[e] = 0;
+    __syncthreads();
+    const int a0 = blockIdx.x * kChunk;
+    const int a1 = min(A, a0 + kChunk);
+    for (int a = a0 + threadIdx.x; a < a1; a += blockDim.x) atomicAdd(&h[ids[a]], 1);
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x) block_hist[(size_t)blockIdx.x * E + e] = h[e];
+}
+
+// Block-wide exclusive scan of E <= 1024 values held one per thread.
+__device__ int block_exclusive_scan(int v, int *sh /* >= blockDim.x ints */) {
+    const int tid = threadIdx.x;
+    sh[tid] = v;
+    __syncthreads();
+    for (int off = 1; off < (int)blockDim.x; off <<= 1) {
+        const int add = tid >= off ? sh[tid - off] : 0;
+        __syncthreads();
+        sh[tid] += add;
+        __syncthreads();
+    }
+    const int incl = sh[tid];
+    __syncthreads();
+    return incl - v;
+}
+
+// One block of 1024 threads: counts[e] = sum over blocks; offsets = exclusive
+// scan; block_hist[b][e] is replaced by the absolute start of block b's
+// assignments of expert e.
+__global__ __launch_bounds__(1024) void scan_kernel(int32_t *__restrict__ block_hist,
+                                                    int32_t *__restrict__ counts,
+                                                    int32_t *__restrict__ offsets, int NB, int E, int A) {
+    __shared__ int sh[1024];
+    const int e = threadIdx.x;
+    int total = 0;
+    if (e < E)
+        for (int b = 0; b < NB; ++b) {
+            const int c = block_hist[(size_t)b * E + e];
+            block_hist[(size_t)b * E + e] = total;
+            total += c;
+        }
+    const int start = block_exclusive_scan(e < E ? total : 0, sh);
+    if (e < E) {
+        counts[e] = total;
+        offsets[e] = start;
+        for (int b = 0; b < NB; ++b) block_hist[(size_t)b * E + e] += start;
+    }
+    if (e == 0) offsets[E] = A;
+}
+
+// Stable rank of the assignments of one chunk, one wave, in 64-lane steps.
+// cnt[e] holds the next free position of expert e and is advanced here.
+__device__ __forceinline__ void rank_chunk(const int32_t *__restrict__ ids, int a0, int a1,
+                                           int *cnt, int nbits, int32_t *__restrict__ sorted_ids,
+                                           int32_t *__restrict__ inv) {
+    const int lane = threadIdx.x & 63;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int base = a0; base < a1; base += 64) {
+        const int a = base + lane;
+        const bool valid = a < a1;
+        const int e = valid ? ids[a] : 0;
+        const uint64_t m = match_lanes(e, valid, nbits);
+        const int rank = __popcll(m & below);
+        int pos = 0;
+        if (valid) pos = cnt[e] + rank;
+        // The highest lane of each group advances the counter after every
+        // lane of the wave has read it.
+        __builtin_amdgcn_wave_barrier();
+        if (valid && (m >> lane) == 1ull) cnt[e] = pos + 1;
+        __builtin_amdgcn_wave_barrier();
+        if (valid) {
+            sorted_ids[pos] = a;
+            inv[a] = pos;
+        }
+    }
+}
+
+// One wave per block: positions for the block's chunk.
+__global__ __launch_bounds__(64) void scatter_kernel(const int32_t *__restrict__ ids,
+                                                     const int32_t *__restrict__ block_base,
+                                                     int32_t *__restrict__ sorted_ids,
+                                                     int32_t *__restrict__ inv, int A, int E, int nbits) {
+    extern __shared__ int cnt[];
+    for (int e = threadIdx.x; e < E; e += 64) cnt[e] = block_base[(size_t)blockIdx.x * E + e];
+    __syncthreads();
+    const int a0 = blockIdx.x * kChunk;
+    rank_chunk(ids, a0, min(A, a0 + kChunk), cnt, nbits, sorted_ids, inv);
+}
+
+// Everything in one block when A <= kChunk: histogram, scan, scatter.
+__global__ __launch_bounds__(1024) void permute_small_kernel(const int32_t *__restrict__ ids,
+                                                             int32_t *__restrict__ counts,
+                                                             int32_t *__restrict__ offsets,
+                                                             int32_t *__restrict__ sorted_ids,
+                                                             int32_t *__restrict__ inv, int A, int E, int nbits) {
+    __shared__ int h[1024];
+    __shared__ int sh[1024];
+    const int tid = threadIdx.x;
+    if (tid < E) h[tid] = 0;
+    __syncthreads();
+    for (int a = tid; a < A; a += blockDim.x) atomicAdd(&h[ids[a]], 1);
+    __syncthreads();
+    const int c = tid < E ? h[tid] : 0;
+    const int start = block_exclusive_scan(c, sh);
+    if (tid < E) {
+        counts[tid] = c;
+        offsets[tid] = start;
+        h[tid] = start;
+    }
+    if (tid == 0) offsets[E] = A;
+    __syncthreads();
+    if (tid < 64) rank_chunk(ids, 0, A, h, nbits, sorted_ids, inv);
+}
+
+// x_perm[p] = x[sorted_ids[p] / k]: one wave per row, 16-byte vectors.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t *__restrict__ x,
+                                                          const int32_t *__restrict__ sorted_ids,
+                                                          uint16_t *__restrict__ x_perm, int A, int H, int k) {
+    const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (p >= A) return;
+    const int lane = threadIdx.x & 63;
+    const int t = sorted_ids[p] / k;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(x + (size_t)t * H);
+    u32x4 *dst = reinterpret_cast<u32x4 *>(x_perm + (size_t)p * H);
+    for (int c = lane; c < H / 8; c += 64) dst[c] = src[c];
+}
+
+static int bits_for(int E) {
+    int b = 0;
+    while ((1 << b) < E) ++b;
+    return b;
+}
+
+hipError_t launch_permute(const int32_t *ids, int32_t *counts, int32_t *offsets,
+                          int32_t *sorted_ids, int32_t *inv, int32_t *block_hist, int A, int E,
+                          hipStream_t st) {
+    const int nbits = bits_for(E);
+    if (A <= kChunk) {
+        permute_small_kernel<<<1, 1024, 0, st>>>(ids, counts, offsets, sorted_ids, inv, A, E, nbits);
+        return hipGetLastError();
+    }
+    const int NB = (A + kChunk - 1) / kChunk;
+    hist_kernel<<<NB, 256, E * sizeof(int32_t), st>>>(ids, block_hist, A, E);
+    scan_kernel<<<1, 1024, 0, st>>>(block_hist, counts, offsets, NB, E, A);
+    scatter_kernel<<<NB, 64, E * sizeof(int32_t), st>>>(ids, block_hist, sorted_ids, inv, A, E, nbits);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const uint16_t *x, const int32_t *sorted_ids, uint16_t *x_perm,
+                              int A, int H, int k, hipStream_t st) {
+    gather_rows_kernel<<<(A + 3) / 4, 256, 0, st>>>(x, sorted_ids, x_perm, A, H, k);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,119 @@
+"""The C ABI on the CPU: the library loads, exports every entry point of
+include/moe.h, and rejects bad arguments on the host before any HIP call.
+Every call here fails validation, so nothing is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_router_amd as moe
+from mixture_experts_router_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+FAKE = 0x100000          # a 256-byte aligned non-NULL address that is never dereferenced
+MIS = FAKE + 2            # misaligned
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return moe.load()
+
+
+def declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(moe_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_exports(lib):
+    names = declared()
+    assert set(names) == set(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n)
+
+
+def test_single_hip_runtime_in_process(lib):
+    maps = [l.split()[-1] for l in open("/proc/self/maps") if "libamdhip64" in l]
+    assert len(set(maps)) == 1
+
+
+def test_status_strings(lib):
+    for st, name in [(0, "ok"), (-1, "invalid"), (-2, "unsupported"), (-3, "workspace"), (-4, "HIP")]:
+        assert name in lib.moe_status_string(st).decode()
+    assert lib.moe_status_string(7) is not None
+
+
+def S(T=16, H=256, E=8, k=2, I=128, f=0):
+    return _lib.MoeShape(T, H, E, k, I, f)
+
+
+@pytest.mark.parametrize("s,expect", [
+    (S(T=0), -1), (S(H=0), -1), (S(E=0), -1), (S(k=0), -1), (S(I=0), -1), (S(k=9), -1),
+    (S(H=96), -2), (S(I=100), -2), (S(E=2000, k=8), -2), (S(E=64, k=33), -2), (S(f=2), -2),
+    (S(T=1 << 28, k=8), -2),
+])
+def test_bad_shapes_rejected_everywhere(lib, s, expect):
+    b = ctypes.byref(s)
+    F = FAKE
+    assert lib.moe_route(b, F, F, None, F, F, F, None) == expect
+    assert lib.moe_permute(b, F, None, F, F, F, F, None, F, 1 << 30, None) == expect
+    assert lib.moe_grouped_gemm_gateup(b, F, F, F, F, None, F, None) == expect
+    assert lib.moe_grouped_gemm_down(b, F, F, F, None, F, None) == expect
+    assert lib.moe_combine(b, F, F, F, F, None) == expect
+    assert lib.moe_forward(b, F, F, None, F, None, F, None, F, None, None, F, 1 << 40, None, None) == expect
+    assert lib.moe_workspace_bytes(b) == 0 and lib.moe_permute_workspace_bytes(b) == 0
+    assert lib.moe_route(None, F, F, None, F, F, F, None) == -1
+
+
+def test_null_and_misaligned_pointers(lib):
+    s = S()
+    b = ctypes.byref(s)
+    F = FAKE
+    assert lib.moe_route(b, F, None, None, F, F, F, None) == -1          # x without router weight
+    assert lib.moe_route(b, MIS, F, None, F, F, F, None) == -1           # misaligned x
+    assert lib.moe_route(b, None, None, None, None, F, F, None) == -1    # no logits
+    assert lib.moe_permute(b, None, None, F, F, F, F, None, F, 1 << 20, None) == -1
+    assert lib.moe_permute(b, F, F, F, F, F, F, None, F, 1 << 20, None) == -1   # x without x_perm
+    assert lib.moe_permute(b, F, None, F, F, F, F, None, None, 1 << 20, None) == -3
+    assert lib.moe_permute(b, F, None, F, F, F, F, None, F, 4, None) == -3
+    assert lib.moe_grouped_gemm_gateup(b, F, None, F, F, F, F, None) == -1     # bf16 with scales
+    assert lib.moe_grouped_gemm_gateup(b, F, None, F, MIS, None, F, None) == -1
+    mx = S(f=1)
+    assert lib.moe_grouped_gemm_gateup(ctypes.byref(mx), F, None, F, F, None, F, None) == -1  # mx without scales
+    assert lib.moe_grouped_gemm_down(b, F, F, None, None, F, None) == -1
+    assert lib.moe_combine(b, F, F, F, MIS, None) == -1
+    need = lib.moe_workspace_bytes(b)
+    assert need > 0
+    assert lib.moe_forward(b, F, F, None, F, None, F, None, F, None, None, F, need - 1, None, None) == -3
+    assert lib.moe_forward(b, F, F, None, F, None, F, None, F, None, None, None, need, None, None) == -3
+    ev = (ctypes.c_void_p * 6)(F, F, F, None, F, F)
+    assert lib.moe_forward(b, F, F, None, F, None, F, None, F, None, None, F, need,
+                           None, ctypes.cast(ev, ctypes.c_void_p)) == -1
+
+
+def test_workspace_monotone_in_T(lib):
+    prev = 0
+    for T in (1, 7, 8, 100, 2048, 8192):
+        s = _lib.MoeShape(T, 2816, 128, 8, 704, 0)
+        n = lib.moe_workspace_bytes(ctypes.byref(s))
+        assert n > prev and n % 256 == 0
+        prev = n
+    s = _lib.MoeShape(2048, 2816, 128, 8, 704, 0)
+    # h and y dominate: T*k*(I + H) bf16
+    assert lib.moe_workspace_bytes(ctypes.byref(s)) >= 2048 * 8 * (704 + 2816) * 2
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.load.__wrapped__(str(tmp_path / "nope.so")) if hasattr(_lib.load, "__wrapped__") else \
+            _load_fresh(str(tmp_path / "nope.so"))
+
+
+def _load_fresh(path):
+    saved = _lib._lib
+    _lib._lib = None
+    try:
+        return _lib.load(path)
+    finally:
+        _lib._lib = saved

@@ -1,0 +1,115 @@
+"""End-to-end parity of moe_forward against the fp64 oracle.
+
+Small problems are compared in full; the four Gemma-4-26B-A4B workloads
+(decode T=8, prefill T=2048, Zipf-skewed T=8192, MXFP4 experts T=2048) run in
+the launch configuration the benchmark times and are compared on the whole
+routing table plus a sample of tokens the oracle evaluates one by one."""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+import oracle
+import mixture_experts_router_amd as moe
+from mixture_experts_router_amd import device as dev
+from gpu_helpers import say, upload, run_forward, to64, check_layer, TIE_MARGIN
+
+pytestmark = pytest.mark.gpu
+
+
+SMALL = {
+    "tiny": mi.CONFIGS["tiny"],
+    "ragged": mi.Shape(T=300, H=512, E=16, k=4, I=192),
+    "ragged-skew": mi.Shape(T=300, H=512, E=16, k=4, I=192, skew=True),
+    "ragged-mxfp4": mi.Shape(T=300, H=512, E=16, k=4, I=192, mxfp4=True),
+    "one-token": mi.Shape(T=1, H=256, E=8, k=2, I=128),
+    "k-equals-E": mi.Shape(T=40, H=256, E=8, k=8, I=128),
+    "many-experts": mi.Shape(T=130, H=256, E=300, k=6, I=64),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_forward_small_full_compare(gpu, name):
+    s = SMALL[name]
+    say(f"forward {name}: {s}")
+    inp = mi.make(s, seed=2)
+    out, ids, w = run_forward(inp)
+    ref = oracle.forward(inp)
+    check_layer(to64(out), ids.cpu().numpy(), w.cpu().numpy(), ref["ids"], ref["w"], ref["out"],
+                ref["margin"], name)
+
+
+def test_forward_zero_input_is_zero(gpu):
+    inp = mi.make(mi.Shape(T=50, H=256, E=8, k=2, I=128), seed=3)
+    inp.x[:] = 0
+    out, ids, w = run_forward(inp)
+    assert (out.float() == 0).all()
+    assert (ids.cpu().numpy() == np.arange(2)).all()      # all logits 0: lowest indices
+    assert (w.cpu().numpy() == 0.5).all()
+
+
+def test_forward_single_hot_expert(gpu):
+    """A bias that sends every token to the same experts: two experts own all
+    rows, the rest are empty."""
+    s = mi.Shape(T=700, H=256, E=16, k=2, I=128)
+    inp = mi.make(s, seed=4)
+    inp.router_bias = np.full(16, -100.0, dtype=np.float32)
+    inp.router_bias[[3, 11]] = 100.0
+    out, ids, w = run_forward(inp)
+    ref = oracle.forward(inp)
+    assert set(np.unique(ids.cpu().numpy())) == {3, 11}
+    check_layer(to64(out), ids.cpu().numpy(), w.cpu().numpy(), ref["ids"], ref["w"], ref["out"],
+                ref["margin"], "single hot expert")
+
+
+def test_forward_is_deterministic_and_reusable(gpu):
+    big = mi.make(mi.Shape(T=700, H=512, E=16, k=4, I=192), seed=6)
+    small = mi.make(mi.Shape(T=9, H=512, E=16, k=4, I=192), seed=6)
+    db, ds = upload(big), upload(small)
+    ws = dev.workspace(db["shape"])
+    o1, _, _ = run_forward(big, db, ws)
+    o2, _, _ = run_forward(small, ds, ws)       # same workspace, smaller T
+    o3, _, _ = run_forward(big, db, ws)
+    o4, _, _ = run_forward(small, ds)
+    assert (dev.bf16_bits(o1) == dev.bf16_bits(o3)).all()
+    assert (dev.bf16_bits(o2) == dev.bf16_bits(o4)).all()
+
+
+# ---------------------------------------------------------------- full sizes
+def _sample_tokens(ids, T, n, seed):
+    """Random tokens plus the first/last token and tokens of the busiest expert."""
+    rng = np.random.default_rng(seed)
+    counts = np.bincount(ids.reshape(-1), minlength=ids.max() + 1)
+    hot = int(np.argmax(counts))
+    hot_tok = np.nonzero((ids == hot).any(axis=1))[0]
+    pick = set(rng.choice(T, size=min(n, T), replace=False).tolist())
+    pick |= {0, T - 1}
+    pick |= set(hot_tok[-4:].tolist())
+    return np.array(sorted(pick))
+
+
+@pytest.mark.parametrize("name", ["decode", "prefill", "skew", "mxfp4"])
+def test_forward_full_size(gpu, name):
+    s = mi.CONFIGS[name]
+    say(f"forward full size {name}: {s}")
+    inp = mi.make(name, seed=0)
+    out, ids, w = run_forward(inp)
+    ids_np, w_np = ids.cpu().numpy(), w.cpu().numpy()
+    # whole routing table against fp64 routing
+    L = oracle.router_logits(oracle.bf16_to_f64(inp.x), oracle.bf16_to_f64(inp.w_router), inp.router_bias)
+    rid, rw = oracle.topk_softmax(L, s.k)
+    margin = oracle.routing_margin(L, s.k)
+    keep = margin >= TIE_MARGIN
+    flips = np.array([set(a) != set(b) for a, b in zip(ids_np, rid)])
+    counts = np.bincount(ids_np.reshape(-1), minlength=s.E)
+    say(f"  near ties {int((~keep).sum())}, flips outside ties {int((flips & keep).sum())}, "
+        f"counts min {counts.min()} max {counts.max()} empty {int((counts == 0).sum())}")
+    assert not (flips & keep).any()
+    assert counts.sum() == s.T * s.k
+    assert all(len(set(r)) == s.k for r in ids_np)
+    assert np.abs(w_np.sum(axis=1) - 1).max() <= 1e-6
+    # sampled outputs
+    tok = np.arange(s.T) if s.T <= 16 else _sample_tokens(ids_np, s.T, 40, seed=1)
+    ref = oracle.forward_tokens(inp, tok)
+    check_layer(to64(out)[tok], ids_np[tok], w_np[tok], ref["ids"], ref["w"], ref["out"],
+                ref["margin"], f"{name} ({len(tok)} sampled tokens)")
