@@ -176,16 +176,27 @@ def main():
     alg = algorithmic(inp, ids_np)
 
     K = args.steps
-    ev = dev.StageEvents(K)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+
+    # Timed region 1: K plain steps -> ms_per_step and value.
     torch.cuda.synchronize()
     start.record()
     for i in range(K):
-        step(i, ev.arrays[i])
+        step(i)
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / K
+
+    # Timed region 2: K more steps with the library recording HIP events on
+    # its launch stream between the stages -> per-kernel durations.  (An event
+    # between two kernels adds a gap of a few microseconds, which is why the
+    # step time comes from region 1.)
+    ev = dev.StageEvents(K)
+    torch.cuda.synchronize()
+    for i in range(K):
+        step(i, ev.arrays[i])
+    torch.cuda.synchronize()
     stage_ms = np.array([ev.stage_ms(i) for i in range(K)])      # [K, 5]
     ev.close()
     stage_avg_us = {n: float(v) * 1e3 for n, v in zip(STAGES, stage_ms.mean(axis=0))}

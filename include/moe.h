@@ -99,10 +99,12 @@ typedef void *moe_event_t;  /* hipEvent_t */
  *   router_bias  [E] fp32 or NULL
  *   logits       [T][E] fp32: output when x != NULL, input when x == NULL
  *   topk_ids     [T][k] int32 out;  topk_w [T][k] fp32 out (rows sum to 1)
+ *   ws           device scratch of at least moe_route_workspace_bytes(s)
+ *                (may be NULL when that is 0 or when x == NULL)
  */
 int moe_route(const moe_shape *s, const uint16_t *x, const uint16_t *w_router,
               const float *router_bias, float *logits, int32_t *topk_ids,
-              float *topk_w, moe_stream_t stream);
+              float *topk_w, void *ws, size_t ws_bytes, moe_stream_t stream);
 
 /*
  * moe_permute -- expert histogram, prefix scan and stable scatter: the
@@ -182,6 +184,11 @@ int moe_forward(const moe_shape *s, const uint16_t *x, const uint16_t *w_router,
 /* Workspace bytes moe_forward needs for this shape; 0 for an invalid or
  * unsupported shape.  Monotone in T. */
 size_t moe_workspace_bytes(const moe_shape *s);
+
+/* Workspace bytes moe_route needs for this shape (0: none needed, or an
+ * invalid shape).  Few tokens use a split-K router with per-chunk partial
+ * sums; many tokens need no scratch. */
+size_t moe_route_workspace_bytes(const moe_shape *s);
 
 /* Workspace bytes moe_permute needs for this shape; 0 if invalid. */
 size_t moe_permute_workspace_bytes(const moe_shape *s);

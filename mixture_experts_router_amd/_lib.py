@@ -16,8 +16,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARGUMENT", -2: "MOE_ERR_UNSUPPORTED"
 
 # Entry points declared in include/moe.h.
 EXPORTS = ("moe_route", "moe_permute", "moe_grouped_gemm_gateup", "moe_grouped_gemm_down",
-           "moe_combine", "moe_forward", "moe_workspace_bytes", "moe_permute_workspace_bytes",
-           "moe_status_string")
+           "moe_combine", "moe_forward", "moe_workspace_bytes", "moe_route_workspace_bytes",
+           "moe_permute_workspace_bytes", "moe_status_string")
 
 
 class MoeShape(ctypes.Structure):
@@ -52,7 +52,7 @@ def load(path: str = LIB_PATH):
     lib = ctypes.CDLL(path)
     c_int, c_size = ctypes.c_int, ctypes.c_size_t
     sig = {
-        "moe_route": [_S, _P, _P, _P, _P, _P, _P, _P],
+        "moe_route": [_S, _P, _P, _P, _P, _P, _P, _P, c_size, _P],
         "moe_permute": [_S, _P, _P, _P, _P, _P, _P, _P, _P, c_size, _P],
         "moe_grouped_gemm_gateup": [_S, _P, _P, _P, _P, _P, _P, _P],
         "moe_grouped_gemm_down": [_S, _P, _P, _P, _P, _P, _P],
@@ -63,7 +63,7 @@ def load(path: str = LIB_PATH):
         f = getattr(lib, name)
         f.argtypes = args
         f.restype = c_int
-    for name in ("moe_workspace_bytes", "moe_permute_workspace_bytes"):
+    for name in ("moe_workspace_bytes", "moe_route_workspace_bytes", "moe_permute_workspace_bytes"):
         f = getattr(lib, name)
         f.argtypes = [_S]
         f.restype = c_size
@@ -106,14 +106,20 @@ def workspace_bytes(s: MoeShape) -> int:
     return load().moe_workspace_bytes(ctypes.byref(s))
 
 
+def route_workspace_bytes(s: MoeShape) -> int:
+    return load().moe_route_workspace_bytes(ctypes.byref(s))
+
+
 def permute_workspace_bytes(s: MoeShape) -> int:
     return load().moe_permute_workspace_bytes(ctypes.byref(s))
 
 
-def route(s, x, w_router, router_bias, logits, topk_ids, topk_w, stream=None):
+def route(s, x, w_router, router_bias, logits, topk_ids, topk_w, ws=None, stream=None):
     lib = load()
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check("moe_route", lib.moe_route(ctypes.byref(s), _ptr(x), _ptr(w_router), _ptr(router_bias),
-                                      _ptr(logits), _ptr(topk_ids), _ptr(topk_w), _stream(stream)))
+                                      _ptr(logits), _ptr(topk_ids), _ptr(topk_w), _ptr(ws), nbytes,
+                                      _stream(stream)))
 
 
 def permute(s, topk_ids, x, counts, offsets, sorted_ids, inv, x_perm, ws, stream=None):

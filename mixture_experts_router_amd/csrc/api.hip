@@ -33,6 +33,24 @@ int num_blocks(const moe_shape *s) {
 
 size_t permute_ws(const moe_shape *s) { return round_up((size_t)num_blocks(s) * s->E * sizeof(int32_t)); }
 
+// fp32 chunk partials of the split-K router (few tokens only).
+size_t route_ws(const moe_shape *s) {
+    if (!moe::router_uses_partials(s->T)) return 0;
+    return round_up((size_t)moe::router_chunks(s->H) * s->T * s->E * sizeof(float));
+}
+
+int launch_route(const moe_shape *s, const uint16_t *x, const uint16_t *w_router, const float *bias,
+                 float *logits, int32_t *ids, float *w, float *part, hipStream_t hs) {
+    if (moe::router_uses_partials(s->T)) {
+        if (moe::launch_router_partials(x, w_router, part, s->T, s->H, s->E, hs) != hipSuccess) return MOE_ERR_HIP;
+        return moe::launch_topk(part, moe::router_chunks(s->H), bias, logits, ids, w, s->T, s->E, s->k, hs) ==
+                       hipSuccess ? MOE_OK : MOE_ERR_HIP;
+    }
+    if (moe::launch_router_dense(x, w_router, bias, logits, s->T, s->H, s->E, hs) != hipSuccess) return MOE_ERR_HIP;
+    return moe::launch_topk(nullptr, 0, nullptr, logits, ids, w, s->T, s->E, s->k, hs) == hipSuccess ? MOE_OK
+                                                                                                      : MOE_ERR_HIP;
+}
+
 // Weight pointers: bf16 weights must be 16-byte aligned and come without
 // scales; MXFP4 codes must be 4-byte aligned and come with scales.
 int check_weights(const moe_shape *s, const void *w, const uint8_t *scales) {
@@ -46,6 +64,7 @@ int check_weights(const moe_shape *s, const void *w, const uint8_t *scales) {
 }
 
 struct Workspace {
+    float *part;
     float *logits;
     int32_t *ids;
     float *w;
@@ -64,6 +83,7 @@ Workspace carve(const moe_shape *s, void *base) {
         off += round_up(bytes);
         return q;
     };
+    w.part = reinterpret_cast<float *>(take(route_ws(s)));
     w.logits = reinterpret_cast<float *>(take(T * E * sizeof(float)));
     w.ids = reinterpret_cast<int32_t *>(take(A * sizeof(int32_t)));
     w.w = reinterpret_cast<float *>(take(A * sizeof(float)));
@@ -100,13 +120,18 @@ size_t moe_workspace_bytes(const moe_shape *s) {
     return carve(s, nullptr).bytes;
 }
 
+size_t moe_route_workspace_bytes(const moe_shape *s) {
+    if (check_shape(s) != MOE_OK) return 0;
+    return route_ws(s);
+}
+
 size_t moe_permute_workspace_bytes(const moe_shape *s) {
     if (check_shape(s) != MOE_OK) return 0;
     return permute_ws(s);
 }
 
 int moe_route(const moe_shape *s, const uint16_t *x, const uint16_t *w_router, const float *router_bias,
-              float *logits, int32_t *topk_ids, float *topk_w, moe_stream_t stream) {
+              float *logits, int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes, moe_stream_t stream) {
     int st = check_shape(s);
     if (st != MOE_OK) return st;
     if (!logits || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARGUMENT;
@@ -114,13 +139,14 @@ int moe_route(const moe_shape *s, const uint16_t *x, const uint16_t *w_router, c
     if (x) {
         if (!w_router || !al16(x) || !al16(w_router)) return MOE_ERR_INVALID_ARGUMENT;
         if (router_bias && !al4(router_bias)) return MOE_ERR_INVALID_ARGUMENT;
+        const size_t need = route_ws(s);
+        if (need && (!ws || ws_bytes < need || !al4(ws))) return MOE_ERR_WORKSPACE;
     }
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    if (x) {
-        st = hip_status(moe::launch_router_gemm(x, w_router, router_bias, logits, s->T, s->H, s->E, hs));
-        if (st != MOE_OK) return st;
-    }
-    return hip_status(moe::launch_topk(logits, topk_ids, topk_w, s->T, s->E, s->k, hs));
+    if (x) return launch_route(s, x, w_router, router_bias, logits, topk_ids, topk_w, static_cast<float *>(ws), hs);
+    return moe::launch_topk(nullptr, 0, nullptr, logits, topk_ids, topk_w, s->T, s->E, s->k, hs) == hipSuccess
+               ? MOE_OK
+               : MOE_ERR_HIP;
 }
 
 int moe_permute(const moe_shape *s, const int32_t *topk_ids, const uint16_t *x, int32_t *counts,
@@ -209,11 +235,23 @@ int moe_forward(const moe_shape *s, const uint16_t *x, const uint16_t *w_router,
         return hip_status(hipEventRecord(static_cast<hipEvent_t>(stage_events[stage++]), hs));
     };
     if ((st = mark()) != MOE_OK) return st;
-    st = hip_status(moe::launch_router_gemm(x, w_router, router_bias, w.logits, T, H, E, hs));
-    if (st == MOE_OK) st = hip_status(moe::launch_topk(w.logits, ids, wts, T, E, k, hs));
-    if (st != MOE_OK || (st = mark()) != MOE_OK) return st;
-    st = hip_status(moe::launch_permute(ids, w.counts, w.offsets, w.sorted_ids, w.inv, w.block_hist, A, E, hs));
-    if (st != MOE_OK || (st = mark()) != MOE_OK) return st;
+    if (moe::router_uses_partials(T) && moe::topk_permute_fits(T, k)) {
+        // few tokens: split-K router, then top-k and the permutation in one
+        // launch (the permute stage is empty)
+        st = hip_status(moe::launch_router_partials(x, w_router, w.part, T, H, E, hs));
+        if (st == MOE_OK)
+            st = hip_status(moe::launch_topk_permute_small(w.part, moe::router_chunks(H), router_bias, w.logits,
+                                                           ids, wts, w.counts, w.offsets, w.sorted_ids, w.inv,
+                                                           T, E, k, hs));
+        if (st != MOE_OK || (st = mark()) != MOE_OK) return st;
+        if ((st = mark()) != MOE_OK) return st;
+    } else {
+        st = launch_route(s, x, w_router, router_bias, w.logits, ids, wts, w.part, hs);
+        if (st != MOE_OK || (st = mark()) != MOE_OK) return st;
+        st = hip_status(
+            moe::launch_permute(ids, w.counts, w.offsets, w.sorted_ids, w.inv, w.block_hist, A, E, hs));
+        if (st != MOE_OK || (st = mark()) != MOE_OK) return st;
+    }
     st = hip_status(moe::launch_gateup(x, w.sorted_ids, k, w.offsets, w_gate_up, gu_scales, w.h, A, H, E, I, mx, hs));
     if (st != MOE_OK || (st = mark()) != MOE_OK) return st;
     st = hip_status(moe::launch_down(w.h, w.offsets, w_down, d_scales, w.y, A, H, E, I, mx, hs));

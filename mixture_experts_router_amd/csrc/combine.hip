@@ -27,13 +27,22 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
         float acc[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) acc[q] = 0.f;
-        for (int j = 0; j < k; ++j) {
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(y + (size_t)s_row[j] * H + c * 8);
-            const float wj = s_w[j];
+        // rows in batches of 8 loads in flight, summed in ascending j
+        for (int j0 = 0; j0 < k; j0 += 8) {
+            u32x4 v[8];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                acc[2 * q] = fmaf(wj, bf16_to_f32(v[q] & 0xFFFFu), acc[2 * q]);
-                acc[2 * q + 1] = fmaf(wj, bf16_to_f32(v[q] >> 16), acc[2 * q + 1]);
+            for (int u = 0; u < 8; ++u)
+                v[u] = (j0 + u < k) ? *reinterpret_cast<const u32x4 *>(y + (size_t)s_row[j0 + u] * H + c * 8)
+                                    : u32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (j0 + u >= k) break;
+                const float wj = s_w[j0 + u];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    acc[2 * q] = fmaf(wj, bf16_to_f32(v[u][q] & 0xFFFFu), acc[2 * q]);
+                    acc[2 * q + 1] = fmaf(wj, bf16_to_f32(v[u][q] >> 16), acc[2 * q + 1]);
+                }
             }
         }
         u32x4 o;

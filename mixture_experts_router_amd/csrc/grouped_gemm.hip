@@ -9,45 +9,36 @@
 // order; for gate/up those rows may be gathered straight from x through
 // sorted_ids, so the dispatched copy of x is never written to HBM.  The
 // grouped matmul of the pages (SwiftGMM, Pangu Pro MoE summary article,
-// group 4) is prior art; this is a bf16 MFMA kernel with LDS-staged tiles.
+// group 4) is prior art only.
 //
-// Workgroup = 4 waves = WAVES_M x WAVES_N; tile BM rows x BN columns, K steps
-// of 64 staged through double-buffered LDS from registers.  For gate/up the
-// BN columns are BN/2 gate rows and the BN/2 matching up rows of the weight,
-// laid out so each wave holds gate column n and up column I + n in the same
-// lanes and registers, and the GEGLU runs on the fp32 accumulators.
+// Workgroup = 4 waves = WAVES_M (token direction) x WAVES_N (weight-row
+// direction); tile BM tokens x BN weight rows, K in steps of 64.  Two K steps
+// are in flight per workgroup: while the waves multiply step kt out of LDS,
+// the registers hold step kt+1 (landing) and the loads of step kt+2 are
+// issued.  The MFMA takes the weight tile as its A operand and the tokens as
+// B, so each lane ends with four consecutive output columns of one token and
+// stores them as one 8-byte word.
 //
-// The launch grid is static: blockIdx.x = N tile, blockIdx.y = M-tile slot.
-// Each workgroup finds its (expert, row block) from the offsets; slots past
-// the last tile exit at once, and an empty expert owns no tile, so its
-// weights are never read.
+// For gate/up the BN weight rows of a tile are BN/2 gate rows and the BN/2
+// matching up rows, interleaved per wave so that gate column n and up column
+// I + n land in the same lane and register; the GEGLU runs on the fp32
+// accumulators.  MXFP4 weights stay packed in LDS (4 bits per value plus one
+// scale byte per 32) and are expanded to bf16 by the hardware scaled FP4
+// conversion when each fragment is read.
+//
+// The launch grid is static (one dimension, N tiles x M-tile slots, dealt
+// to the XCDs in groups).  Each workgroup finds its (expert, row block) from the offsets; slots past
+// the last tile exit at once, an empty expert owns no tile (its weights are
+// never read), and waves whose rows all lie past the expert's last row skip
+// their MFMAs.
+#include <type_traits>
+
 #include "moe_common.h"
 #include "moe_launch.h"
 
 namespace moe {
 
-// bf16 bits of an E2M1 code scaled by 2^(sexp): the magnitude (3 bits) is
-// 0, 0.5, 1, 1.5, 2, 3, 4, 6; bit 3 is the sign.  The result is exact when
-// it is a normal bf16 number.
-__device__ __forceinline__ uint32_t e2m1_to_bf16(uint32_t c, int sexp) {
-    const uint32_t m = c & 7u;
-    uint32_t bits = (m == 1u) ? (126u << 7) : (((126u + (m >> 1)) << 7) | ((m & 1u) << 6));
-    bits = (m == 0u) ? 0u : (uint32_t)((int)bits + (sexp << 7));
-    return bits | ((c & 8u) << 12);
-}
-
-// Eight codes (low nibble first) and one E8M0 scale byte -> 8 bf16 values.
-__device__ __forceinline__ u32x4 dequant8(uint32_t codes, uint32_t sbyte) {
-    const int sexp = (int)sbyte - 127;
-    u32x4 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = e2m1_to_bf16((codes >> (8 * i)) & 15u, sexp);
-        const uint32_t hi = e2m1_to_bf16((codes >> (8 * i + 4)) & 15u, sexp);
-        r[i] = lo | (hi << 16);
-    }
-    return r;
-}
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 struct GemmArgs {
     const uint16_t *a;        // activations: x (gather), x_perm or h
@@ -59,6 +50,11 @@ struct GemmArgs {
     uint16_t *out;            // [A][n_out] bf16
     int E, K, n_out, I;       // I: gate/up split (gate/up only)
     int w_rows;               // weight rows per expert (2I or H)
+    int n_tiles;              // N tiles per M tile
+    // dense router mode: one group of `dense_rows` tokens, fp32 output
+    int dense_rows;
+    float *out32;             // [T][E] logits
+    const float *bias;        // [E] or nullptr
 };
 
 // Locate this workgroup's M tile: tile index -> (expert, first row).  Run by
@@ -99,185 +95,365 @@ __device__ __forceinline__ void find_tile(const int32_t *__restrict__ offsets, i
     if (!found && lane == 0) s_info[0] = -1;
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool GEGLU, bool MX>
-__global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs p) {
+enum GemmMode { kDown = 0, kGateUp = 1, kRouter = 2 };
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int MODE, bool MX, int NS_>
+struct GemmTile {
+    static constexpr bool GEGLU = MODE == kGateUp;
+    static constexpr int BK = 64;
+    static constexpr int NS = NS_;                // LDS stages (NS - 1 loads ahead)
+    static constexpr int WTM = BM / WAVES_M;      // tokens per wave
+    static constexpr int WN = BN / WAVES_N;       // weight rows per wave
+    static constexpr int MI = WTM / 16;           // token tiles per wave (MFMA B operand)
+    static constexpr int NI = WN / 16;            // weight-row tiles per wave (MFMA A operand)
+    // Direct-to-LDS loads move 1 KB per wave instruction (64 lanes x 16 B):
+    // 8 rows of 64 bf16.
+    static constexpr int NA = BM / 8;             // token-tile instructions per stage
+    static constexpr int NB = MX ? 0 : BN / 8;    // bf16 weight-tile instructions per stage
+    static constexpr int A_W = (NA + 3) / 4;      // per wave (upper bound)
+    static constexpr int B_W = (NB + 3) / 4;
+    // Loads every wave issues per stage at least (waves with more wait a
+    // little longer, never too short).
+    static constexpr int DMA_MIN = NA / 4 + NB / 4;
+    // MXFP4 weights: BN rows x 2 chunks of 16 bytes (64 codes) + 2 scale bytes,
+    // staged through registers.
+    static constexpr int MB_CHUNKS = MX ? BN * 2 : 0;
+    static constexpr int MB_PER = MX ? (MB_CHUNKS + 255) / 256 : 1;
+    static constexpr int MS_PER = MX ? (BN + 255) / 256 : 1;
+    static constexpr int A_LDS = BM * BK;                      // uint16 per stage
+    static constexpr int B_LDS = MX ? BN * BK / 4 : BN * BK;   // uint16 per stage
     static_assert(WAVES_M * WAVES_N == 4, "four waves");
-    constexpr int BK = 64;
-    constexpr int WTM = BM / WAVES_M;     // rows per wave
-    constexpr int WN = BN / WAVES_N;      // columns per wave
-    constexpr int MI = WTM / 16, NI = WN / 16;
     static_assert(MI >= 1 && NI >= 1, "tile too small");
     static_assert(!GEGLU || (NI % 2 == 0), "GEGLU pairs gate and up tiles");
-    constexpr int A_CHUNKS = BM * 8;      // 16-byte chunks per A tile
-    constexpr int B_CHUNKS = BN * 8;
-    constexpr int A_PER = (A_CHUNKS + 255) / 256;
-    constexpr int B_PER = (B_CHUNKS + 255) / 256;
+    static_assert(BM % 8 == 0 && BN % 8 == 0, "whole 1 KB load groups");
+    static_assert(NS >= 2 && NS <= 8, "stages");
+    // MXFP4 codes go through registers one step ahead; the wait counts
+    // below assume at most one DMA step is issued after them.
+    static_assert(!MX || NS <= 3, "MXFP4 pipeline depth");
+};
 
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * BK];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * BK];
+// s_waitcnt with vmcnt = VM and lgkmcnt = 0 (expcnt left at its maximum).
+template <int VM>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+    static_assert(VM >= 0 && VM < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
+}
+
+// 16-byte direct global->LDS load of one wave: lane l's 16 bytes from `g`
+// land at lds + 16 l.  Issued from inline asm so that the compiler adds no
+// waits of its own on later LDS reads (it cannot tell the stage buffers
+// apart); every wait is the explicit s_waitcnt of the pipeline below.  The
+// asm has no register outputs, and M0 is only ever set here.
+__device__ __forceinline__ void dma16(const void *g, const void *lds) {
+    const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(l) : "memory", "m0");
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int MODE, bool MX, int NS_>
+__global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs p) {
+    using G = GemmTile<BM, BN, WAVES_M, WAVES_N, MODE, MX, NS_>;
+    constexpr bool GEGLU = MODE == kGateUp, ROUTER = MODE == kRouter;
+    constexpr int BK = G::BK, NS = G::NS, WTM = G::WTM, WN = G::WN, MI = G::MI, NI = G::NI;
+    constexpr int NA = G::NA, NB = G::NB, A_W = G::A_W, B_W = G::B_W;
+
+    // bf16 tiles: [row][8 chunks of 16 B], chunk index XOR-swizzled by row.
+    // MXFP4 codes: [chunk (8 words of 4 B)][row]; scales: [2 blocks][row].
+    __shared__ __attribute__((aligned(1024))) uint16_t As[NS][G::A_LDS];
+    __shared__ __attribute__((aligned(1024))) uint16_t Bs[NS][G::B_LDS];
+    __shared__ __attribute__((aligned(16))) uint8_t Ss[NS][MX ? 2 * BN : 1];
     __shared__ int s_info[4];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (wave == 0) find_tile<BM>(p.offsets, p.E, blockIdx.y, s_info);
-    __syncthreads();
-    const int e = s_info[0];
-    if (e < 0) return;
-    const int m0 = s_info[1];
-    const int rows = min(BM, s_info[2] - m0);   // valid rows of this tile
-    const int seg = s_info[3] + m0;             // global row of tile row 0
-    const int K = p.K;
-    const int nt = blockIdx.x;
-
-    // ---- per-thread global sources for the A and B chunks
-    const uint16_t *a_src[A_PER];
-    bool a_ok[A_PER];
-#pragma unroll
-    for (int i = 0; i < A_PER; ++i) {
-        const int c = tid + 256 * i;
-        const int r = c >> 3, ch = c & 7;
-        a_ok[i] = (c < A_CHUNKS) && (r < rows);
-        size_t row = 0;
-        if (a_ok[i]) row = p.gather ? (size_t)(p.gather[seg + r] / p.gather_k) : (size_t)(seg + r);
-        a_src[i] = p.a + row * K + ch * 8;
+    // XCD-aware tile order.  Workgroups go to the 8 XCDs round-robin (block
+    // b -> XCD b % 8).  The N tiles of one M tile form a group that shares
+    // its token rows; groups are dealt to XCDs round-robin (group m -> XCD
+    // m % 8) and each XCD runs its groups in order, so a group's token rows
+    // stay in one XCD's L2 while the empty slots at the end of the grid are
+    // spread evenly over the XCDs.
+    // Small row blocks share little: there the plain order (N tile fastest)
+    // spreads each expert's weight slabs over all XCDs.
+    int mslot, nt;
+    if (BM >= 64) {
+        const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+        mslot = xcd + 8 * (j / p.n_tiles);
+        nt = j % p.n_tiles;
+    } else {
+        mslot = blockIdx.x / p.n_tiles;
+        nt = blockIdx.x % p.n_tiles;
     }
-    const char *b_src[B_PER];
-    const uint8_t *s_src[B_PER];
-    bool b_ok[B_PER];
-#pragma unroll
-    for (int i = 0; i < B_PER; ++i) {
-        const int c = tid + 256 * i;
-        const int v = c >> 3, ch = c & 7;
-        int wrow;
-        bool ok = c < B_CHUNKS;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
+    int e, m0, rows, seg;
+    if (ROUTER) {                               // one dense group of tokens
+        if (mslot * BM >= p.dense_rows) return;
+        e = 0;
+        m0 = mslot * BM;
+        rows = min(BM, p.dense_rows - m0);
+        seg = m0;
+    } else {
+        if (wave == 0) find_tile<BM>(p.offsets, p.E, mslot, s_info);
+        __syncthreads();
+        e = __builtin_amdgcn_readfirstlane(s_info[0]);
+        if (e < 0) return;
+        m0 = __builtin_amdgcn_readfirstlane(s_info[1]);
+        rows = min(BM, __builtin_amdgcn_readfirstlane(s_info[2]) - m0);   // valid tokens of this tile
+        seg = __builtin_amdgcn_readfirstlane(s_info[3]) + m0;             // global row of tile token 0
+    }
+    const int K = p.K;
+    const int KT = K / BK;
+
+    // Weight row of tile row v (0 <= v < BN), clamped to a valid row.
+    auto weight_row = [&](int v) -> int {
         if (GEGLU) {
             const int half = WN / 2;
             const int wn = v / WN, within = v % WN;
             const int n = nt * (BN / 2) + wn * half + (within % half);
-            ok = ok && n < p.I;
-            wrow = within < half ? n : p.I + n;
-        } else {
-            wrow = nt * BN + v;
-            ok = ok && wrow < p.n_out;
+            return n < p.I ? (within < half ? n : p.I + n) : 0;
         }
-        b_ok[i] = ok;
-        if (!ok) wrow = 0;
-        const size_t rid = (size_t)e * p.w_rows + wrow;
-        if (MX) {
-            b_src[i] = reinterpret_cast<const char *>(p.w) + rid * (K / 2) + ch * 4;
-            s_src[i] = p.scales + rid * (K / 32) + (ch >> 2);
-        } else {
-            b_src[i] = reinterpret_cast<const char *>(p.w) + (rid * K + ch * 8) * 2;
-            s_src[i] = nullptr;
-        }
-    }
+        const int r = nt * BN + v;
+        return r < p.n_out ? r : 0;
+    };
 
-    u32x4 ra[A_PER], rb[B_PER];
-    auto load = [&](int kt) {
+    // ---- direct-to-LDS sources.  Instruction g fills rows 8g..8g+7 of the
+    // stage buffer; lane l lands at row 8g + l/8, physical chunk l%8, so it
+    // fetches logical chunk (l%8) ^ swizzle(row).  A token row past the
+    // tile's end reads the tile's first row and a weight row past the matrix
+    // reads row 0; both only feed outputs that are never stored.
+    const int lr = lane >> 3, lc = lane & 7;
+    const uint16_t *a_src[A_W];
 #pragma unroll
-        for (int i = 0; i < A_PER; ++i)
-            ra[i] = a_ok[i] ? *reinterpret_cast<const u32x4 *>(a_src[i] + kt * BK) : u32x4{0, 0, 0, 0};
+    for (int q = 0; q < A_W; ++q) {
+        const int g = q * 4 + wave;
+        const int row = 8 * (g < NA ? g : 0) + lr;
+        const int rr = row < rows ? row : 0;
+        const size_t src = p.gather ? (size_t)(p.gather[seg + rr] / p.gather_k) : (size_t)(seg + rr);
+        a_src[q] = p.a + src * K + 8 * (lc ^ ((row ^ (row >> 3)) & 7));
+    }
+    const uint16_t *b_src[B_W > 0 ? B_W : 1];
 #pragma unroll
-        for (int i = 0; i < B_PER; ++i) {
-            if (MX) {
-                if (b_ok[i]) {
-                    const uint32_t codes = *reinterpret_cast<const uint32_t *>(b_src[i] + kt * (BK / 2));
-                    const uint32_t sb = s_src[i][kt * (BK / 32)];
-                    rb[i] = dequant8(codes, sb);
-                } else {
-                    rb[i] = u32x4{0, 0, 0, 0};
-                }
-            } else {
-                rb[i] = b_ok[i] ? *reinterpret_cast<const u32x4 *>(b_src[i] + kt * BK * 2) : u32x4{0, 0, 0, 0};
-            }
+    for (int q = 0; q < B_W; ++q) {
+        const int g = q * 4 + wave;
+        const int row = 8 * (g < NB ? g : 0) + lr;
+        const size_t rid = (size_t)e * p.w_rows + weight_row(row);
+        b_src[q] = reinterpret_cast<const uint16_t *>(p.w) + rid * K + 8 * (lc ^ ((row ^ (row >> 3)) & 7));
+    }
+    auto issue_dma = [&](int kt) {
+        const int slot = kt % NS;
+#pragma unroll
+        for (int q = 0; q < A_W; ++q) {
+            const int g = q * 4 + wave;
+            if (NA % 4 == 0 || g < NA)
+                dma16(a_src[q] + kt * BK, As[slot] + g * 512);
+        }
+#pragma unroll
+        for (int q = 0; q < B_W; ++q) {
+            const int g = q * 4 + wave;
+            if (NB % 4 == 0 || g < NB)
+                dma16(b_src[q] + kt * BK, Bs[slot] + g * 512);
         }
     };
-    auto store = [&](int buf) {
+
+    // ---- MXFP4 weights through registers (one set: committed, then reloaded).
+    const char *mb_src[G::MB_PER];
+    const uint8_t *ms_src[G::MS_PER];
+    u32x4 mb[G::MB_PER];
+    uint32_t ms[G::MS_PER];
+    if (MX) {
 #pragma unroll
-        for (int i = 0; i < A_PER; ++i) {
+        for (int i = 0; i < G::MB_PER; ++i) {
+            const int c = (tid + 256 * i) % (G::MB_CHUNKS > 0 ? G::MB_CHUNKS : 1);
+            const size_t rid = (size_t)e * p.w_rows + weight_row(c >> 1);
+            mb_src[i] = reinterpret_cast<const char *>(p.w) + rid * (K / 2) + (c & 1) * 16;
+        }
+#pragma unroll
+        for (int i = 0; i < G::MS_PER; ++i) {
+            const int v = (tid + 256 * i) % BN;
+            ms_src[i] = p.scales + ((size_t)e * p.w_rows + weight_row(v)) * (K / 32);
+        }
+    }
+    auto issue_mx = [&](int kt) {
+#pragma unroll
+        for (int i = 0; i < G::MB_PER; ++i) mb[i] = *reinterpret_cast<const u32x4 *>(mb_src[i] + kt * (BK / 2));
+#pragma unroll
+        for (int i = 0; i < G::MS_PER; ++i) ms[i] = *reinterpret_cast<const uint16_t *>(ms_src[i] + kt * 2);
+    };
+    auto commit_mx = [&](int kt) {
+        const int slot = kt % NS;
+        uint32_t *words = reinterpret_cast<uint32_t *>(Bs[slot]);
+#pragma unroll
+        for (int i = 0; i < G::MB_PER; ++i) {
             const int c = tid + 256 * i;
-            if (c < A_CHUNKS) {
-                const int r = c >> 3, ch = c & 7;
-                *reinterpret_cast<u32x4 *>(&As[buf][r * BK + swz(r, ch) * 8]) = ra[i];
+            if (c < G::MB_CHUNKS) {
+                const int v = c >> 1, half = c & 1;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) words[(half * 4 + q) * BN + v] = mb[i][q];
             }
         }
 #pragma unroll
-        for (int i = 0; i < B_PER; ++i) {
-            const int c = tid + 256 * i;
-            if (c < B_CHUNKS) {
-                const int r = c >> 3, ch = c & 7;
-                *reinterpret_cast<u32x4 *>(&Bs[buf][r * BK + swz(r, ch) * 8]) = rb[i];
+        for (int i = 0; i < G::MS_PER; ++i) {
+            const int v = tid + 256 * i;
+            if (v < BN) {
+                Ss[slot][v] = (uint8_t)(ms[i] & 0xFFu);
+                Ss[slot][BN + v] = (uint8_t)(ms[i] >> 8);
             }
         }
     };
 
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-    f32x4 acc[MI][NI];
+    const int lrow = lane & 15, lk = lane >> 4;
+    f32x4 acc[NI][MI];
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+    for (int j = 0; j < NI; ++j)
 #pragma unroll
-        for (int j = 0; j < NI; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const int KT = K / BK;
-    load(0);
-    store(0);
-    __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < KT) load(kt + 1);
+        for (int i = 0; i < MI; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Router: the fp32 sums of each 256-wide K chunk (4 steps) are added into
+    // fp64 in chunk order.
+    double acc64[ROUTER ? NI : 1][ROUTER ? MI : 1][4];
+    if (ROUTER) {
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const int ch = kk * 4 + (lane >> 4);
-            u32x4 af[MI], bfr[NI];
+        for (int j = 0; j < NI; ++j)
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc64[j][i][q] = 0.0;
+    }
+    auto flush = [&]() {
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
 #pragma unroll
             for (int i = 0; i < MI; ++i) {
-                const int r = wm * WTM + i * 16 + (lane & 15);
-                af[i] = *reinterpret_cast<const u32x4 *>(&As[cur][r * BK + swz(r, ch) * 8]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc64[j][i][q] += (double)acc[j][i][q];
+                acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
+    };
+
+    // A wave whose token rows all lie past the tile's end multiplies nothing
+    // (its partial tile rows are multiplied anyway: their outputs are simply
+    // not stored).
+    const bool wave_has_rows = wm * WTM < rows;   // scalar condition
+    auto compute = [&](int kt) {
+        const int slot = kt % NS;
+        // All fragments of the step first, then the MFMAs.
+        u32x4 wf[2][NI], xf[2][MI];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int ch = kk * 4 + lk;
 #pragma unroll
             for (int j = 0; j < NI; ++j) {
-                const int r = wn * WN + j * 16 + (lane & 15);
-                bfr[j] = *reinterpret_cast<const u32x4 *>(&Bs[cur][r * BK + swz(r, ch) * 8]);
+                const int r = wn * WN + j * 16 + lrow;
+                if (MX) {
+                    const uint32_t codes = reinterpret_cast<const uint32_t *>(Bs[slot])[ch * BN + r];
+                    const float sc = __uint_as_float((uint32_t)Ss[slot][kk * BN + r] << 23);
+                    u32x4 v;
+                    v[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 0));
+                    v[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 1));
+                    v[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 2));
+                    v[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 3));
+                    wf[kk][j] = v;
+                } else {
+                    wf[kk][j] = *reinterpret_cast<const u32x4 *>(&Bs[slot][r * BK + swz(r, ch) * 8]);
+                }
             }
 #pragma unroll
-            for (int i = 0; i < MI; ++i)
-#pragma unroll
-                for (int j = 0; j < NI; ++j) acc[i][j] = mfma16x16x32(af[i], bfr[j], acc[i][j]);
+            for (int i = 0; i < MI; ++i) {
+                const int r = wm * WTM + i * 16 + lrow;
+                xf[kk][i] = *reinterpret_cast<const u32x4 *>(&As[slot][r * BK + swz(r, ch) * 8]);
+            }
         }
-        if (kt + 1 < KT) store(cur ^ 1);
-        __syncthreads();
-    }
-
-    // ---- epilogue
-    const int col = lane & 15, rq = (lane >> 4) * 4;
-    if (GEGLU) {
-        constexpr int HALF_T = NI / 2;
 #pragma unroll
-        for (int j = 0; j < HALF_T; ++j) {
-            const int n = nt * (BN / 2) + wn * (WN / 2) + j * 16 + col;
-            if (n >= p.I) continue;
+        for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < NI; ++j) acc[j][i] = mfma16x16x32(wf[kk][j], xf[kk][i], acc[j][i]);
+    };
+
+    // ---- pipeline.  Step kt: wait until its loads have landed (the loads of
+    // the later steps already issued may stay in flight), publish, issue the
+    // loads of step kt + NS - 1 into the buffer freed by step kt - 1, then
+    // multiply.  Issue order keeps the counts exact: every wave issues its
+    // loads of one step before those of the next.
+    auto wait_for = [&](int kt) {
+        const int later = min(NS - 2, KT - 1 - kt);   // steps issued after kt
+        switch (later) {
+            case 0: wait_vm_lgkm0<0>(); break;
+            case 1: wait_vm_lgkm0<G::DMA_MIN * 1>(); break;
+            case 2: wait_vm_lgkm0<G::DMA_MIN * (NS > 3 ? 2 : 1)>(); break;
+            case 3: wait_vm_lgkm0<G::DMA_MIN * (NS > 4 ? 3 : 1)>(); break;
+            case 4: wait_vm_lgkm0<G::DMA_MIN * (NS > 5 ? 4 : 1)>(); break;
+            case 5: wait_vm_lgkm0<G::DMA_MIN * (NS > 6 ? 5 : 1)>(); break;
+            default: wait_vm_lgkm0<G::DMA_MIN * (NS > 7 ? 6 : 1)>(); break;
+        }
+    };
+    if (MX) issue_mx(0);
+#pragma unroll
+    for (int s0 = 0; s0 < NS - 1; ++s0)
+        if (s0 < KT) issue_dma(s0);
+    // The loop is instantiated twice so that the accumulators are never live
+    // across a branch: waves with rows multiply, the others only load.
+    auto run = [&](auto mul_c) {
+        constexpr bool MUL = decltype(mul_c)::value;
+        for (int kt = 0; kt < KT; ++kt) {
+            wait_for(kt);
+            if (MX) {
+                commit_mx(kt);
+                wait_vm_lgkm0<63>();      // this wave's LDS writes are done
+            }
+            __builtin_amdgcn_s_barrier();
+            if (MX && kt + 1 < KT) issue_mx(kt + 1);
+            if (kt + NS - 1 < KT) issue_dma(kt + NS - 1);
+            if (MUL) {
+                compute(kt);
+                if (ROUTER && ((kt & 3) == 3 || kt == KT - 1)) flush();
+            }
+        }
+    };
+    if (wave_has_rows) run(std::true_type{});
+    else run(std::false_type{});
+
+    // ---- epilogue: lane holds weight rows 4*lk .. 4*lk+3 of tile j for the
+    // token lrow of token tile i.
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+        const int t = wm * WTM + i * 16 + lrow;
+        if (t >= rows) continue;
+        uint16_t *orow = p.out + (size_t)(seg + t) * p.n_out;
+        if (ROUTER) {
+            float *lrow_out = p.out32 + (size_t)(seg + t) * p.n_out;
+#pragma unroll
+            for (int j = 0; j < NI; ++j)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int r = wm * WTM + i * 16 + rq + q;
-                    if (r < rows) {
-                        const float g = acc[i][j][q], u = acc[i][j + HALF_T][q];
-                        p.out[(size_t)(seg + r) * p.n_out + n] = (uint16_t)f32_to_bf16_rne(gelu_tanh(g) * u);
+                    const int n = nt * BN + wn * WN + j * 16 + 4 * lk + q;
+                    if (n < p.n_out) {
+                        const double b = p.bias ? (double)p.bias[n] : 0.0;
+                        lrow_out[n] = (float)(acc64[j][i][q] + b);
                     }
                 }
-        }
-    } else {
+        } else if (GEGLU) {
+            constexpr int HALF_T = NI / 2;
 #pragma unroll
-        for (int j = 0; j < NI; ++j) {
-            const int n = nt * BN + wn * WN + j * 16 + col;
-            if (n >= p.n_out) continue;
+            for (int j = 0; j < HALF_T; ++j) {
+                const int n = nt * (BN / 2) + wn * (WN / 2) + j * 16 + 4 * lk;
+                if (n >= p.I) continue;
+                const f32x4 g = acc[j][i], u = acc[j + HALF_T][i];
+                uint2 o;
+                o.x = pack_bf16x2(gelu_tanh(g[0]) * u[0], gelu_tanh(g[1]) * u[1]);
+                o.y = pack_bf16x2(gelu_tanh(g[2]) * u[2], gelu_tanh(g[3]) * u[3]);
+                *reinterpret_cast<uint2 *>(orow + n) = o;
+            }
+        } else {
 #pragma unroll
-            for (int i = 0; i < MI; ++i)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int r = wm * WTM + i * 16 + rq + q;
-                    if (r < rows) p.out[(size_t)(seg + r) * p.n_out + n] = (uint16_t)f32_to_bf16_rne(acc[i][j][q]);
-                }
+            for (int j = 0; j < NI; ++j) {
+                const int n = nt * BN + wn * WN + j * 16 + 4 * lk;
+                if (n >= p.n_out) continue;
+                const f32x4 v = acc[j][i];
+                uint2 o;
+                o.x = pack_bf16x2(v[0], v[1]);
+                o.y = pack_bf16x2(v[2], v[3]);
+                *reinterpret_cast<uint2 *>(orow + n) = o;
+            }
         }
     }
 }
@@ -289,38 +465,53 @@ static int mtile_slots(int A, int E, int BM) {
     return (int)(((long long)A + (long long)(BM - 1) * ne) / BM);
 }
 
-template <int BM, int BN, int WM, int WN, bool GEGLU, bool MX>
-static hipError_t launch_cfg(const GemmArgs &a, int A, hipStream_t st) {
+template <int BM, int BN, int WM, int WN, int MODE, bool MX, int NS>
+static hipError_t launch_cfg(GemmArgs a, int A, hipStream_t st) {
+    constexpr bool GEGLU = MODE == kGateUp;
     const int ncols = GEGLU ? a.I : a.n_out;
     const int per_tile = GEGLU ? BN / 2 : BN;
-    dim3 grid((ncols + per_tile - 1) / per_tile, mtile_slots(A, a.E, BM));
-    if (grid.y == 0) return hipSuccess;
-    grouped_gemm_kernel<BM, BN, WM, WN, GEGLU, MX><<<grid, 256, 0, st>>>(a);
+    a.n_tiles = (ncols + per_tile - 1) / per_tile;
+    const int slots = MODE == kRouter ? (a.dense_rows + BM - 1) / BM : mtile_slots(A, a.E, BM);
+    // whole rounds of 8 groups (one per XCD)
+    const long long blocks = (long long)a.n_tiles * ((slots + 7) / 8 * 8);
+    if (blocks == 0) return hipSuccess;
+    grouped_gemm_kernel<BM, BN, WM, WN, MODE, MX, NS><<<dim3((unsigned)blocks), 256, 0, st>>>(a);
     return hipGetLastError();
 }
 
 // Row-block size from the mean rows per expert (a function of the shape
 // only, so the launch does not depend on the routing).
-template <bool GEGLU, bool MX>
+template <int MODE, bool MX>
 static hipError_t launch_sized(const GemmArgs &a, int A, hipStream_t st) {
     const int mean_rows = A / a.E;
-    if (mean_rows <= 16) return launch_cfg<16, 128, 1, 4, GEGLU, MX>(a, A, st);
-    if (mean_rows <= 48) return launch_cfg<32, 128, 2, 2, GEGLU, MX>(a, A, st);
-    if (mean_rows <= 96) return launch_cfg<64, 128, 2, 2, GEGLU, MX>(a, A, st);
-    return launch_cfg<128, 128, 2, 2, GEGLU, MX>(a, A, st);
+    // Small row blocks stream weights: two stages keep LDS small enough for
+    // four workgroups per CU.  The 256-row block runs one workgroup per CU
+    // with three stages.
+    if (mean_rows <= 16) return launch_cfg<16, 128, 1, 4, MODE, MX, 2>(a, A, st);
+    if (mean_rows <= 40) return launch_cfg<32, 128, 2, 2, MODE, MX, 2>(a, A, st);
+    if (mean_rows <= 80) return launch_cfg<64, 128, 2, 2, MODE, MX, 2>(a, A, st);
+    return launch_cfg<256, 128, 4, 1, MODE, MX, 3>(a, A, st);
 }
 
 hipError_t launch_gateup(const uint16_t *x, const int32_t *sorted_ids, int k, const int32_t *offsets,
                          const void *w, const uint8_t *scales, uint16_t *h, int A, int H, int E, int I,
                          bool mx, hipStream_t st) {
-    GemmArgs a{x, sorted_ids, k, offsets, w, scales, h, E, H, I, I, 2 * I};
-    return mx ? launch_sized<true, true>(a, A, st) : launch_sized<true, false>(a, A, st);
+    GemmArgs a{x, sorted_ids, k, offsets, w, scales, h, E, H, I, I, 2 * I, 0, 0, nullptr, nullptr};
+    return mx ? launch_sized<kGateUp, true>(a, A, st) : launch_sized<kGateUp, false>(a, A, st);
 }
 
 hipError_t launch_down(const uint16_t *h, const int32_t *offsets, const void *w, const uint8_t *scales,
                        uint16_t *y, int A, int H, int E, int I, bool mx, hipStream_t st) {
-    GemmArgs a{h, nullptr, 1, offsets, w, scales, y, E, I, H, I, H};
-    return mx ? launch_sized<false, true>(a, A, st) : launch_sized<false, false>(a, A, st);
+    GemmArgs a{h, nullptr, 1, offsets, w, scales, y, E, I, H, I, H, 0, 0, nullptr, nullptr};
+    return mx ? launch_sized<kDown, true>(a, A, st) : launch_sized<kDown, false>(a, A, st);
+}
+
+// Router for many tokens: x [T][H] times W_r [E][H]^T as one dense group, 16
+// tokens x 64 experts per workgroup, six stages (five steps in flight).
+hipError_t launch_router_dense(const uint16_t *x, const uint16_t *wr, const float *bias, float *logits,
+                               int T, int H, int E, hipStream_t st) {
+    GemmArgs a{x, nullptr, 1, nullptr, wr, nullptr, nullptr, 1, H, E, 0, E, 0, T, logits, bias};
+    return launch_cfg<16, 64, 1, 4, kRouter, false, 6>(a, T, st);
 }
 
 }  // namespace moe

@@ -53,7 +53,7 @@ __device__ __forceinline__ float gelu_tanh(float z) {
     const float k0 = 0.7978845608028654f;   // sqrt(2/pi)
     const float k1 = 0.044715f;
     float u = k0 * (z + k1 * z * z * z);
-    return z / (1.0f + __expf(-2.0f * u));
+    return __fdividef(z, 1.0f + __expf(-2.0f * u));
 }
 
 }  // namespace moe

@@ -6,12 +6,29 @@
 
 namespace moe {
 
-constexpr int kChunk = 1024;   // assignments per permutation block
+constexpr int kChunk = 1024;           // assignments per permutation block
+constexpr int kSmallRouteMaxA = 2048;  // fused few-token top-k + permutation: T*k up to this
 
-hipError_t launch_router_gemm(const uint16_t *x, const uint16_t *wr, const float *bias,
-                              float *logits, int T, int H, int E, hipStream_t st);
-hipError_t launch_topk(const float *logits, int32_t *ids, float *w, int T, int E, int k,
-                       hipStream_t st);
+constexpr int kRouterSplitMaxT = 64;   // split-K router (chunk partials) up to this many tokens
+
+int router_chunks(int H);
+bool router_uses_partials(int T);
+// Few tokens: fp32 chunk sums part[router_chunks(H)][T][E].
+hipError_t launch_router_partials(const uint16_t *x, const uint16_t *wr, float *part, int T, int H, int E,
+                                  hipStream_t st);
+// Many tokens: final fp32 logits [T][E] from the grouped GEMM engine.
+hipError_t launch_router_dense(const uint16_t *x, const uint16_t *wr, const float *bias, float *logits,
+                               int T, int H, int E, hipStream_t st);
+// Top-k from chunk partials (part != nullptr; logits optional output) or
+// from final logits (part == nullptr).
+hipError_t launch_topk(const float *part, int nchunks, const float *bias, float *logits, int32_t *ids,
+                       float *w, int T, int E, int k, hipStream_t st);
+// Few tokens: top-k from chunk partials and the whole permutation (counts,
+// offsets, sorted_ids, inv) in one launch.
+bool topk_permute_fits(int T, int k);
+hipError_t launch_topk_permute_small(const float *part, int nchunks, const float *bias, float *logits,
+                                     int32_t *ids, float *w, int32_t *counts, int32_t *offsets,
+                                     int32_t *sorted_ids, int32_t *inv, int T, int E, int k, hipStream_t st);
 hipError_t launch_permute(const int32_t *ids, int32_t *counts, int32_t *offsets,
                           int32_t *sorted_ids, int32_t *inv, int32_t *block_hist, int A, int E,
                           hipStream_t st);

@@ -10,18 +10,9 @@
 // carries it across the block's chunks).
 #include "moe_common.h"
 #include "moe_launch.h"
+#include "permute_block.h"
 
 namespace moe {
-
-// Mask of the lanes (among those with `valid`) holding the same expert id.
-__device__ __forceinline__ uint64_t match_lanes(int e, bool valid, int nbits) {
-    uint64_t m = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-        const uint64_t ones = __ballot(valid && ((e >> b) & 1));
-        m &= ((e >> b) & 1) ? ones : ~ones;
-    }
-    return m;
-}
 
 // Block b counts experts of assignments [b*kChunk, (b+1)*kChunk).
 __global__ __launch_bounds__(256) void hist_kernel(const int32_t *__restrict__ ids,
@@ -36,25 +27,11 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t *__restrict__ i
     for (int e = threadIdx.x; e < E; e += blockDim.x) block_hist[(size_t)blockIdx.x * E + e] = h[e];
 }
 
-// Block-wide exclusive scan of E <= 1024 values held one per thread.
-__device__ int block_exclusive_scan(int v, int *sh /* >= blockDim.x ints */) {
-    const int tid = threadIdx.x;
-    sh[tid] = v;
-    __syncthreads();
-    for (int off = 1; off < (int)blockDim.x; off <<= 1) {
-        const int add = tid >= off ? sh[tid - off] : 0;
-        __syncthreads();
-        sh[tid] += add;
-        __syncthreads();
-    }
-    const int incl = sh[tid];
-    __syncthreads();
-    return incl - v;
-}
-
 // One block of 1024 threads: counts[e] = sum over blocks; offsets = exclusive
 // scan; block_hist[b][e] is replaced by the absolute start of block b's
 // assignments of expert e.
+// The block histograms are read in batches of 16 before any is rewritten, so
+// the loads of a batch are in flight together.
 __global__ __launch_bounds__(1024) void scan_kernel(int32_t *__restrict__ block_hist,
                                                     int32_t *__restrict__ counts,
                                                     int32_t *__restrict__ offsets, int NB, int E, int A) {
@@ -62,45 +39,34 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t *__restrict__ block_
     const int e = threadIdx.x;
     int total = 0;
     if (e < E)
-        for (int b = 0; b < NB; ++b) {
-            const int c = block_hist[(size_t)b * E + e];
-            block_hist[(size_t)b * E + e] = total;
-            total += c;
+        for (int b0 = 0; b0 < NB; b0 += 16) {
+            int c[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) c[i] = (b0 + i < NB) ? block_hist[(size_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int cnt = c[i];
+                c[i] = total;      // exclusive start within the expert
+                total += cnt;
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (b0 + i < NB) block_hist[(size_t)(b0 + i) * E + e] = c[i];
         }
     const int start = block_exclusive_scan(e < E ? total : 0, sh);
     if (e < E) {
         counts[e] = total;
         offsets[e] = start;
-        for (int b = 0; b < NB; ++b) block_hist[(size_t)b * E + e] += start;
-    }
-    if (e == 0) offsets[E] = A;
-}
-
-// Stable rank of the assignments of one chunk, one wave, in 64-lane steps.
-// cnt[e] holds the next free position of expert e and is advanced here.
-__device__ __forceinline__ void rank_chunk(const int32_t *__restrict__ ids, int a0, int a1,
-                                           int *cnt, int nbits, int32_t *__restrict__ sorted_ids,
-                                           int32_t *__restrict__ inv) {
-    const int lane = threadIdx.x & 63;
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int base = a0; base < a1; base += 64) {
-        const int a = base + lane;
-        const bool valid = a < a1;
-        const int e = valid ? ids[a] : 0;
-        const uint64_t m = match_lanes(e, valid, nbits);
-        const int rank = __popcll(m & below);
-        int pos = 0;
-        if (valid) pos = cnt[e] + rank;
-        // The highest lane of each group advances the counter after every
-        // lane of the wave has read it.
-        __builtin_amdgcn_wave_barrier();
-        if (valid && (m >> lane) == 1ull) cnt[e] = pos + 1;
-        __builtin_amdgcn_wave_barrier();
-        if (valid) {
-            sorted_ids[pos] = a;
-            inv[a] = pos;
+        for (int b0 = 0; b0 < NB; b0 += 16) {
+            int c[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) c[i] = (b0 + i < NB) ? block_hist[(size_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (b0 + i < NB) block_hist[(size_t)(b0 + i) * E + e] = c[i] + start;
         }
     }
+    if (e == 0) offsets[E] = A;
 }
 
 // One wave per block: positions for the block's chunk.
@@ -115,7 +81,8 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t *__restrict__
     rank_chunk(ids, a0, min(A, a0 + kChunk), cnt, nbits, sorted_ids, inv);
 }
 
-// Everything in one block when A <= kChunk: histogram, scan, scatter.
+// Everything in one block of 1024 threads when A <= kChunk: histogram,
+// scan, scatter.
 __global__ __launch_bounds__(1024) void permute_small_kernel(const int32_t *__restrict__ ids,
                                                              int32_t *__restrict__ counts,
                                                              int32_t *__restrict__ offsets,
@@ -123,21 +90,8 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(const int32_t *__re
                                                              int32_t *__restrict__ inv, int A, int E, int nbits) {
     __shared__ int h[1024];
     __shared__ int sh[1024];
-    const int tid = threadIdx.x;
-    if (tid < E) h[tid] = 0;
-    __syncthreads();
-    for (int a = tid; a < A; a += blockDim.x) atomicAdd(&h[ids[a]], 1);
-    __syncthreads();
-    const int c = tid < E ? h[tid] : 0;
-    const int start = block_exclusive_scan(c, sh);
-    if (tid < E) {
-        counts[tid] = c;
-        offsets[tid] = start;
-        h[tid] = start;
-    }
-    if (tid == 0) offsets[E] = A;
-    __syncthreads();
-    if (tid < 64) rank_chunk(ids, 0, A, h, nbits, sorted_ids, inv);
+    if ((int)threadIdx.x < E) h[threadIdx.x] = 0;
+    permute_in_block(ids, A, E, nbits, h, sh, counts, offsets, sorted_ids, inv);
 }
 
 // x_perm[p] = x[sorted_ids[p] / k]: one wave per row, 16-byte vectors.

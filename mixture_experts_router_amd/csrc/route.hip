@@ -1,216 +1,270 @@
 // Router: logits = x W_r^T (+ b) on MFMA, then per token the top-k experts
-// and their renormalised softmax weights, one wavefront per token.
+// and their renormalised softmax weights.
 //
 // The pages fuse the routing as one gating top-k softmax op (Gemma-4-26B-A4B
 // optimisation report, section 5, MoE Router row, 30 calls per step); here
 // the router GEMM is a dense contraction on the matrix cores and the top-k is
-// a wave-wide lexicographic argmax repeated k times.
+// a wave-wide radix select.
+//
+// Logit definition shared by both GEMM paths (split-K below for few tokens,
+// the pipelined grouped GEMM engine for many): the K (hidden) axis is cut
+// into chunks of 256; each chunk is summed in fp32 by 8 MFMA steps of 32
+// products in K order, experts as the A operand (bf16 products are exact in
+// fp32), the chunk sums are added in fp64 in chunk order, the bias is added
+// in fp64, and the result is rounded to fp32 once.
 #include "moe_common.h"
 #include "moe_launch.h"
+#include "permute_block.h"
 
 namespace moe {
 
-// ---------------------------------------------------------------- router GEMM
-// Each wave owns SM x SN tiles of 16x16 (tokens x experts); the workgroup has
-// WM x WN x WK waves: WM along tokens, WN along experts and WK splitting the
-// K (hidden) steps round-robin.  Products of bf16 are exact in fp32; each
-// wave sums blocks of up to 8 MFMA steps (256 products) in fp32 and adds the
-// block sums into fp64, and the WK partials are added in fixed order, so the
-// logit is rounded to fp32 once and the result does not depend on timing.
-template <int SM, int SN, int WM, int WN, int WK>
-__global__ __launch_bounds__(256) void router_gemm_kernel(
-    const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
-    const float *__restrict__ bias, float *__restrict__ logits, int T, int H, int E) {
-    static_assert(WM * WN * WK == 4, "four waves");
-    constexpr int TM = 16 * SM * WM;   // tokens per workgroup
-    constexpr int TN = 16 * SN * WN;   // experts per workgroup
-    constexpr int kRed = (WK > 1 ? (WK - 1) * WM * WN : 1) * SM * SN * 4 * 64;
-    __shared__ double red[kRed];
+constexpr int kRouteChunk = 256;   // K per fp32 chunk sum (8 MFMA steps)
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wk = wave % WK, wn = (wave / WK) % WN, wm = wave / (WK * WN);
+// ---------------------------------------------------------------- few tokens
+// Split-K: block (expert group of 64, chunk c, token tile of 16).  Each wave
+// owns 16 experts, issues all 16 loads of its chunk at once and writes the
+// fp32 chunk sums part[c][t][e].  Many small blocks stream the router weight
+// in one memory round trip.
+__global__ __launch_bounds__(256) void router_partial_kernel(const uint16_t *__restrict__ x,
+                                                             const uint16_t *__restrict__ wr,
+                                                             float *__restrict__ part, int T, int H, int E) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, g = lane >> 4;
-    const int tok0 = blockIdx.x * TM + wm * 16 * SM;
-    const int exp0 = blockIdx.y * TN + wn * 16 * SN;
-
-    const uint16_t *arow[SM];
-    bool aok[SM];
+    const int etile = blockIdx.x * 4 + wave;
+    if (etile * 16 >= E) return;
+    const int c = blockIdx.y;
+    const int tok = blockIdx.z * 16 + r;   // token row loaded by this lane
+    const int e = etile * 16 + r;           // expert row loaded by this lane
+    const int k0 = c * kRouteChunk;
+    const int nsteps = min(kRouteChunk, H - k0) / 32;
+    const uint16_t *arow = x + (size_t)(tok < T ? tok : 0) * H + k0 + 8 * g;
+    const uint16_t *brow = wr + (size_t)(e < E ? e : 0) * H + k0 + 8 * g;
+    u32x4 a[8], b[8];
 #pragma unroll
-    for (int i = 0; i < SM; ++i) {
-        int t = tok0 + 16 * i + r;
-        aok[i] = t < T;
-        arow[i] = x + (size_t)(aok[i] ? t : 0) * H + 8 * g;
+    for (int u = 0; u < 8; ++u) {
+        const int su = u < nsteps ? u : 0;
+        a[u] = *reinterpret_cast<const u32x4 *>(arow + 32 * su);
+        b[u] = *reinterpret_cast<const u32x4 *>(brow + 32 * su);
     }
-    const uint16_t *brow[SN];
-    bool bok[SN];
+    // Experts are the MFMA A operand and tokens the B operand, as in the
+    // grouped GEMM engine that computes the router for many tokens: lane
+    // (r, g) ends with experts 4g..4g+3 of token r.
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < SN; ++j) {
-        int e = exp0 + 16 * j + r;
-        bok[j] = e < E;
-        brow[j] = wr + (size_t)(bok[j] ? e : 0) * H + 8 * g;
-    }
-
-    double acc64[SM][SN][4];
+    for (int u = 0; u < 8; ++u)
+        if (u < nsteps) acc = mfma16x16x32(b[u], a[u], acc);
+    const int t = blockIdx.z * 16 + r;
+    if (t < T) {
 #pragma unroll
-    for (int i = 0; i < SM; ++i)
-#pragma unroll
-        for (int j = 0; j < SN; ++j)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) acc64[i][j][q] = 0.0;
-
-    const int nsteps = H / 32;
-    for (int s0 = wk; s0 < nsteps; s0 += 8 * WK) {
-        f32x4 acc[SM][SN];
-#pragma unroll
-        for (int i = 0; i < SM; ++i)
-#pragma unroll
-            for (int j = 0; j < SN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int s = s0 + u * WK;
-            if (s < nsteps) {
-                u32x4 a[SM], b[SN];
-#pragma unroll
-                for (int i = 0; i < SM; ++i)
-                    a[i] = aok[i] ? *reinterpret_cast<const u32x4 *>(arow[i] + 32 * s) : u32x4{0, 0, 0, 0};
-#pragma unroll
-                for (int j = 0; j < SN; ++j)
-                    b[j] = bok[j] ? *reinterpret_cast<const u32x4 *>(brow[j] + 32 * s) : u32x4{0, 0, 0, 0};
-#pragma unroll
-                for (int i = 0; i < SM; ++i)
-#pragma unroll
-                    for (int j = 0; j < SN; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < SM; ++i)
-#pragma unroll
-            for (int j = 0; j < SN; ++j)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) acc64[i][j][q] += (double)acc[i][j][q];
-    }
-
-    // Fixed-order reduction of the WK partials through LDS.
-    if constexpr (WK > 1) {
-        const int slot = wm * WN + wn;
-        if (wk > 0) {
-            double *dst = red + ((wk - 1) * WM * WN + slot) * SM * SN * 256;
-#pragma unroll
-            for (int i = 0; i < SM; ++i)
-#pragma unroll
-                for (int j = 0; j < SN; ++j)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        dst[((i * SN + j) * 4 + q) * 64 + lane] = acc64[i][j][q];
-        }
-        __syncthreads();
-        if (wk != 0) return;
-#pragma unroll
-        for (int w = 1; w < WK; ++w) {
-            const double *src = red + ((w - 1) * WM * WN + slot) * SM * SN * 256;
-#pragma unroll
-            for (int i = 0; i < SM; ++i)
-#pragma unroll
-                for (int j = 0; j < SN; ++j)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        acc64[i][j][q] += src[((i * SN + j) * 4 + q) * 64 + lane];
+        for (int q = 0; q < 4; ++q) {
+            const int eo = etile * 16 + 4 * g + q;
+            if (eo < E) part[((size_t)c * T + t) * E + eo] = acc[q];
         }
     }
-
-#pragma unroll
-    for (int i = 0; i < SM; ++i)
-#pragma unroll
-        for (int j = 0; j < SN; ++j) {
-            const int e = exp0 + 16 * j + r;
-            if (e >= E) continue;
-            const double b = bias ? (double)bias[e] : 0.0;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int t = tok0 + 16 * i + 4 * g + q;
-                if (t < T) logits[(size_t)t * E + e] = (float)(acc64[i][j][q] + b);
-            }
-        }
 }
 
 // ---------------------------------------------------------------- top-k
-// One wave per token.  Lane l holds logits e = l + 64 i.  Each of the k rounds
-// takes the lexicographic maximum of (logit, -index) over the wave and retires
-// it, so ties resolve to the lower expert index and slots come out in
-// (logit descending, index ascending) order.  Weights: exp(l_j - l_0) divided
-// by their sum over the k slots.
+// Order-preserving integer key of a float: larger float -> larger key.
+// -0.0 is mapped to +0.0 so equal values tie.
+__device__ __forceinline__ uint32_t order_key(float v) {
+    const uint32_t u = __float_as_uint(v == 0.f ? 0.f : v);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Top-k of one token by one wave; lane l holds experts e = l + 64 i.  The
+// k-th largest key is found bit by bit (32 rounds of ballots); the selection
+// is every key above it plus, among keys equal to it, the lowest expert
+// indices.  Slots are then ordered by (logit descending, index ascending) and
+// the weights are exp(l_j - l_0) over their sum in slot order.  If part !=
+// nullptr the logit is first assembled from nchunks fp32 chunk sums (fp64
+// adds in chunk order, plus the fp64 bias, one rounding) and written to
+// `logits` if given.  s_key/s_idx/s_ex: this wave's 32-entry LDS scratch.
+// lds_ids (optional): also receives ids[t][slot].
 template <int VPL>
-__global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits,
-                                                   int32_t *__restrict__ ids,
-                                                   float *__restrict__ wts, int T, int E, int k) {
+__device__ __forceinline__ void topk_token(int t, const float *__restrict__ part, int nchunks,
+                                           const float *__restrict__ bias, float *__restrict__ logits,
+                                           int32_t *__restrict__ ids, float *__restrict__ wts, int T, int E,
+                                           int k, uint32_t *s_key, int *s_idx, float *s_ex, int32_t *lds_ids) {
     const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= T) return;
-    const float *L = logits + (size_t)t * E;
-    float v[VPL];
+    uint32_t key[VPL];
     bool live[VPL];
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
         const int e = lane + 64 * i;
         live[i] = e < E;
-        v[i] = live[i] ? L[e] : 0.f;
-    }
-    float my_v = 0.f;
-    int my_i = 0;
-    for (int j = 0; j < k; ++j) {
-        float bv = 0.f;
-        int bi = -1;
+        float v = 0.f;
+        if (live[i]) {
+            if (part) {
+                // chunk sums in batches of 8 loads in flight, added in chunk order
+                double s = 0.0;
+                for (int c0 = 0; c0 < nchunks; c0 += 8) {
+                    float pv[8];
 #pragma unroll
-        for (int i = 0; i < VPL; ++i)
-            if (live[i] && (bi < 0 || v[i] > bv)) { bv = v[i]; bi = lane + 64 * i; }
+                    for (int u = 0; u < 8; ++u)
+                        pv[u] = (c0 + u < nchunks) ? part[((size_t)(c0 + u) * T + t) * E + e] : 0.f;
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const float ov = __shfl_xor(bv, off, 64);
-            const int oi = __shfl_xor(bi, off, 64);
-            if (oi >= 0 && (bi < 0 || ov > bv || (ov == bv && oi < bi))) { bv = ov; bi = oi; }
+                    for (int u = 0; u < 8; ++u)
+                        if (c0 + u < nchunks) s += (double)pv[u];
+                }
+                if (bias) s += (double)bias[e];
+                v = (float)s;
+                if (logits) logits[(size_t)t * E + e] = v;
+            } else {
+                v = logits[(size_t)t * E + e];
+            }
         }
-        if ((bi & 63) == lane) {
-#pragma unroll
-            for (int i = 0; i < VPL; ++i)
-                if (i == (bi >> 6)) live[i] = false;
-        }
-        if (lane == j) { my_v = bv; my_i = bi; }
+        key[i] = live[i] ? order_key(v) : 0u;
     }
-    const float m = __shfl(my_v, 0, 64);
-    float ex = lane < k ? expf(my_v - m) : 0.f;
-    float sum = ex;
+    // k-th largest key: the largest th with #{key >= th} >= k.
+    uint32_t th = 0;
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t cand = th | (1u << b);
+        int cnt = 0;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
+        for (int i = 0; i < VPL; ++i) cnt += __popcll(__ballot(live[i] && key[i] >= cand));
+        if (cnt >= k) th = cand;
+    }
+    int gt = 0;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) gt += __popcll(__ballot(live[i] && key[i] > th));
+    const int need = k - gt;   // equal keys to take, lowest indices first
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int eq_before = 0, sel_before = 0;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        const bool eq = live[i] && key[i] == th;
+        const uint64_t eqm = __ballot(eq);
+        const bool sel = live[i] && (key[i] > th || (eq && eq_before + __popcll(eqm & below) < need));
+        const uint64_t selm = __ballot(sel);
+        if (sel) {
+            const int pos = sel_before + __popcll(selm & below);
+            s_key[pos] = key[i];
+            s_idx[pos] = lane + 64 * i;
+        }
+        eq_before += __popcll(eqm);
+        sel_before += __popcll(selm);
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    int slot = 0;
+    uint32_t my_key = 0;
+    int my_idx = 0;
     if (lane < k) {
-        ids[(size_t)t * k + lane] = my_i;
-        wts[(size_t)t * k + lane] = ex / sum;
+        my_key = s_key[lane];
+        my_idx = s_idx[lane];
+        for (int m = 0; m < k; ++m) {
+            const uint32_t km = s_key[m];
+            const int im = s_idx[m];
+            slot += (km > my_key || (km == my_key && im < my_idx)) ? 1 : 0;
+        }
     }
+    // the top logit is the largest selected key
+    uint32_t top = my_key;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) top = max(top, (uint32_t)__shfl_xor((int)top, off, 64));
+    const float ex = lane < k ? expf(key_value(my_key) - key_value(top)) : 0.f;
+    __builtin_amdgcn_wave_barrier();
+    if (lane < k) s_ex[slot] = ex;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    if (lane < k) {
+        float sum = 0.f;
+        for (int m = 0; m < k; ++m) sum += s_ex[m];
+        ids[(size_t)t * k + slot] = my_idx;
+        wts[(size_t)t * k + slot] = ex / sum;
+        if (lds_ids) lds_ids[t * k + slot] = my_idx;
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
+// One wave per token, four tokens per workgroup.
+template <int VPL>
+__global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ part, int nchunks,
+                                                   const float *__restrict__ bias, float *__restrict__ logits,
+                                                   int32_t *__restrict__ ids, float *__restrict__ wts, int T,
+                                                   int E, int k) {
+    __shared__ uint32_t s_key[4][32];
+    __shared__ int s_idx[4][32];
+    __shared__ float s_ex[4][32];
+    const int wave = threadIdx.x >> 6;
+    const int t = blockIdx.x * 4 + wave;
+    if (t >= T) return;
+    topk_token<VPL>(t, part, nchunks, bias, logits, ids, wts, T, E, k, s_key[wave], s_idx[wave], s_ex[wave],
+                    nullptr);
+}
+
+// Few tokens, one workgroup of 16 waves: the top-k of every token, then the
+// expert histogram, its scan and the stable scatter of the assignments, all
+// from the routing table kept in LDS (one launch instead of two, and the
+// table never makes a round trip through global memory before the scatter).
+template <int VPL>
+__global__ __launch_bounds__(1024) void topk_permute_small_kernel(
+    const float *__restrict__ part, int nchunks, const float *__restrict__ bias, float *__restrict__ logits,
+    int32_t *__restrict__ ids, float *__restrict__ wts, int32_t *__restrict__ counts,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_ids, int32_t *__restrict__ inv, int T, int E,
+    int k, int nbits) {
+    __shared__ uint32_t s_key[16][32];
+    __shared__ int s_idx[16][32];
+    __shared__ float s_ex[16][32];
+    __shared__ int32_t s_ids[kSmallRouteMaxA];
+    __shared__ int h[1024];
+    __shared__ int sh[1024];
+    const int tid = threadIdx.x, wave = tid >> 6;
+    const int A = T * k;
+    if (tid < E) h[tid] = 0;
+    for (int t = wave; t < T; t += 16)
+        topk_token<VPL>(t, part, nchunks, bias, logits, ids, wts, T, E, k, s_key[wave], s_idx[wave],
+                        s_ex[wave], s_ids);
+    __syncthreads();
+    permute_in_block(s_ids, A, E, nbits, h, sh, counts, offsets, sorted_ids, inv);
 }
 
 // ---------------------------------------------------------------- launchers
-hipError_t launch_router_gemm(const uint16_t *x, const uint16_t *wr, const float *bias,
-                              float *logits, int T, int H, int E, hipStream_t st) {
-    if (T <= 256) {
-        // Few tokens: 16x16 tiles with the hidden dimension split over the
-        // four waves, so the router weight is streamed by E/16 workgroups.
-        dim3 grid((T + 15) / 16, (E + 15) / 16);
-        router_gemm_kernel<1, 1, 1, 1, 4><<<grid, 256, 0, st>>>(x, wr, bias, logits, T, H, E);
-    } else {
-        dim3 grid((T + 63) / 64, (E + 31) / 32);
-        router_gemm_kernel<2, 1, 2, 2, 1><<<grid, 256, 0, st>>>(x, wr, bias, logits, T, H, E);
-    }
+int router_chunks(int H) { return (H + kRouteChunk - 1) / kRouteChunk; }
+
+bool router_uses_partials(int T) { return T <= kRouterSplitMaxT; }
+
+hipError_t launch_router_partials(const uint16_t *x, const uint16_t *wr, float *part, int T, int H, int E,
+                                  hipStream_t st) {
+    dim3 grid((E + 63) / 64, router_chunks(H), (T + 15) / 16);
+    router_partial_kernel<<<grid, 256, 0, st>>>(x, wr, part, T, H, E);
     return hipGetLastError();
 }
 
-hipError_t launch_topk(const float *logits, int32_t *ids, float *w, int T, int E, int k,
-                       hipStream_t st) {
+bool topk_permute_fits(int T, int k) { return T * k <= kSmallRouteMaxA; }
+
+hipError_t launch_topk_permute_small(const float *part, int nchunks, const float *bias, float *logits,
+                                     int32_t *ids, float *w, int32_t *counts, int32_t *offsets,
+                                     int32_t *sorted_ids, int32_t *inv, int T, int E, int k, hipStream_t st) {
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    const int vpl = (E + 63) / 64;
+#define MOE_TOPK_PERM(V)                                                                                  \
+    topk_permute_small_kernel<V><<<1, 1024, 0, st>>>(part, nchunks, bias, logits, ids, w, counts, offsets, \
+                                                     sorted_ids, inv, T, E, k, nbits)
+    if (vpl <= 1) MOE_TOPK_PERM(1);
+    else if (vpl <= 2) MOE_TOPK_PERM(2);
+    else if (vpl <= 4) MOE_TOPK_PERM(4);
+    else if (vpl <= 8) MOE_TOPK_PERM(8);
+    else MOE_TOPK_PERM(16);
+#undef MOE_TOPK_PERM
+    return hipGetLastError();
+}
+
+hipError_t launch_topk(const float *part, int nchunks, const float *bias, float *logits, int32_t *ids,
+                       float *w, int T, int E, int k, hipStream_t st) {
     dim3 grid((T + 3) / 4);
     const int vpl = (E + 63) / 64;
-    if (vpl <= 1) topk_kernel<1><<<grid, 256, 0, st>>>(logits, ids, w, T, E, k);
-    else if (vpl <= 2) topk_kernel<2><<<grid, 256, 0, st>>>(logits, ids, w, T, E, k);
-    else if (vpl <= 4) topk_kernel<4><<<grid, 256, 0, st>>>(logits, ids, w, T, E, k);
-    else if (vpl <= 8) topk_kernel<8><<<grid, 256, 0, st>>>(logits, ids, w, T, E, k);
-    else topk_kernel<16><<<grid, 256, 0, st>>>(logits, ids, w, T, E, k);
+#define MOE_TOPK(V) topk_kernel<V><<<grid, 256, 0, st>>>(part, nchunks, bias, logits, ids, w, T, E, k)
+    if (vpl <= 1) MOE_TOPK(1);
+    else if (vpl <= 2) MOE_TOPK(2);
+    else if (vpl <= 4) MOE_TOPK(4);
+    else if (vpl <= 8) MOE_TOPK(8);
+    else MOE_TOPK(16);
+#undef MOE_TOPK
     return hipGetLastError();
 }
 

@@ -56,23 +56,28 @@ def S(T=16, H=256, E=8, k=2, I=128, f=0):
 def test_bad_shapes_rejected_everywhere(lib, s, expect):
     b = ctypes.byref(s)
     F = FAKE
-    assert lib.moe_route(b, F, F, None, F, F, F, None) == expect
+    assert lib.moe_route(b, F, F, None, F, F, F, F, 1 << 30, None) == expect
     assert lib.moe_permute(b, F, None, F, F, F, F, None, F, 1 << 30, None) == expect
     assert lib.moe_grouped_gemm_gateup(b, F, F, F, F, None, F, None) == expect
     assert lib.moe_grouped_gemm_down(b, F, F, F, None, F, None) == expect
     assert lib.moe_combine(b, F, F, F, F, None) == expect
     assert lib.moe_forward(b, F, F, None, F, None, F, None, F, None, None, F, 1 << 40, None, None) == expect
     assert lib.moe_workspace_bytes(b) == 0 and lib.moe_permute_workspace_bytes(b) == 0
-    assert lib.moe_route(None, F, F, None, F, F, F, None) == -1
+    assert lib.moe_route_workspace_bytes(b) == 0
+    assert lib.moe_route(None, F, F, None, F, F, F, F, 1 << 30, None) == -1
 
 
 def test_null_and_misaligned_pointers(lib):
     s = S()
     b = ctypes.byref(s)
     F = FAKE
-    assert lib.moe_route(b, F, None, None, F, F, F, None) == -1          # x without router weight
-    assert lib.moe_route(b, MIS, F, None, F, F, F, None) == -1           # misaligned x
-    assert lib.moe_route(b, None, None, None, None, F, F, None) == -1    # no logits
+    assert lib.moe_route(b, F, None, None, F, F, F, F, 1 << 20, None) == -1        # x without router weight
+    assert lib.moe_route(b, MIS, F, None, F, F, F, F, 1 << 20, None) == -1         # misaligned x
+    assert lib.moe_route(b, None, None, None, None, F, F, None, 0, None) == -1     # no logits
+    need_r = lib.moe_route_workspace_bytes(b)
+    assert need_r > 0                                                             # T=16: split-K router
+    assert lib.moe_route(b, F, F, None, F, F, F, None, 0, None) == -3
+    assert lib.moe_route(b, F, F, None, F, F, F, F, need_r - 4, None) == -3
     assert lib.moe_permute(b, None, None, F, F, F, F, None, F, 1 << 20, None) == -1
     assert lib.moe_permute(b, F, F, F, F, F, F, None, F, 1 << 20, None) == -1   # x without x_perm
     assert lib.moe_permute(b, F, None, F, F, F, F, None, None, 1 << 20, None) == -3
@@ -90,6 +95,14 @@ def test_null_and_misaligned_pointers(lib):
     ev = (ctypes.c_void_p * 6)(F, F, F, None, F, F)
     assert lib.moe_forward(b, F, F, None, F, None, F, None, F, None, None, F, need,
                            None, ctypes.cast(ev, ctypes.c_void_p)) == -1
+
+
+def test_route_workspace(lib):
+    small = _lib.MoeShape(8, 2816, 128, 8, 704, 0)
+    big = _lib.MoeShape(2048, 2816, 128, 8, 704, 0)
+    # few tokens: fp32 partial sums of 11 chunks of 256; many tokens: none
+    assert lib.moe_route_workspace_bytes(ctypes.byref(small)) >= 11 * 8 * 128 * 4
+    assert lib.moe_route_workspace_bytes(ctypes.byref(big)) == 0
 
 
 def test_workspace_monotone_in_T(lib):

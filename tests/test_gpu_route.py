@@ -61,8 +61,20 @@ def test_topk_extremes(gpu):
     _check_topk(gpu, L32, 8, "wide logits")
 
 
-@pytest.mark.parametrize("T,H,E,skew", [(8, 2816, 128, False), (300, 512, 128, False),
-                                        (2048, 2816, 128, False), (999, 256, 8, True)])
+def _route_x(gpu, s, x, wr, b):
+    T, E, k = s.T, s.E, s.k
+    logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    nws = moe.route_workspace_bytes(s)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda") if nws else None
+    gpu.route(s, x, wr, b, logits, ids, w, ws)
+    torch.cuda.synchronize()
+    return logits.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy()
+
+
+@pytest.mark.parametrize("T,H,E,skew", [(8, 2816, 128, False), (64, 2816, 128, True), (300, 512, 128, False),
+                                        (2048, 2816, 128, False), (999, 256, 8, True), (77, 320, 200, False)])
 def test_router_gemm_and_routing(gpu, T, H, E, skew):
     say(f"router GEMM T={T} H={H} E={E} skew={skew}")
     inp = mi.make(mi.Shape(T=T, H=H, E=E, k=min(8, E), I=64, skew=skew), seed=1)
@@ -71,12 +83,7 @@ def test_router_gemm_and_routing(gpu, T, H, E, skew):
     wr = dev.to_device(inp.w_router)
     b = dev.to_device(inp.router_bias) if skew else None
     s = moe.shape(T, H, E, k, 64)
-    logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
-    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
-    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
-    gpu.route(s, x, wr, b, logits, ids, w)
-    torch.cuda.synchronize()
-    Lg = logits.cpu().numpy()
+    Lg, ids, w = _route_x(gpu, s, x, wr, b)
     x64 = oracle.bf16_to_f64(inp.x)
     w64 = oracle.bf16_to_f64(inp.w_router)
     L = oracle.router_logits(x64, w64, inp.router_bias)
@@ -90,11 +97,26 @@ def test_router_gemm_and_routing(gpu, T, H, E, skew):
     assert (err <= bound).all()
     # the decision on the GPU's own fp32 logits is the oracle's decision on them
     rid, rw = oracle.topk_softmax(Lg.astype(np.float64), k)
-    assert (ids.cpu().numpy() == rid).all()
-    assert np.abs(w.cpu().numpy() - rw).max() <= 1e-6
+    assert (ids == rid).all()
+    assert np.abs(w - rw).max() <= 1e-6
     # against fp64 routing: differences only at near ties
     fid, _ = oracle.topk_softmax(L, k)
     margin = oracle.routing_margin(L, k)
-    diff = np.array([set(a) != set(b) for a, b in zip(ids.cpu().numpy(), fid)])
+    diff = np.array([set(a) != set(b) for a, b in zip(ids, fid)])
     say(f"  fp64-routing differences {diff.sum()}, min margin {margin.min():.3e}")
     assert (margin[diff] < 1e-6).all()
+
+
+def test_router_paths_agree_bitwise(gpu):
+    """Few tokens go through the split-K router, many through the GEMM
+    engine; both follow one definition of the logit, so the logits of the
+    same token agree bit for bit."""
+    T, H, E = 200, 2816, 128
+    inp = mi.make(mi.Shape(T=T, H=H, E=E, k=8, I=64, skew=True), seed=4)
+    x = dev.to_device(inp.x)
+    wr = dev.to_device(inp.w_router)
+    b = dev.to_device(inp.router_bias)
+    L_many, _, _ = _route_x(gpu, moe.shape(T, H, E, 8, 64), x, wr, b)
+    for t0 in (0, 64, 136):
+        L_few, _, _ = _route_x(gpu, moe.shape(64, H, E, 8, 64), x[t0:t0 + 64].contiguous(), wr, b)
+        assert (L_few.view(np.uint32) == L_many[t0:t0 + 64].view(np.uint32)).all()
