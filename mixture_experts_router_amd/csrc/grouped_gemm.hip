@@ -102,6 +102,8 @@ struct GemmTile {
     static constexpr bool GEGLU = MODE == kGateUp;
     static constexpr int BK = 64;
     static constexpr int NS = NS_;                // LDS stages (NS - 1 loads ahead)
+    static constexpr int NW = WAVES_M * WAVES_N;   // waves per workgroup
+    static constexpr int NT = 64 * NW;             // threads per workgroup
     static constexpr int WTM = BM / WAVES_M;      // tokens per wave
     static constexpr int WN = BN / WAVES_N;       // weight rows per wave
     static constexpr int MI = WTM / 16;           // token tiles per wave (MFMA B operand)
@@ -110,19 +112,19 @@ struct GemmTile {
     // 8 rows of 64 bf16.
     static constexpr int NA = BM / 8;             // token-tile instructions per stage
     static constexpr int NB = MX ? 0 : BN / 8;    // bf16 weight-tile instructions per stage
-    static constexpr int A_W = (NA + 3) / 4;      // per wave (upper bound)
-    static constexpr int B_W = (NB + 3) / 4;
+    static constexpr int A_W = (NA + NW - 1) / NW;   // per wave (upper bound)
+    static constexpr int B_W = (NB + NW - 1) / NW;
     // Loads every wave issues per stage at least (waves with more wait a
     // little longer, never too short).
-    static constexpr int DMA_MIN = NA / 4 + NB / 4;
+    static constexpr int DMA_MIN = NA / NW + NB / NW;
     // MXFP4 weights: BN rows x 2 chunks of 16 bytes (64 codes) + 2 scale bytes,
     // staged through registers.
     static constexpr int MB_CHUNKS = MX ? BN * 2 : 0;
-    static constexpr int MB_PER = MX ? (MB_CHUNKS + 255) / 256 : 1;
-    static constexpr int MS_PER = MX ? (BN + 255) / 256 : 1;
+    static constexpr int MB_PER = MX ? (MB_CHUNKS + NT - 1) / NT : 1;
+    static constexpr int MS_PER = MX ? (BN + NT - 1) / NT : 1;
     static constexpr int A_LDS = BM * BK;                      // uint16 per stage
     static constexpr int B_LDS = MX ? BN * BK / 4 : BN * BK;   // uint16 per stage
-    static_assert(WAVES_M * WAVES_N == 4, "four waves");
+    static_assert(NW == 4 || NW == 8, "four or eight waves");
     static_assert(MI >= 1 && NI >= 1, "tile too small");
     static_assert(!GEGLU || (NI % 2 == 0), "GEGLU pairs gate and up tiles");
     static_assert(BM % 8 == 0 && BN % 8 == 0, "whole 1 KB load groups");
@@ -150,11 +152,11 @@ __device__ __forceinline__ void dma16(const void *g, const void *lds) {
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int MODE, bool MX, int NS_>
-__global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs p) {
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(GemmArgs p) {
     using G = GemmTile<BM, BN, WAVES_M, WAVES_N, MODE, MX, NS_>;
     constexpr bool GEGLU = MODE == kGateUp, ROUTER = MODE == kRouter;
     constexpr int BK = G::BK, NS = G::NS, WTM = G::WTM, WN = G::WN, MI = G::MI, NI = G::NI;
-    constexpr int NA = G::NA, NB = G::NB, A_W = G::A_W, B_W = G::B_W;
+    constexpr int NA = G::NA, NB = G::NB, A_W = G::A_W, B_W = G::B_W, NW = G::NW, NT = G::NT;
 
     // bf16 tiles: [row][8 chunks of 16 B], chunk index XOR-swizzled by row.
     // MXFP4 codes: [chunk (8 words of 4 B)][row]; scales: [2 blocks][row].
@@ -223,7 +225,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs p) {
     const uint16_t *a_src[A_W];
 #pragma unroll
     for (int q = 0; q < A_W; ++q) {
-        const int g = q * 4 + wave;
+        const int g = q * NW + wave;
         const int row = 8 * (g < NA ? g : 0) + lr;
         const int rr = row < rows ? row : 0;
         const size_t src = p.gather ? (size_t)(p.gather[seg + rr] / p.gather_k) : (size_t)(seg + rr);
@@ -232,7 +234,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs p) {
     const uint16_t *b_src[B_W > 0 ? B_W : 1];
 #pragma unroll
     for (int q = 0; q < B_W; ++q) {
-        const int g = q * 4 + wave;
+        const int g = q * NW + wave;
         const int row = 8 * (g < NB ? g : 0) + lr;
         const size_t rid = (size_t)e * p.w_rows + weight_row(row);
         b_src[q] = reinterpret_cast<const uint16_t *>(p.w) + rid * K + 8 * (lc ^ ((row ^ (row >> 3)) & 7));
@@ -241,14 +243,14 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs p) {
         const int slot = kt % NS;
 #pragma unroll
         for (int q = 0; q < A_W; ++q) {
-            const int g = q * 4 + wave;
-            if (NA % 4 == 0 || g < NA)
+            const int g = q * NW + wave;
+            if (NA % NW == 0 || g < NA)
                 dma16(a_src[q] + kt * BK, As[slot] + g * 512);
         }
 #pragma unroll
         for (int q = 0; q < B_W; ++q) {
-            const int g = q * 4 + wave;
-            if (NB % 4 == 0 || g < NB)
+            const int g = q * NW + wave;
+            if (NB % NW == 0 || g < NB)
                 dma16(b_src[q] + kt * BK, Bs[slot] + g * 512);
         }
     };
@@ -261,13 +263,13 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs p) {
     if (MX) {
 #pragma unroll
         for (int i = 0; i < G::MB_PER; ++i) {
-            const int c = (tid + 256 * i) % (G::MB_CHUNKS > 0 ? G::MB_CHUNKS : 1);
+            const int c = (tid + NT * i) % (G::MB_CHUNKS > 0 ? G::MB_CHUNKS : 1);
             const size_t rid = (size_t)e * p.w_rows + weight_row(c >> 1);
             mb_src[i] = reinterpret_cast<const char *>(p.w) + rid * (K / 2) + (c & 1) * 16;
         }
 #pragma unroll
         for (int i = 0; i < G::MS_PER; ++i) {
-            const int v = (tid + 256 * i) % BN;
+            const int v = (tid + NT * i) % BN;
             ms_src[i] = p.scales + ((size_t)e * p.w_rows + weight_row(v)) * (K / 32);
         }
     }
@@ -282,7 +284,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs p) {
         uint32_t *words = reinterpret_cast<uint32_t *>(Bs[slot]);
 #pragma unroll
         for (int i = 0; i < G::MB_PER; ++i) {
-            const int c = tid + 256 * i;
+            const int c = tid + NT * i;
             if (c < G::MB_CHUNKS) {
                 const int v = c >> 1, half = c & 1;
 #pragma unroll
@@ -291,7 +293,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs p) {
         }
 #pragma unroll
         for (int i = 0; i < G::MS_PER; ++i) {
-            const int v = tid + 256 * i;
+            const int v = tid + NT * i;
             if (v < BN) {
                 Ss[slot][v] = (uint8_t)(ms[i] & 0xFFu);
                 Ss[slot][BN + v] = (uint8_t)(ms[i] >> 8);
@@ -475,7 +477,7 @@ static hipError_t launch_cfg(GemmArgs a, int A, hipStream_t st) {
     // whole rounds of 8 groups (one per XCD)
     const long long blocks = (long long)a.n_tiles * ((slots + 7) / 8 * 8);
     if (blocks == 0) return hipSuccess;
-    grouped_gemm_kernel<BM, BN, WM, WN, MODE, MX, NS><<<dim3((unsigned)blocks), 256, 0, st>>>(a);
+    grouped_gemm_kernel<BM, BN, WM, WN, MODE, MX, NS><<<dim3((unsigned)blocks), 64 * WM * WN, 0, st>>>(a);
     return hipGetLastError();
 }
 
@@ -485,12 +487,13 @@ template <int MODE, bool MX>
 static hipError_t launch_sized(const GemmArgs &a, int A, hipStream_t st) {
     const int mean_rows = A / a.E;
     // Small row blocks stream weights: two stages keep LDS small enough for
-    // four workgroups per CU.  The 256-row block runs one workgroup per CU
-    // with three stages.
+    // four workgroups per CU.  The 256-row block runs one workgroup of eight
+    // waves (two per SIMD, so one wave's LDS reads overlap the other's MFMAs)
+    // per CU with three stages.
     if (mean_rows <= 16) return launch_cfg<16, 128, 1, 4, MODE, MX, 2>(a, A, st);
     if (mean_rows <= 40) return launch_cfg<32, 128, 2, 2, MODE, MX, 2>(a, A, st);
     if (mean_rows <= 80) return launch_cfg<64, 128, 2, 2, MODE, MX, 2>(a, A, st);
-    return launch_cfg<256, 128, 4, 1, MODE, MX, 3>(a, A, st);
+    return launch_cfg<256, 128, 4, 2, MODE, MX, 3>(a, A, st);
 }
 
 hipError_t launch_gateup(const uint16_t *x, const int32_t *sorted_ids, int k, const int32_t *offsets,

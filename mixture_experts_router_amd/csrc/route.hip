@@ -98,18 +98,20 @@ __device__ __forceinline__ void topk_token(int t, const float *__restrict__ part
         float v = 0.f;
         if (live[i]) {
             if (part) {
-                // chunk sums in batches of 8 loads in flight, added in chunk order
+                // chunk sums in batches of 16 loads in flight (one batch for
+                // H <= 4096), added in chunk order; the bias load goes along
+                const float b = bias ? bias[e] : 0.f;
                 double s = 0.0;
-                for (int c0 = 0; c0 < nchunks; c0 += 8) {
-                    float pv[8];
+                for (int c0 = 0; c0 < nchunks; c0 += 16) {
+                    float pv[16];
 #pragma unroll
-                    for (int u = 0; u < 8; ++u)
-                        pv[u] = (c0 + u < nchunks) ? part[((size_t)(c0 + u) * T + t) * E + e] : 0.f;
+                    for (int u = 0; u < 16; ++u)
+                        pv[u] = part[((size_t)min(c0 + u, nchunks - 1) * T + t) * E + e];
 #pragma unroll
-                    for (int u = 0; u < 8; ++u)
+                    for (int u = 0; u < 16; ++u)
                         if (c0 + u < nchunks) s += (double)pv[u];
                 }
-                if (bias) s += (double)bias[e];
+                s += (double)b;
                 v = (float)s;
                 if (logits) logits[(size_t)t * E + e] = v;
             } else {
