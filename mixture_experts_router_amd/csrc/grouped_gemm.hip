@@ -97,10 +97,13 @@ __device__ __forceinline__ void find_tile(const int32_t *__restrict__ offsets, i
 
 enum GemmMode { kDown = 0, kGateUp = 1, kRouter = 2 };
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int MODE, bool MX, int NS_>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int MODE, bool MX, int NS_, int BK_>
 struct GemmTile {
     static constexpr bool GEGLU = MODE == kGateUp;
-    static constexpr int BK = 64;
+    static constexpr int BK = BK_;                // K per step (32 or 64)
+    static constexpr int CH = BK / 8;             // 16-byte chunks per tile row
+    static constexpr int RPD = 64 / CH;           // tile rows per 1 KB direct-to-LDS load
+    static constexpr int KK = BK / 32;            // MFMA K steps per step
     static constexpr int NS = NS_;                // LDS stages (NS - 1 loads ahead)
     static constexpr int NW = WAVES_M * WAVES_N;   // waves per workgroup
     static constexpr int NT = 64 * NW;             // threads per workgroup
@@ -109,14 +112,11 @@ struct GemmTile {
     static constexpr int MI = WTM / 16;           // token tiles per wave (MFMA B operand)
     static constexpr int NI = WN / 16;            // weight-row tiles per wave (MFMA A operand)
     // Direct-to-LDS loads move 1 KB per wave instruction (64 lanes x 16 B):
-    // 8 rows of 64 bf16.
-    static constexpr int NA = BM / 8;             // token-tile instructions per stage
-    static constexpr int NB = MX ? 0 : BN / 8;    // bf16 weight-tile instructions per stage
+    // RPD rows of BK bf16.
+    static constexpr int NA = BM / RPD;           // token-tile instructions per stage
+    static constexpr int NB = MX ? 0 : BN / RPD;  // bf16 weight-tile instructions per stage
     static constexpr int A_W = (NA + NW - 1) / NW;   // per wave (upper bound)
     static constexpr int B_W = (NB + NW - 1) / NW;
-    // Loads every wave issues per stage at least (waves with more wait a
-    // little longer, never too short).
-    static constexpr int DMA_MIN = NA / NW + NB / NW;
     // MXFP4 weights: BN rows x 2 chunks of 16 bytes (64 codes) + 2 scale bytes,
     // staged through registers.
     static constexpr int MB_CHUNKS = MX ? BN * 2 : 0;
@@ -127,10 +127,12 @@ struct GemmTile {
     static_assert(NW == 4 || NW == 8, "four or eight waves");
     static_assert(MI >= 1 && NI >= 1, "tile too small");
     static_assert(!GEGLU || (NI % 2 == 0), "GEGLU pairs gate and up tiles");
-    static_assert(BM % 8 == 0 && BN % 8 == 0, "whole 1 KB load groups");
+    static_assert(BK == 32 || BK == 64, "K step");
+    static_assert(BM % RPD == 0 && BN % RPD == 0, "whole 1 KB load groups");
+    static_assert(!MX || BK == 64, "MXFP4 tiles use K steps of 64");
     static_assert(NS >= 2 && NS <= 8, "stages");
     // MXFP4 codes go through registers one step ahead; the wait counts
-    // below assume at most one DMA step is issued after them.
+    // assume at most one DMA step is issued after them.
     static_assert(!MX || NS <= 3, "MXFP4 pipeline depth");
 };
 
@@ -139,6 +141,24 @@ template <int VM>
 __device__ __forceinline__ void wait_vm_lgkm0() {
     static_assert(VM >= 0 && VM < 64, "vmcnt field");
     __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
+}
+
+// The same for a wave-uniform count known only at run time (0..31; larger
+// counts wait for everything, which is always safe).
+__device__ __forceinline__ void wait_vm_lgkm0_rt(int n) {
+    switch (n) {
+#define MOE_WAIT_CASE(N) \
+    case N: wait_vm_lgkm0<N>(); break;
+        MOE_WAIT_CASE(1) MOE_WAIT_CASE(2) MOE_WAIT_CASE(3) MOE_WAIT_CASE(4) MOE_WAIT_CASE(5)
+        MOE_WAIT_CASE(6) MOE_WAIT_CASE(7) MOE_WAIT_CASE(8) MOE_WAIT_CASE(9) MOE_WAIT_CASE(10)
+        MOE_WAIT_CASE(11) MOE_WAIT_CASE(12) MOE_WAIT_CASE(13) MOE_WAIT_CASE(14) MOE_WAIT_CASE(15)
+        MOE_WAIT_CASE(16) MOE_WAIT_CASE(17) MOE_WAIT_CASE(18) MOE_WAIT_CASE(19) MOE_WAIT_CASE(20)
+        MOE_WAIT_CASE(21) MOE_WAIT_CASE(22) MOE_WAIT_CASE(23) MOE_WAIT_CASE(24) MOE_WAIT_CASE(25)
+        MOE_WAIT_CASE(26) MOE_WAIT_CASE(27) MOE_WAIT_CASE(28) MOE_WAIT_CASE(29) MOE_WAIT_CASE(30)
+        MOE_WAIT_CASE(31)
+#undef MOE_WAIT_CASE
+        default: wait_vm_lgkm0<0>(); break;
+    }
 }
 
 // 16-byte direct global->LDS load of one wave: lane l's 16 bytes from `g`
@@ -151,11 +171,12 @@ __device__ __forceinline__ void dma16(const void *g, const void *lds) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(l) : "memory", "m0");
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int MODE, bool MX, int NS_>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int MODE, bool MX, int NS_, int BK_>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(GemmArgs p) {
-    using G = GemmTile<BM, BN, WAVES_M, WAVES_N, MODE, MX, NS_>;
+    using G = GemmTile<BM, BN, WAVES_M, WAVES_N, MODE, MX, NS_, BK_>;
     constexpr bool GEGLU = MODE == kGateUp, ROUTER = MODE == kRouter;
     constexpr int BK = G::BK, NS = G::NS, WTM = G::WTM, WN = G::WN, MI = G::MI, NI = G::NI;
+    constexpr int CH = G::CH, RPD = G::RPD, KK = G::KK;
     constexpr int NA = G::NA, NB = G::NB, A_W = G::A_W, B_W = G::B_W, NW = G::NW, NT = G::NT;
 
     // bf16 tiles: [row][8 chunks of 16 B], chunk index XOR-swizzled by row.
@@ -216,35 +237,38 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
         return r < p.n_out ? r : 0;
     };
 
-    // ---- direct-to-LDS sources.  Instruction g fills rows 8g..8g+7 of the
-    // stage buffer; lane l lands at row 8g + l/8, physical chunk l%8, so it
-    // fetches logical chunk (l%8) ^ swizzle(row).  A token row past the
-    // tile's end reads the tile's first row and a weight row past the matrix
-    // reads row 0; both only feed outputs that are never stored.
-    const int lr = lane >> 3, lc = lane & 7;
+    // ---- direct-to-LDS sources.  Instruction g fills rows RPD*g .. RPD*g +
+    // RPD - 1 of the stage buffer; lane l lands at row RPD*g + l/CH, physical
+    // chunk l%CH, so it fetches logical chunk (l%CH) ^ swizzle(row).  A token
+    // row past the tile's end reads the tile's first row and a weight row
+    // past the matrix reads row 0; both only feed outputs never stored.
+    const int lr = lane / CH, lc = lane % CH;
     const uint16_t *a_src[A_W];
 #pragma unroll
     for (int q = 0; q < A_W; ++q) {
         const int g = q * NW + wave;
-        const int row = 8 * (g < NA ? g : 0) + lr;
+        const int row = RPD * (g < NA ? g : 0) + lr;
         const int rr = row < rows ? row : 0;
         const size_t src = p.gather ? (size_t)(p.gather[seg + rr] / p.gather_k) : (size_t)(seg + rr);
-        a_src[q] = p.a + src * K + 8 * (lc ^ ((row ^ (row >> 3)) & 7));
+        a_src[q] = p.a + src * K + 8 * tswz<BK>(row, lc);
     }
     const uint16_t *b_src[B_W > 0 ? B_W : 1];
 #pragma unroll
     for (int q = 0; q < B_W; ++q) {
         const int g = q * NW + wave;
-        const int row = 8 * (g < NB ? g : 0) + lr;
+        const int row = RPD * (g < NB ? g : 0) + lr;
         const size_t rid = (size_t)e * p.w_rows + weight_row(row);
-        b_src[q] = reinterpret_cast<const uint16_t *>(p.w) + rid * K + 8 * (lc ^ ((row ^ (row >> 3)) & 7));
+        b_src[q] = reinterpret_cast<const uint16_t *>(p.w) + rid * K + 8 * tswz<BK>(row, lc);
     }
+    // Token-row groups past the tile's last valid row are not loaded (their
+    // LDS rows keep stale data that only reaches outputs never stored).
+    const int na_valid = (rows + RPD - 1) / RPD;
     auto issue_dma = [&](int kt) {
         const int slot = kt % NS;
 #pragma unroll
         for (int q = 0; q < A_W; ++q) {
             const int g = q * NW + wave;
-            if (NA % NW == 0 || g < NA)
+            if (g < na_valid)
                 dma16(a_src[q] + kt * BK, As[slot] + g * 512);
         }
 #pragma unroll
@@ -308,8 +332,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
     for (int j = 0; j < NI; ++j)
 #pragma unroll
         for (int i = 0; i < MI; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // Router: the fp32 sums of each 256-wide K chunk (4 steps) are added into
-    // fp64 in chunk order.
+    // Router: the fp32 sums of each 256-wide K chunk (256 / BK steps) are
+    // added into fp64 in chunk order.
     double acc64[ROUTER ? NI : 1][ROUTER ? MI : 1][4];
     if (ROUTER) {
 #pragma unroll
@@ -336,11 +360,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
     const bool wave_has_rows = wm * WTM < rows;   // scalar condition
     auto compute = [&](int kt) {
         const int slot = kt % NS;
-        // All fragments of the step first, then the MFMAs.
-        u32x4 wf[2][NI], xf[2][MI];
+        // Per MFMA K step of 32: the fragments, then the MFMAs.
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
+        for (int kk = 0; kk < KK; ++kk) {
             const int ch = kk * 4 + lk;
+            u32x4 wf[NI], xf[MI];
 #pragma unroll
             for (int j = 0; j < NI; ++j) {
                 const int r = wn * WN + j * 16 + lrow;
@@ -352,23 +376,21 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
                     v[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 1));
                     v[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 2));
                     v[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 3));
-                    wf[kk][j] = v;
+                    wf[j] = v;
                 } else {
-                    wf[kk][j] = *reinterpret_cast<const u32x4 *>(&Bs[slot][r * BK + swz(r, ch) * 8]);
+                    wf[j] = *reinterpret_cast<const u32x4 *>(&Bs[slot][r * BK + tswz<BK>(r, ch) * 8]);
                 }
             }
 #pragma unroll
             for (int i = 0; i < MI; ++i) {
                 const int r = wm * WTM + i * 16 + lrow;
-                xf[kk][i] = *reinterpret_cast<const u32x4 *>(&As[slot][r * BK + swz(r, ch) * 8]);
+                xf[i] = *reinterpret_cast<const u32x4 *>(&As[slot][r * BK + tswz<BK>(r, ch) * 8]);
             }
-        }
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
-                for (int j = 0; j < NI; ++j) acc[j][i] = mfma16x16x32(wf[kk][j], xf[kk][i], acc[j][i]);
+                for (int j = 0; j < NI; ++j) acc[j][i] = mfma16x16x32(wf[j], xf[i], acc[j][i]);
+        }
     };
 
     // ---- pipeline.  Step kt: wait until its loads have landed (the loads of
@@ -376,17 +398,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
     // loads of step kt + NS - 1 into the buffer freed by step kt - 1, then
     // multiply.  Issue order keeps the counts exact: every wave issues its
     // loads of one step before those of the next.
+    // Loads this wave issues per step: its valid token-row groups and its
+    // weight-row groups (exact, so each wave waits for no more than it must).
+    int dma_per_step = 0;
+#pragma unroll
+    for (int q = 0; q < A_W; ++q) dma_per_step += (q * NW + wave < na_valid) ? 1 : 0;
+#pragma unroll
+    for (int q = 0; q < B_W; ++q) dma_per_step += (NB % NW == 0 || q * NW + wave < NB) ? 1 : 0;
     auto wait_for = [&](int kt) {
         const int later = min(NS - 2, KT - 1 - kt);   // steps issued after kt
-        switch (later) {
-            case 0: wait_vm_lgkm0<0>(); break;
-            case 1: wait_vm_lgkm0<G::DMA_MIN * 1>(); break;
-            case 2: wait_vm_lgkm0<G::DMA_MIN * (NS > 3 ? 2 : 1)>(); break;
-            case 3: wait_vm_lgkm0<G::DMA_MIN * (NS > 4 ? 3 : 1)>(); break;
-            case 4: wait_vm_lgkm0<G::DMA_MIN * (NS > 5 ? 4 : 1)>(); break;
-            case 5: wait_vm_lgkm0<G::DMA_MIN * (NS > 6 ? 5 : 1)>(); break;
-            default: wait_vm_lgkm0<G::DMA_MIN * (NS > 7 ? 6 : 1)>(); break;
-        }
+        wait_vm_lgkm0_rt(later * dma_per_step);
     };
     if (MX) issue_mx(0);
 #pragma unroll
@@ -407,7 +428,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
             if (kt + NS - 1 < KT) issue_dma(kt + NS - 1);
             if (MUL) {
                 compute(kt);
-                if (ROUTER && ((kt & 3) == 3 || kt == KT - 1)) flush();
+                if (ROUTER && ((kt % (256 / BK)) == 256 / BK - 1 || kt == KT - 1)) flush();
             }
         }
     };
@@ -467,7 +488,7 @@ static int mtile_slots(int A, int E, int BM) {
     return (int)(((long long)A + (long long)(BM - 1) * ne) / BM);
 }
 
-template <int BM, int BN, int WM, int WN, int MODE, bool MX, int NS>
+template <int BM, int BN, int WM, int WN, int MODE, bool MX, int NS, int BK>
 static hipError_t launch_cfg(GemmArgs a, int A, hipStream_t st) {
     constexpr bool GEGLU = MODE == kGateUp;
     const int ncols = GEGLU ? a.I : a.n_out;
@@ -477,7 +498,7 @@ static hipError_t launch_cfg(GemmArgs a, int A, hipStream_t st) {
     // whole rounds of 8 groups (one per XCD)
     const long long blocks = (long long)a.n_tiles * ((slots + 7) / 8 * 8);
     if (blocks == 0) return hipSuccess;
-    grouped_gemm_kernel<BM, BN, WM, WN, MODE, MX, NS><<<dim3((unsigned)blocks), 64 * WM * WN, 0, st>>>(a);
+    grouped_gemm_kernel<BM, BN, WM, WN, MODE, MX, NS, BK><<<dim3((unsigned)blocks), 64 * WM * WN, 0, st>>>(a);
     return hipGetLastError();
 }
 
@@ -487,13 +508,15 @@ template <int MODE, bool MX>
 static hipError_t launch_sized(const GemmArgs &a, int A, hipStream_t st) {
     const int mean_rows = A / a.E;
     // Small row blocks stream weights: two stages keep LDS small enough for
-    // four workgroups per CU.  The 256-row block runs one workgroup of eight
+    // four workgroups per CU.  The 256 x 256 block runs one workgroup of eight
     // waves (two per SIMD, so one wave's LDS reads overlap the other's MFMAs)
-    // per CU with three stages.
-    if (mean_rows <= 16) return launch_cfg<16, 128, 1, 4, MODE, MX, 2>(a, A, st);
-    if (mean_rows <= 40) return launch_cfg<32, 128, 2, 2, MODE, MX, 2>(a, A, st);
-    if (mean_rows <= 80) return launch_cfg<64, 128, 2, 2, MODE, MX, 2>(a, A, st);
-    return launch_cfg<256, 128, 4, 2, MODE, MX, 3>(a, A, st);
+    // per CU: the large tile moves the fewest bytes per FLOP through the
+    // per-CU load path; bf16 in two stages of 64 KB, MXFP4 (small weight
+    // tiles) in three.  (Measured: K steps of 32 in four stages are slower.)
+    if (mean_rows <= 16) return launch_cfg<16, 128, 1, 4, MODE, MX, 2, 64>(a, A, st);
+    if (mean_rows <= 40) return launch_cfg<32, 128, 2, 2, MODE, MX, 2, 64>(a, A, st);
+    if (mean_rows <= 80) return launch_cfg<64, 128, 2, 2, MODE, MX, 2, 64>(a, A, st);
+    return launch_cfg<256, 256, 4, 2, MODE, MX, MX ? 3 : 2, 64>(a, A, st);
 }
 
 hipError_t launch_gateup(const uint16_t *x, const int32_t *sorted_ids, int k, const int32_t *offsets,
@@ -514,7 +537,7 @@ hipError_t launch_down(const uint16_t *h, const int32_t *offsets, const void *w,
 hipError_t launch_router_dense(const uint16_t *x, const uint16_t *wr, const float *bias, float *logits,
                                int T, int H, int E, hipStream_t st) {
     GemmArgs a{x, nullptr, 1, nullptr, wr, nullptr, nullptr, 1, H, E, 0, E, 0, T, logits, bias};
-    return launch_cfg<16, 64, 1, 4, kRouter, false, 6>(a, T, st);
+    return launch_cfg<16, 64, 1, 4, kRouter, false, 6, 64>(a, T, st);
 }
 
 }  // namespace moe

@@ -30,11 +30,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // A tile row holds 64 bf16 (128 bytes = 8 chunks of 16 bytes).  The chunk
-// index is XORed with a function of the row so that 16 lanes reading the same
-// logical chunk of 16 consecutive rows hit distinct LDS banks, whether the
-// LDS is 32 or 64 banks wide.
-__device__ __forceinline__ int swz(int row, int chunk) {
-    return chunk ^ ((row ^ (row >> 3)) & 7);
+// index is XORed with the low three bits of the row.  Measured on gfx950
+// (SQ_LDS_BANK_CONFLICT) for the MFMA fragment read -- lane l reads chunk
+// 4*kk + l/16 of row 16*m + l%16 with ds_read_b128 -- this layout has no
+// bank conflicts (so does XOR with (row >> 1) & 7), while XOR with
+// (row ^ row >> 3) & 7 costs 4 extra cycles per read and no swizzle 12.
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
+
+// Swizzle of a tile with K-step BK (rows of BK bf16).  Rows of 32 bf16
+// (64 bytes = 4 chunks) measured the same way: XOR with (row >> 1) & 3 is
+// conflict-free; XOR with row & 3, (row >> 2) & 3 or none cost 4 extra cycles.
+template <int BK>
+__device__ __forceinline__ int tswz(int row, int chunk) {
+    if constexpr (BK == 64) return chunk ^ (row & 7);
+    else return chunk ^ ((row >> 1) & 3);
 }
 
 // 16x16x32 bf16 MFMA with fp32 accumulation.  Operand layout per lane l:
