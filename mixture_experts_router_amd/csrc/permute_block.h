@@ -95,4 +95,61 @@ __device__ __forceinline__ void permute_in_block(const int32_t *ids, int A, int 
         for (int a0 = 0; a0 < A; a0 += kChunk) rank_chunk(ids, a0, min(A, a0 + kChunk), h, nbits, sorted_ids, inv);
 }
 
+// Histogram, exclusive scan and stable scatter of A <= 64 assignments by one
+// wave, lane a holding assignment a.  One pass over the id bits, high to
+// low, gives both the number of assignments with a smaller expert id (the
+// expert's start) and the mask of lanes with the same id (the stable rank
+// within it).  h (>= E ints of LDS, zero on entry) receives the counts.
+// Each lane then scans C = ceil(E / 64) <= 16 consecutive experts.
+template <int C>
+__device__ __forceinline__ void permute_wave(const int32_t *ids, int A, int E, int nbits, int *h,
+                                             int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+                                             int32_t *__restrict__ sorted_ids, int32_t *__restrict__ inv) {
+    const int lane = threadIdx.x & 63;
+    const bool valid = lane < A;
+    const int id = valid ? ids[lane] : 0;
+    uint64_t m = __ballot(valid);   // valid lanes whose id agrees on the bits seen so far
+    int less = 0;
+    for (int b = nbits - 1; b >= 0; --b) {
+        const bool bit = (id >> b) & 1;
+        const uint64_t ones = __ballot(valid && bit);
+        if (bit) less += __popcll(m & ~ones);
+        m &= bit ? ones : ~ones;
+    }
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    if (valid) {
+        const int pos = less + __popcll(m & below);
+        sorted_ids[pos] = lane;
+        inv[lane] = pos;
+        if ((m >> lane) == 1ull) h[id] = __popcll(m);   // highest lane of its expert group
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    int c[C];
+    int tot = 0;
+#pragma unroll
+    for (int q = 0; q < C; ++q) {
+        const int e = lane * C + q;
+        c[q] = e < E ? h[e] : 0;
+        tot += c[q];
+    }
+    int incl = tot;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int v = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += v;
+    }
+    int run = incl - tot;
+#pragma unroll
+    for (int q = 0; q < C; ++q) {
+        const int e = lane * C + q;
+        if (e < E) {
+            counts[e] = c[q];
+            offsets[e] = run;
+        }
+        run += c[q];
+    }
+    if (lane == 0) offsets[E] = A;
+}
+
 }  // namespace moe

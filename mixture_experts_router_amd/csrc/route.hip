@@ -74,112 +74,116 @@ __device__ __forceinline__ float key_value(uint32_t k) {
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-// Top-k of one token by one wave; lane l holds experts e = l + 64 i.  The
-// k-th largest key is found bit by bit (32 rounds of ballots); the selection
-// is every key above it plus, among keys equal to it, the lowest expert
-// indices.  Slots are then ordered by (logit descending, index ascending) and
-// the weights are exp(l_j - l_0) over their sum in slot order.  If part !=
-// nullptr the logit is first assembled from nchunks fp32 chunk sums (fp64
+// Wave-wide maximum, returned as a scalar: DPP steps inside each row of 16
+// lanes (quad swaps, then the half-row and row mirrors), then the four row
+// results.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));    // quad [1,0,3,2]
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));    // quad [2,3,0,1]
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));   // row_half_mirror
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));   // row_mirror
+    const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+    return max(max(r0, r1), max(r2, r3));
+}
+
+// Top-k of one token by one wave; lane l holds experts e = l + 64 i.  Slot j
+// takes the largest remaining key, the lowest expert index among equal keys
+// (so slots come out ordered by logit descending, index ascending), and the
+// weights are exp(l_j - l_0) over their sum, summed in slot order.  If part
+// != nullptr the logit is first assembled from nchunks fp32 chunk sums (fp64
 // adds in chunk order, plus the fp64 bias, one rounding) and written to
-// `logits` if given.  s_key/s_idx/s_ex: this wave's 32-entry LDS scratch.
-// lds_ids (optional): also receives ids[t][slot].
+// `logits` if given.  lds_ids (optional): also receives ids[t][slot].
 template <int VPL>
 __device__ __forceinline__ void topk_token(int t, const float *__restrict__ part, int nchunks,
                                            const float *__restrict__ bias, float *__restrict__ logits,
                                            int32_t *__restrict__ ids, float *__restrict__ wts, int T, int E,
-                                           int k, uint32_t *s_key, int *s_idx, float *s_ex, int32_t *lds_ids) {
+                                           int k, int32_t *lds_ids) {
     const int lane = threadIdx.x & 63;
-    uint32_t key[VPL];
-    bool live[VPL];
+    uint32_t key[VPL];   // 0 = no expert (past E) or already taken
+    if (part) {
+        // Values in groups of IB; all chunk-sum loads of a batch (every chunk
+        // for H <= 4096 and E <= 128) are issued before the first add.
+        constexpr int IB = VPL < 4 ? VPL : 4;
+        constexpr int CB = IB <= 2 ? 16 : 4;
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-        const int e = lane + 64 * i;
-        live[i] = e < E;
-        float v = 0.f;
-        if (live[i]) {
-            if (part) {
-                // chunk sums in batches of 16 loads in flight (one batch for
-                // H <= 4096), added in chunk order; the bias load goes along
-                const float b = bias ? bias[e] : 0.f;
-                double s = 0.0;
-                for (int c0 = 0; c0 < nchunks; c0 += 16) {
-                    float pv[16];
+        for (int i0 = 0; i0 < VPL; i0 += IB) {
+            double s[IB];
+            float b[IB];
 #pragma unroll
-                    for (int u = 0; u < 16; ++u)
-                        pv[u] = part[((size_t)min(c0 + u, nchunks - 1) * T + t) * E + e];
+            for (int i = 0; i < IB; ++i) {
+                const int e = lane + 64 * (i0 + i);
+                b[i] = (bias && e < E) ? bias[e] : 0.f;
+                s[i] = 0.0;
+            }
+            for (int c0 = 0; c0 < nchunks; c0 += CB) {
+                float pv[IB][CB];
 #pragma unroll
-                    for (int u = 0; u < 16; ++u)
-                        if (c0 + u < nchunks) s += (double)pv[u];
+                for (int i = 0; i < IB; ++i) {
+                    const int e = min(lane + 64 * (i0 + i), E - 1);
+#pragma unroll
+                    for (int u = 0; u < CB; ++u)
+                        pv[i][u] = part[((size_t)min(c0 + u, nchunks - 1) * T + t) * E + e];
                 }
-                s += (double)b;
-                v = (float)s;
-                if (logits) logits[(size_t)t * E + e] = v;
-            } else {
-                v = logits[(size_t)t * E + e];
+#pragma unroll
+                for (int i = 0; i < IB; ++i)
+#pragma unroll
+                    for (int u = 0; u < CB; ++u)
+                        if (c0 + u < nchunks) s[i] += (double)pv[i][u];
+            }
+#pragma unroll
+            for (int i = 0; i < IB; ++i) {
+                const int e = lane + 64 * (i0 + i);
+                key[i0 + i] = 0u;
+                if (e < E) {
+                    const float v = (float)(s[i] + (double)b[i]);
+                    if (logits) logits[(size_t)t * E + e] = v;
+                    key[i0 + i] = order_key(v);
+                }
             }
         }
-        key[i] = live[i] ? order_key(v) : 0u;
-    }
-    // k-th largest key: the largest th with #{key >= th} >= k.
-    uint32_t th = 0;
-    for (int b = 31; b >= 0; --b) {
-        const uint32_t cand = th | (1u << b);
-        int cnt = 0;
+    } else {
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) cnt += __popcll(__ballot(live[i] && key[i] >= cand));
-        if (cnt >= k) th = cand;
-    }
-    int gt = 0;
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) gt += __popcll(__ballot(live[i] && key[i] > th));
-    const int need = k - gt;   // equal keys to take, lowest indices first
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    int eq_before = 0, sel_before = 0;
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-        const bool eq = live[i] && key[i] == th;
-        const uint64_t eqm = __ballot(eq);
-        const bool sel = live[i] && (key[i] > th || (eq && eq_before + __popcll(eqm & below) < need));
-        const uint64_t selm = __ballot(sel);
-        if (sel) {
-            const int pos = sel_before + __popcll(selm & below);
-            s_key[pos] = key[i];
-            s_idx[pos] = lane + 64 * i;
+        for (int i = 0; i < VPL; ++i) {
+            const int e = lane + 64 * i;
+            key[i] = e < E ? order_key(logits[(size_t)t * E + e]) : 0u;
         }
-        eq_before += __popcll(eqm);
-        sel_before += __popcll(selm);
     }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    int slot = 0;
-    uint32_t my_key = 0;
+    // k rounds of wave argmax; every value below is wave-uniform except the
+    // per-lane slot record (lane j keeps slot j).
     int my_idx = 0;
-    if (lane < k) {
-        my_key = s_key[lane];
-        my_idx = s_idx[lane];
-        for (int m = 0; m < k; ++m) {
-            const uint32_t km = s_key[m];
-            const int im = s_idx[m];
-            slot += (km > my_key || (km == my_key && im < my_idx)) ? 1 : 0;
+    float my_ex = 0.f, top = 0.f, sum = 0.f;
+    for (int j = 0; j < k; ++j) {
+        uint32_t lm = key[0];
+#pragma unroll
+        for (int i = 1; i < VPL; ++i) lm = max(lm, key[i]);
+        const uint32_t km = wave_max_u32(lm);
+        int sel = 0;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            const uint64_t hit = __ballot(key[i] == km);
+            if (hit) {
+                sel = 64 * i + (int)__builtin_ctzll(hit);
+                break;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+            if (64 * i + lane == sel) key[i] = 0u;
+        const float v = key_value(km);
+        if (j == 0) top = v;
+        const float ex = expf(v - top);
+        sum += ex;
+        if (lane == j) {
+            my_idx = sel;
+            my_ex = ex;
         }
     }
-    // the top logit is the largest selected key
-    uint32_t top = my_key;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) top = max(top, (uint32_t)__shfl_xor((int)top, off, 64));
-    const float ex = lane < k ? expf(key_value(my_key) - key_value(top)) : 0.f;
-    __builtin_amdgcn_wave_barrier();
-    if (lane < k) s_ex[slot] = ex;
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     if (lane < k) {
-        float sum = 0.f;
-        for (int m = 0; m < k; ++m) sum += s_ex[m];
-        ids[(size_t)t * k + slot] = my_idx;
-        wts[(size_t)t * k + slot] = ex / sum;
-        if (lds_ids) lds_ids[t * k + slot] = my_idx;
+        ids[(size_t)t * k + lane] = my_idx;
+        wts[(size_t)t * k + lane] = my_ex / sum;
+        if (lds_ids) lds_ids[t * k + lane] = my_idx;
     }
-    __builtin_amdgcn_wave_barrier();
 }
 
 // One wave per token, four tokens per workgroup.
@@ -188,40 +192,35 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ par
                                                    const float *__restrict__ bias, float *__restrict__ logits,
                                                    int32_t *__restrict__ ids, float *__restrict__ wts, int T,
                                                    int E, int k) {
-    __shared__ uint32_t s_key[4][32];
-    __shared__ int s_idx[4][32];
-    __shared__ float s_ex[4][32];
-    const int wave = threadIdx.x >> 6;
-    const int t = blockIdx.x * 4 + wave;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
-    topk_token<VPL>(t, part, nchunks, bias, logits, ids, wts, T, E, k, s_key[wave], s_idx[wave], s_ex[wave],
-                    nullptr);
+    topk_token<VPL>(t, part, nchunks, bias, logits, ids, wts, T, E, k, nullptr);
 }
 
 // Few tokens, one workgroup of 16 waves: the top-k of every token, then the
 // expert histogram, its scan and the stable scatter of the assignments, all
 // from the routing table kept in LDS (one launch instead of two, and the
 // table never makes a round trip through global memory before the scatter).
+// Up to 64 assignments the permutation is one wave's work.
 template <int VPL>
 __global__ __launch_bounds__(1024) void topk_permute_small_kernel(
     const float *__restrict__ part, int nchunks, const float *__restrict__ bias, float *__restrict__ logits,
     int32_t *__restrict__ ids, float *__restrict__ wts, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_ids, int32_t *__restrict__ inv, int T, int E,
     int k, int nbits) {
-    __shared__ uint32_t s_key[16][32];
-    __shared__ int s_idx[16][32];
-    __shared__ float s_ex[16][32];
     __shared__ int32_t s_ids[kSmallRouteMaxA];
     __shared__ int h[1024];
     __shared__ int sh[1024];
     const int tid = threadIdx.x, wave = tid >> 6;
     const int A = T * k;
     if (tid < E) h[tid] = 0;
-    for (int t = wave; t < T; t += 16)
-        topk_token<VPL>(t, part, nchunks, bias, logits, ids, wts, T, E, k, s_key[wave], s_idx[wave],
-                        s_ex[wave], s_ids);
+    for (int t = wave; t < T; t += 16) topk_token<VPL>(t, part, nchunks, bias, logits, ids, wts, T, E, k, s_ids);
     __syncthreads();
-    permute_in_block(s_ids, A, E, nbits, h, sh, counts, offsets, sorted_ids, inv);
+    if (A <= 64) {
+        if (wave == 0) permute_wave<VPL>(s_ids, A, E, nbits, h, counts, offsets, sorted_ids, inv);
+    } else {
+        permute_in_block(s_ids, A, E, nbits, h, sh, counts, offsets, sorted_ids, inv);
+    }
 }
 
 // ---------------------------------------------------------------- launchers
