@@ -10,7 +10,7 @@ cannot serve them from a previous step.
 
 Prints one JSON line:  value = tokens/s of the whole layer; roofline = the
 dominant kernel (grouped gate/up GEMM) against the HBM or MFMA peak, its
-duration from HIP events the library records on the launch stream;
+duration from HIP events around back-to-back launches on the launch stream;
 cpu_baseline = the fp64 numpy oracle timed on this host on a bounded sample.
 """
 from __future__ import annotations
@@ -203,8 +203,39 @@ def main():
     print(f"# {K} steps: {ms * 1e3:.1f} us/step; stages (us) " +
           " ".join(f"{n}={v:.1f}" for n, v in stage_avg_us.items()), file=sys.stderr, flush=True)
 
+    # Timed region 3: the dominant kernel alone, K back-to-back launches of
+    # moe_grouped_gemm_gateup on this step's routing (the weight copies
+    # rotate as in region 1) -> its average launch duration for the roofline.
+    A = s.T * s.k
+    i32 = dict(dtype=torch.int32, device="cuda")
+    r_logits = torch.empty((s.T, s.E), dtype=torch.float32, device="cuda")
+    r_ids = torch.empty((s.T, s.k), **i32)
+    r_w = torch.empty((s.T, s.k), dtype=torch.float32, device="cuda")
+    counts = torch.empty(s.E, **i32)
+    offsets = torch.empty(s.E + 1, **i32)
+    sorted_ids = torch.empty(A, **i32)
+    inv = torch.empty(A, **i32)
+    x_perm = torch.empty((A, s.H), dtype=torch.bfloat16, device="cuda")
+    h = torch.empty((A, s.I), dtype=torch.bfloat16, device="cuda")
+    rws = torch.empty(max(1, moe.route_workspace_bytes(sh)), dtype=torch.uint8, device="cuda")
+    pws = torch.empty(max(1, moe.permute_workspace_bytes(sh)), dtype=torch.uint8, device="cuda")
+    moe.route(sh, x, wr, bias, r_logits, r_ids, r_w, ws=rws)
+    moe.permute(sh, r_ids, x, counts, offsets, sorted_ids, inv, x_perm, pws)
+    torch.cuda.synchronize()
+    if not torch.equal(r_ids.cpu(), ids.cpu()):
+        raise RuntimeError("moe_route and moe_forward disagree on the routing")
+    moe.gemm_gateup(sh, x, sorted_ids, offsets, copies[0][0], gus, h)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(K):
+        moe.gemm_gateup(sh, x, sorted_ids, offsets, copies[i % len(copies)][0], gus, h)
+    end.record()
+    torch.cuda.synchronize()
+    gateup_launch_us = start.elapsed_time(end) / K * 1e3
+    print(f"# gate/up kernel alone: {gateup_launch_us:.1f} us per launch", file=sys.stderr, flush=True)
+
     tokens_per_s = s.T / (ms * 1e-3)
-    gu_s = stage_avg_us["gateup"] * 1e-6
+    gu_s = gateup_launch_us * 1e-6
     ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     if alg["gateup_flops"] / alg["gateup_bytes"] > ridge:
         bound, unit, peak = "mfma", "TFLOP/s", BF16_PEAK_TFLOPS
@@ -244,7 +275,7 @@ def main():
             "frac": achieved / peak,
             "traffic": traffic_from_profiles(args.config),
             "alg_bytes_per_launch": alg["gateup_bytes"], "alg_flops_per_launch": alg["gateup_flops"],
-            "avg_launch_us": stage_avg_us["gateup"],
+            "avg_launch_us": gateup_launch_us,
         },
         "layer": layer,
         "stages_us": stage_avg_us,

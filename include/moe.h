@@ -89,6 +89,8 @@ typedef void *moe_event_t;  /* hipEvent_t */
 
 /* Number of stages moe_forward times when given stage events. */
 #define MOE_FORWARD_STAGES 5
+/* Leading workspace bytes of moe_forward that must start out zero. */
+#define MOE_WS_ZERO_BYTES 256
 
 /*
  * moe_route -- router GEMM, top-k and softmax weights (report, section 5:
@@ -169,7 +171,12 @@ int moe_combine(const moe_shape *s, const uint16_t *y, const int32_t *inv,
  *   weights and scales as for the steps above
  *   out           [T][H] bf16 out
  *   topk_ids_out  [T][k] int32 out or NULL;  topk_w_out [T][k] fp32 out or NULL
- *   ws            device scratch of at least moe_workspace_bytes(s)
+ *   ws            device scratch of at least moe_workspace_bytes(s), 16-byte
+ *                 aligned.  Its first MOE_WS_ZERO_BYTES bytes hold completion
+ *                 counters: they must be zero before the first call with this
+ *                 workspace (allocate it zero-filled), and every call leaves
+ *                 them zero again.  Calls that overlap in time must not share
+ *                 a workspace.
  *   stage_events  NULL, or MOE_FORWARD_STAGES + 1 hipEvent_t recorded on
  *                 `stream` before the first stage and after each stage
  *                 (route, permute, gate/up, down, combine)

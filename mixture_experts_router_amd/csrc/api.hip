@@ -64,6 +64,7 @@ int check_weights(const moe_shape *s, const void *w, const uint8_t *scales) {
 }
 
 struct Workspace {
+    uint32_t *done;   // completion counter of the single-launch few-token routing
     float *part;
     float *logits;
     int32_t *ids;
@@ -83,6 +84,7 @@ Workspace carve(const moe_shape *s, void *base) {
         off += round_up(bytes);
         return q;
     };
+    w.done = reinterpret_cast<uint32_t *>(take(MOE_WS_ZERO_BYTES));
     w.part = reinterpret_cast<float *>(take(route_ws(s)));
     w.logits = reinterpret_cast<float *>(take(T * E * sizeof(float)));
     w.ids = reinterpret_cast<int32_t *>(take(A * sizeof(int32_t)));
@@ -235,14 +237,11 @@ int moe_forward(const moe_shape *s, const uint16_t *x, const uint16_t *w_router,
         return hip_status(hipEventRecord(static_cast<hipEvent_t>(stage_events[stage++]), hs));
     };
     if ((st = mark()) != MOE_OK) return st;
-    if (moe::router_uses_partials(T) && moe::topk_permute_fits(T, k)) {
-        // few tokens: split-K router, then top-k and the permutation in one
-        // launch (the permute stage is empty)
-        st = hip_status(moe::launch_router_partials(x, w_router, w.part, T, H, E, hs));
-        if (st == MOE_OK)
-            st = hip_status(moe::launch_topk_permute_small(w.part, moe::router_chunks(H), router_bias, w.logits,
-                                                           ids, wts, w.counts, w.offsets, w.sorted_ids, w.inv,
-                                                           T, E, k, hs));
+    if (moe::route_permute_fits(T, k)) {
+        // few tokens: router, top-k and the permutation in one launch (the
+        // permute stage is empty)
+        st = hip_status(moe::launch_route_permute(x, w_router, w.part, w.done, router_bias, w.logits, ids, wts,
+                                                  w.counts, w.offsets, w.sorted_ids, w.inv, T, H, E, k, hs));
         if (st != MOE_OK || (st = mark()) != MOE_OK) return st;
         if ((st = mark()) != MOE_OK) return st;
     } else {

@@ -40,9 +40,13 @@ __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7
 // Swizzle of a tile with K-step BK (rows of BK bf16).  Rows of 32 bf16
 // (64 bytes = 4 chunks) measured the same way: XOR with (row >> 1) & 3 is
 // conflict-free; XOR with row & 3, (row >> 2) & 3 or none cost 4 extra cycles.
+// Rows of 128 bf16 (256 bytes = 16 chunks): XOR with row & 15 is
+// conflict-free; XOR with row & 7 or (row >> 1) & 7 costs one extra cycle
+// per read, none seven.
 template <int BK>
 __device__ __forceinline__ int tswz(int row, int chunk) {
-    if constexpr (BK == 64) return chunk ^ (row & 7);
+    if constexpr (BK == 128) return chunk ^ (row & 15);
+    else if constexpr (BK == 64) return chunk ^ (row & 7);
     else return chunk ^ ((row >> 1) & 3);
 }
 

@@ -23,12 +23,15 @@ hipError_t launch_router_dense(const uint16_t *x, const uint16_t *wr, const floa
 // from final logits (part == nullptr).
 hipError_t launch_topk(const float *part, int nchunks, const float *bias, float *logits, int32_t *ids,
                        float *w, int T, int E, int k, hipStream_t st);
-// Few tokens: top-k from chunk partials and the whole permutation (counts,
-// offsets, sorted_ids, inv) in one launch.
-bool topk_permute_fits(int T, int k);
-hipError_t launch_topk_permute_small(const float *part, int nchunks, const float *bias, float *logits,
-                                     int32_t *ids, float *w, int32_t *counts, int32_t *offsets,
-                                     int32_t *sorted_ids, int32_t *inv, int T, int E, int k, hipStream_t st);
+// Few tokens (route_permute_fits): router chunk sums, top-k and the whole
+// permutation (counts, offsets, sorted_ids, inv) in one launch.  `done` is a
+// completion counter that must be zero before the launch; it is zero again
+// after it.
+bool route_permute_fits(int T, int k);
+hipError_t launch_route_permute(const uint16_t *x, const uint16_t *wr, float *part, uint32_t *done,
+                                const float *bias, float *logits, int32_t *ids, float *w, int32_t *counts,
+                                int32_t *offsets, int32_t *sorted_ids, int32_t *inv, int T, int H, int E, int k,
+                                hipStream_t st);
 hipError_t launch_permute(const int32_t *ids, int32_t *counts, int32_t *offsets,
                           int32_t *sorted_ids, int32_t *inv, int32_t *block_hist, int A, int E,
                           hipStream_t st);

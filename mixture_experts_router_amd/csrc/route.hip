@@ -21,20 +21,16 @@ namespace moe {
 constexpr int kRouteChunk = 256;   // K per fp32 chunk sum (8 MFMA steps)
 
 // ---------------------------------------------------------------- few tokens
-// Split-K: block (expert group of 64, chunk c, token tile of 16).  Each wave
-// owns 16 experts, issues all 16 loads of its chunk at once and writes the
-// fp32 chunk sums part[c][t][e].  Many small blocks stream the router weight
-// in one memory round trip.
-__global__ __launch_bounds__(256) void router_partial_kernel(const uint16_t *__restrict__ x,
-                                                             const uint16_t *__restrict__ wr,
-                                                             float *__restrict__ part, int T, int H, int E) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// Split-K: one wave owns (16 experts, chunk c, 16 tokens), issues all 16
+// loads of its chunk at once and writes the fp32 chunk sums part[c][t][e].
+// Many small waves stream the router weight in one memory round trip.
+__device__ __forceinline__ void router_partial_wave(const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
+                                                    float *__restrict__ part, int T, int H, int E, int etile,
+                                                    int c, int ttile) {
+    const int lane = threadIdx.x & 63;
     const int r = lane & 15, g = lane >> 4;
-    const int etile = blockIdx.x * 4 + wave;
-    if (etile * 16 >= E) return;
-    const int c = blockIdx.y;
-    const int tok = blockIdx.z * 16 + r;   // token row loaded by this lane
-    const int e = etile * 16 + r;           // expert row loaded by this lane
+    const int tok = ttile * 16 + r;   // token row loaded by this lane
+    const int e = etile * 16 + r;     // expert row loaded by this lane
     const int k0 = c * kRouteChunk;
     const int nsteps = min(kRouteChunk, H - k0) / 32;
     const uint16_t *arow = x + (size_t)(tok < T ? tok : 0) * H + k0 + 8 * g;
@@ -53,7 +49,7 @@ __global__ __launch_bounds__(256) void router_partial_kernel(const uint16_t *__r
 #pragma unroll
     for (int u = 0; u < 8; ++u)
         if (u < nsteps) acc = mfma16x16x32(b[u], a[u], acc);
-    const int t = blockIdx.z * 16 + r;
+    const int t = ttile * 16 + r;
     if (t < T) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -61,6 +57,15 @@ __global__ __launch_bounds__(256) void router_partial_kernel(const uint16_t *__r
             if (eo < E) part[((size_t)c * T + t) * E + eo] = acc[q];
         }
     }
+}
+
+// Block (64 experts, chunk, 16 tokens), one wave per 16 experts.
+__global__ __launch_bounds__(256) void router_partial_kernel(const uint16_t *__restrict__ x,
+                                                             const uint16_t *__restrict__ wr,
+                                                             float *__restrict__ part, int T, int H, int E) {
+    const int etile = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (etile * 16 >= E) return;
+    router_partial_wave(x, wr, part, T, H, E, etile, blockIdx.y, blockIdx.z);
 }
 
 // ---------------------------------------------------------------- top-k
@@ -74,17 +79,18 @@ __device__ __forceinline__ float key_value(uint32_t k) {
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-// Wave-wide maximum, returned as a scalar: DPP steps inside each row of 16
-// lanes (quad swaps, then the half-row and row mirrors), then the four row
-// results.
+// Wave-wide maximum in every lane: DPP steps inside each row of 16 lanes
+// (quad swaps, then the half-row and row mirrors), then the gfx950 lane swaps
+// between the two halves and between neighbouring rows.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));    // quad [1,0,3,2]
     v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));    // quad [2,3,0,1]
     v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));   // row_half_mirror
     v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));   // row_mirror
-    const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
-    const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
-    return max(max(r0, r1), max(r2, r3));
+    const auto h = __builtin_amdgcn_permlane32_swap(v, v, false, false);   // lanes l and l ^ 32
+    v = max(h[0], h[1]);
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);   // rows 0<->1, 2<->3
+    return max(r[0], r[1]);
 }
 
 // Top-k of one token by one wave; lane l holds experts e = l + 64 i.  Slot j
@@ -149,10 +155,9 @@ __device__ __forceinline__ void topk_token(int t, const float *__restrict__ part
             key[i] = e < E ? order_key(logits[(size_t)t * E + e]) : 0u;
         }
     }
-    // k rounds of wave argmax; every value below is wave-uniform except the
-    // per-lane slot record (lane j keeps slot j).
+    // k rounds of wave argmax; lane j keeps slot j.
     int my_idx = 0;
-    float my_ex = 0.f, top = 0.f, sum = 0.f;
+    uint32_t my_key = 0;
     for (int j = 0; j < k; ++j) {
         uint32_t lm = key[0];
 #pragma unroll
@@ -170,18 +175,19 @@ __device__ __forceinline__ void topk_token(int t, const float *__restrict__ part
 #pragma unroll
         for (int i = 0; i < VPL; ++i)
             if (64 * i + lane == sel) key[i] = 0u;
-        const float v = key_value(km);
-        if (j == 0) top = v;
-        const float ex = expf(v - top);
-        sum += ex;
         if (lane == j) {
             my_idx = sel;
-            my_ex = ex;
+            my_key = km;
         }
     }
+    // weights: exp(l_j - l_0) in every slot lane at once, their sum in slot order
+    const float top = key_value((uint32_t)__builtin_amdgcn_readfirstlane((int)my_key));
+    const float ex = lane < k ? expf(key_value(my_key) - top) : 0.f;
+    float sum = 0.f;
+    for (int m = 0; m < k; ++m) sum += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ex), m));
     if (lane < k) {
         ids[(size_t)t * k + lane] = my_idx;
-        wts[(size_t)t * k + lane] = my_ex / sum;
+        wts[(size_t)t * k + lane] = ex / sum;
         if (lds_ids) lds_ids[t * k + lane] = my_idx;
     }
 }
@@ -199,18 +205,16 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ par
 
 // Few tokens, one workgroup of 16 waves: the top-k of every token, then the
 // expert histogram, its scan and the stable scatter of the assignments, all
-// from the routing table kept in LDS (one launch instead of two, and the
-// table never makes a round trip through global memory before the scatter).
-// Up to 64 assignments the permutation is one wave's work.
+// from the routing table kept in LDS (it never makes a round trip through
+// global memory before the scatter).  Up to 64 assignments the permutation
+// is one wave's work.
 template <int VPL>
-__global__ __launch_bounds__(1024) void topk_permute_small_kernel(
-    const float *__restrict__ part, int nchunks, const float *__restrict__ bias, float *__restrict__ logits,
-    int32_t *__restrict__ ids, float *__restrict__ wts, int32_t *__restrict__ counts,
-    int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_ids, int32_t *__restrict__ inv, int T, int E,
-    int k, int nbits) {
-    __shared__ int32_t s_ids[kSmallRouteMaxA];
-    __shared__ int h[1024];
-    __shared__ int sh[1024];
+__device__ __forceinline__ void topk_permute_block(const float *__restrict__ part, int nchunks,
+                                                   const float *__restrict__ bias, float *__restrict__ logits,
+                                                   int32_t *__restrict__ ids, float *__restrict__ wts,
+                                                   int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+                                                   int32_t *__restrict__ sorted_ids, int32_t *__restrict__ inv,
+                                                   int T, int E, int k, int nbits, int32_t *s_ids, int *h, int *sh) {
     const int tid = threadIdx.x, wave = tid >> 6;
     const int A = T * k;
     if (tid < E) h[tid] = 0;
@@ -221,6 +225,47 @@ __global__ __launch_bounds__(1024) void topk_permute_small_kernel(
     } else {
         permute_in_block(s_ids, A, E, nbits, h, sh, counts, offsets, sorted_ids, inv);
     }
+}
+
+// The whole few-token routing in one launch.  Every block first computes
+// its router chunk sums (block = 256 experts of one chunk and 16 tokens, a
+// wave per 16 experts); the last block to finish -- found with a completion
+// counter -- then runs the top-k and the permutation over all of them.
+// Release/acquire: each block's sums are made visible device-wide (agent-
+// scope fence) before its counter increment, and the last block fences
+// again before reading them.  The counter wraps back to zero on the last
+// increment, so it is zero again for the next call.
+template <int VPL>
+__global__ __launch_bounds__(1024) void route_permute_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr, float *__restrict__ part, int H,
+    uint32_t *__restrict__ done, const float *__restrict__ bias, float *__restrict__ logits,
+    int32_t *__restrict__ ids, float *__restrict__ wts, int32_t *__restrict__ counts,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_ids, int32_t *__restrict__ inv, int T, int E,
+    int k, int nbits) {
+    __shared__ int32_t s_ids[kSmallRouteMaxA];
+    __shared__ int h[1024];
+    __shared__ int sh[1024];
+    __shared__ int s_last;
+    const int etile = blockIdx.x * 16 + (threadIdx.x >> 6);
+    if (etile * 16 < E) router_partial_wave(x, wr, part, T, H, E, etile, blockIdx.y, blockIdx.z);
+    // Every wave waits until its stores are complete in this XCD's L2; after
+    // the barrier one thread makes them visible device-wide (L2 write-back),
+    // counts the block done and, in the last block, invalidates the caches
+    // before any wave reads the other blocks' sums.  (Fencing in every wave
+    // would cost one L2 write-back per wave.)
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t nblocks = gridDim.x * gridDim.y * gridDim.z;
+        __threadfence();
+        const bool last = atomicInc(done, nblocks - 1) == nblocks - 1;
+        if (last) __threadfence();
+        s_last = last;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    topk_permute_block<VPL>(part, gridDim.y, bias, logits, ids, wts, counts, offsets, sorted_ids, inv, T, E, k,
+                            nbits, s_ids, h, sh);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -235,23 +280,25 @@ hipError_t launch_router_partials(const uint16_t *x, const uint16_t *wr, float *
     return hipGetLastError();
 }
 
-bool topk_permute_fits(int T, int k) { return T * k <= kSmallRouteMaxA; }
+bool route_permute_fits(int T, int k) { return router_uses_partials(T) && T * k <= kSmallRouteMaxA; }
 
-hipError_t launch_topk_permute_small(const float *part, int nchunks, const float *bias, float *logits,
-                                     int32_t *ids, float *w, int32_t *counts, int32_t *offsets,
-                                     int32_t *sorted_ids, int32_t *inv, int T, int E, int k, hipStream_t st) {
+hipError_t launch_route_permute(const uint16_t *x, const uint16_t *wr, float *part, uint32_t *done,
+                                const float *bias, float *logits, int32_t *ids, float *w, int32_t *counts,
+                                int32_t *offsets, int32_t *sorted_ids, int32_t *inv, int T, int H, int E, int k,
+                                hipStream_t st) {
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
     const int vpl = (E + 63) / 64;
-#define MOE_TOPK_PERM(V)                                                                                  \
-    topk_permute_small_kernel<V><<<1, 1024, 0, st>>>(part, nchunks, bias, logits, ids, w, counts, offsets, \
-                                                     sorted_ids, inv, T, E, k, nbits)
-    if (vpl <= 1) MOE_TOPK_PERM(1);
-    else if (vpl <= 2) MOE_TOPK_PERM(2);
-    else if (vpl <= 4) MOE_TOPK_PERM(4);
-    else if (vpl <= 8) MOE_TOPK_PERM(8);
-    else MOE_TOPK_PERM(16);
-#undef MOE_TOPK_PERM
+    dim3 grid((E + 255) / 256, router_chunks(H), (T + 15) / 16);
+#define MOE_ROUTE_PERM(V)                                                                                      \
+    route_permute_kernel<V><<<grid, 1024, 0, st>>>(x, wr, part, H, done, bias, logits, ids, w, counts, offsets, \
+                                                   sorted_ids, inv, T, E, k, nbits)
+    if (vpl <= 1) MOE_ROUTE_PERM(1);
+    else if (vpl <= 2) MOE_ROUTE_PERM(2);
+    else if (vpl <= 4) MOE_ROUTE_PERM(4);
+    else if (vpl <= 8) MOE_ROUTE_PERM(8);
+    else MOE_ROUTE_PERM(16);
+#undef MOE_ROUTE_PERM
     return hipGetLastError();
 }
 

@@ -27,8 +27,10 @@ def bf16_bits(t) -> np.ndarray:
 
 
 def workspace(s, device="cuda"):
+    """moe_forward workspace, zero-filled: its leading MOE_WS_ZERO_BYTES hold
+    completion counters that must start at zero (each call leaves them zero)."""
     import torch
-    return torch.empty(_lib.workspace_bytes(s), dtype=torch.uint8, device=device)
+    return torch.zeros(_lib.workspace_bytes(s), dtype=torch.uint8, device=device)
 
 
 _hip = None

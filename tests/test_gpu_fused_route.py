@@ -1,0 +1,66 @@
+"""The single-launch few-token routing of moe_forward (router chunk sums,
+then -- in the last block to finish -- top-k and permutation) against the
+stage-by-stage C ABI path (moe_route, moe_permute, the two grouped GEMMs,
+moe_combine) on the same inputs: routing, weights and output must agree
+bitwise, and the completion counter must be back to zero after every call."""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+import mixture_experts_router_amd as moe
+from mixture_experts_router_amd import device as dev
+from gpu_helpers import say, upload, run_forward
+
+pytestmark = pytest.mark.gpu
+
+WS_ZERO_BYTES = 256   # MOE_WS_ZERO_BYTES in include/moe.h
+
+SHAPES = {
+    "decode-like": mi.Shape(T=8, H=512, E=128, k=8, I=128),          # 64 assignments: one-wave permutation
+    "one-token": mi.Shape(T=1, H=256, E=8, k=1, I=64),
+    "64-tokens": mi.Shape(T=64, H=512, E=64, k=8, I=128),            # 4 token tiles, block permutation
+    "wide-experts": mi.Shape(T=2, H=256, E=1024, k=32, I=64),        # 16 logits per lane
+    "odd-experts": mi.Shape(T=40, H=768, E=300, k=6, I=64),          # 3 chunks of 256, partial expert block
+    "skew-bias": mi.Shape(T=16, H=512, E=128, k=8, I=64, skew=True),
+}
+
+
+def _staged(d, s):
+    sh = d["shape"]
+    A = s.T * s.k
+    i32 = dict(dtype=torch.int32, device="cuda")
+    logits = torch.empty((s.T, s.E), dtype=torch.float32, device="cuda")
+    ids = torch.empty((s.T, s.k), **i32)
+    w = torch.empty((s.T, s.k), dtype=torch.float32, device="cuda")
+    counts, offsets = torch.empty(s.E, **i32), torch.empty(s.E + 1, **i32)
+    sorted_ids, inv = torch.empty(A, **i32), torch.empty(A, **i32)
+    x_perm = torch.empty((A, s.H), dtype=torch.bfloat16, device="cuda")
+    h = torch.empty((A, s.I), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((A, s.H), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((s.T, s.H), dtype=torch.bfloat16, device="cuda")
+    rws = torch.empty(max(1, moe.route_workspace_bytes(sh)), dtype=torch.uint8, device="cuda")
+    pws = torch.empty(max(1, moe.permute_workspace_bytes(sh)), dtype=torch.uint8, device="cuda")
+    moe.route(sh, d["x"], d["w_router"], d["bias"], logits, ids, w, ws=rws)
+    moe.permute(sh, ids, d["x"], counts, offsets, sorted_ids, inv, x_perm, pws)
+    moe.gemm_gateup(sh, d["x"], sorted_ids, offsets, d["w_gu"], d["gu_s"], h)
+    moe.gemm_down(sh, h, offsets, d["w_d"], d["d_s"], y)
+    moe.combine(sh, y, inv, w, out)
+    torch.cuda.synchronize()
+    return out, ids, w
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_fused_routing_matches_staged_path(gpu, name):
+    s = SHAPES[name]
+    say(f"fused routing {name}: {s}")
+    inp = mi.make(s, seed=11)
+    d = upload(inp)
+    ws = dev.workspace(d["shape"])
+    for call in range(3):      # the counter must reset itself between calls
+        out, ids, w = run_forward(inp, d, ws)
+        assert int(ws[:WS_ZERO_BYTES].count_nonzero()) == 0, f"counter not reset after call {call}"
+    o2, i2, w2 = _staged(d, s)
+    assert torch.equal(ids, i2)
+    assert torch.equal(w.view(torch.int32), w2.view(torch.int32))
+    assert (dev.bf16_bits(out) == dev.bf16_bits(o2)).all()
