@@ -42,6 +42,7 @@ def parse():
     p.add_argument("--rotate", type=int, default=4, help="device copies of the weights cycled per step")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle timing")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a device copy of MIB mebibytes (counter calibration) and exit")
     return p.parse_args()
@@ -234,6 +235,47 @@ def main():
     gateup_launch_us = start.elapsed_time(end) / K * 1e3
     print(f"# gate/up kernel alone: {gateup_launch_us:.1f} us per launch", file=sys.stderr, flush=True)
 
+    # Timed region 4: K steps, each bracketed by its own pair of events ->
+    # the spread of the step time (each pair adds its own record latency).
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        ev_a[i].record()
+        step(i)
+        ev_b[i].record()
+    torch.cuda.synchronize()
+    per_step = np.array([a.elapsed_time(b) * 1e3 for a, b in zip(ev_a, ev_b)])
+    spread = {"p10": float(np.percentile(per_step, 10)), "p50": float(np.percentile(per_step, 50)),
+              "p90": float(np.percentile(per_step, 90))}
+
+    # Timed region 5: the same steps captured once as a HIP graph (one
+    # moe_forward per weight copy) and replayed back to back.
+    graph_us = None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step(0)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for i in range(len(copies)):
+                step(i)
+        g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, K // len(copies))
+        start.record()
+        for _ in range(reps):
+            g.replay()
+        end.record()
+        torch.cuda.synchronize()
+        graph_us = start.elapsed_time(end) * 1e3 / (reps * len(copies))
+    print(f"# per-step events p10/p50/p90 {spread['p10']:.1f}/{spread['p50']:.1f}/{spread['p90']:.1f} us; "
+          f"graph replay {graph_us if graph_us is None else round(graph_us, 1)} us per step",
+          file=sys.stderr, flush=True)
+
     tokens_per_s = s.T / (ms * 1e-3)
     gu_s = gateup_launch_us * 1e-6
     ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
@@ -278,6 +320,7 @@ def main():
             "avg_launch_us": gateup_launch_us,
         },
         "layer": layer,
+        "step_us": {"mean_back_to_back": ms * 1e3, "per_step_events": spread, "graph_replay": graph_us},
         "stages_us": stage_avg_us,
     }
     if not args.no_cpu_baseline:
