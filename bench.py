@@ -38,7 +38,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--config", default="decode", help="tiny|decode|prefill|skew|mxfp4")
+    p.add_argument("--config", default="decode", help="tiny|decode|prefill|skew|mxfp4|decode_shared")
     p.add_argument("--rotate", type=int, default=4, help="device copies of the weights cycled per step")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle timing")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -65,6 +65,14 @@ def algorithmic(inp, ids):
     layer_flops = T * (2 * H * E + k * (2 * H * 2 * I + 2 * I * H))
     gateup_bytes = U * gu_bytes + T * H * 2 + A * I * 2
     gateup_flops = A * 2 * H * 2 * I
+    if s.I_sh:   # the dense MLP: its weights once, its FLOPs on every token
+        Is = s.I_sh
+        sh_gu = 2 * Is * (H // 2 + H // 32) if s.mxfp4 else 2 * Is * H * 2
+        sh_d = H * (Is // 2 + Is // 32) if s.mxfp4 else H * Is * 2
+        layer_bytes += sh_gu + sh_d
+        layer_flops += T * (2 * H * 2 * Is + 2 * Is * H)
+        gateup_bytes += sh_gu + T * Is * 2
+        gateup_flops += T * 2 * H * 2 * Is
     return dict(U=U, layer_bytes=layer_bytes, layer_flops=layer_flops, gateup_bytes=gateup_bytes,
                 gateup_flops=gateup_flops, gu_bytes_per_expert=gu_bytes)
 
@@ -158,17 +166,27 @@ def main():
     gus = dev.to_device(inp.gu_scales) if s.mxfp4 else None
     ds = dev.to_device(inp.d_scales) if s.mxfp4 else None
     copies = [(gu0, d0)] + [(gu0.clone(), d0.clone()) for _ in range(max(0, args.rotate - 1))]
+    if s.I_sh:   # the dense MLP's weights rotate with the experts'
+        sg0, sd0 = dev.to_device(inp.w_sh_gate_up), dev.to_device(inp.w_sh_down)
+        sh_copies = [(sg0, sd0)] + [(sg0.clone(), sd0.clone()) for _ in range(len(copies) - 1)]
+        sgs = dev.to_device(inp.sh_gu_scales) if s.mxfp4 else None
+        sds = dev.to_device(inp.sh_d_scales) if s.mxfp4 else None
     out = torch.empty((s.T, s.H), dtype=torch.bfloat16, device="cuda")
     ids = torch.empty((s.T, s.k), dtype=torch.int32, device="cuda")
     wts = torch.empty((s.T, s.k), dtype=torch.float32, device="cuda")
-    ws = dev.workspace(sh)
+    ws = dev.workspace(sh, I_sh=s.I_sh)
     torch.cuda.synchronize()
     gen_s = time.perf_counter() - t_gen
     print(f"# inputs ready in {gen_s:.1f}s: {args.config} {s}", file=sys.stderr, flush=True)
 
     def step(i, events=None):
         gu, d = copies[i % len(copies)]
-        moe.forward(sh, x, wr, bias, gu, gus, d, ds, out, ids, wts, ws, stage_events=events)
+        if s.I_sh:
+            sg, sd = sh_copies[i % len(copies)]
+            moe.forward_shared(sh, x, wr, bias, gu, gus, d, ds, s.I_sh, sg, sgs, sd, sds, out, ids, wts, ws,
+                               stage_events=events)
+        else:
+            moe.forward(sh, x, wr, bias, gu, gus, d, ds, out, ids, wts, ws, stage_events=events)
 
     for i in range(args.warmup):
         step(i)
@@ -225,15 +243,23 @@ def main():
     torch.cuda.synchronize()
     if not torch.equal(r_ids.cpu(), ids.cpu()):
         raise RuntimeError("moe_route and moe_forward disagree on the routing")
-    moe.gemm_gateup(sh, x, sorted_ids, offsets, copies[0][0], gus, h)
-    torch.cuda.synchronize()
-    start.record()
-    for i in range(K):
-        moe.gemm_gateup(sh, x, sorted_ids, offsets, copies[i % len(copies)][0], gus, h)
-    end.record()
-    torch.cuda.synchronize()
-    gateup_launch_us = start.elapsed_time(end) / K * 1e3
-    print(f"# gate/up kernel alone: {gateup_launch_us:.1f} us per launch", file=sys.stderr, flush=True)
+    if s.I_sh:
+        # the shared-MLP tiles run inside the forward's gate/up launch only:
+        # take that launch's duration from the stage events (includes the
+        # gap an event adds)
+        gateup_launch_us = stage_avg_us["gateup"]
+        print(f"# gate/up launch (experts + dense MLP, stage events): {gateup_launch_us:.1f} us",
+              file=sys.stderr, flush=True)
+    else:
+        moe.gemm_gateup(sh, x, sorted_ids, offsets, copies[0][0], gus, h)
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(K):
+            moe.gemm_gateup(sh, x, sorted_ids, offsets, copies[i % len(copies)][0], gus, h)
+        end.record()
+        torch.cuda.synchronize()
+        gateup_launch_us = start.elapsed_time(end) / K * 1e3
+        print(f"# gate/up kernel alone: {gateup_launch_us:.1f} us per launch", file=sys.stderr, flush=True)
 
     # Timed region 4: K steps, each bracketed by its own pair of events ->
     # the spread of the step time (each pair adds its own record latency).
@@ -308,9 +334,11 @@ def main():
         "config": {"workload": f"Gemma-4-26B-A4B MoE FFN layer, {args.config}: T={s.T} tokens, "
                                f"hidden {s.H}, {s.E} experts, top-{s.k}, intermediate {s.I}, "
                                f"GEGLU, {'MXFP4' if s.mxfp4 else 'bf16'} expert weights"
-                               f"{', Zipf(1.2) router bias' if s.skew else ''}",
+                               f"{', Zipf(1.2) router bias' if s.skew else ''}"
+                               f"{f', plus the dense GEGLU MLP (intermediate {s.I_sh}) as a shared expert' if s.I_sh else ''}",
                    "T": s.T, "H": s.H, "E": s.E, "k": s.k, "I": s.I,
-                   "weights": "mxfp4" if s.mxfp4 else "bf16", "weight_copies": len(copies)},
+                   "weights": "mxfp4" if s.mxfp4 else "bf16", "weight_copies": len(copies),
+                   **({"I_shared": s.I_sh} if s.I_sh else {})},
         "roofline": {
             "kernel": "grouped_gemm gate/up + GEGLU",
             "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,

@@ -188,9 +188,44 @@ int moe_forward(const moe_shape *s, const uint16_t *x, const uint16_t *w_router,
                 float *topk_w_out, void *ws, size_t ws_bytes,
                 moe_stream_t stream, const moe_event_t *stage_events);
 
+/*
+ * moe_forward_shared -- moe_forward plus an always-on dense GEGLU MLP of
+ * intermediate size I_sh applied to every token and added with weight 1 (the
+ * decoder block runs a dense MLP next to the MoE: Gemma-4-26B-A4B
+ * optimisation report, section 1, dense MLP of intermediate 2112; section 5,
+ * its gate/up width 4224):
+ *   out[t] = MLP(x[t]) + sum_j topk_w[t][j] * expert_j(x[t]),
+ *   MLP(x) = (gelu_tanh(x Wg^T) * (x Wu^T)) Wd^T
+ * The MLP runs as one more group inside the same two grouped GEMM launches;
+ * its h and output rows are rounded to bf16 like the experts', and the
+ * combine starts its fp32 sum from the MLP row.
+ *   I_sh          > 0, multiple of 64
+ *   w_sh_gate_up  [2*I_sh][H] (gate rows first) in the experts' format:
+ *                 bf16 (sh_gu_scales NULL) or MXFP4 codes [2*I_sh][H/2] with
+ *                 scales [2*I_sh][H/32]
+ *   w_sh_down     [H][I_sh] likewise (sh_d_scales [H][I_sh/32] for MXFP4)
+ *   ws            at least moe_workspace_shared_bytes(s, I_sh) bytes, with
+ *                 the same zero-prefix rule as moe_forward
+ *   other arguments, errors and execution as for moe_forward
+ */
+int moe_forward_shared(const moe_shape *s, const uint16_t *x,
+                       const uint16_t *w_router, const float *router_bias,
+                       const void *w_gate_up, const uint8_t *gu_scales,
+                       const void *w_down, const uint8_t *d_scales,
+                       int32_t I_sh, const void *w_sh_gate_up,
+                       const uint8_t *sh_gu_scales, const void *w_sh_down,
+                       const uint8_t *sh_d_scales, uint16_t *out,
+                       int32_t *topk_ids_out, float *topk_w_out, void *ws,
+                       size_t ws_bytes, moe_stream_t stream,
+                       const moe_event_t *stage_events);
+
 /* Workspace bytes moe_forward needs for this shape; 0 for an invalid or
  * unsupported shape.  Monotone in T. */
 size_t moe_workspace_bytes(const moe_shape *s);
+
+/* Workspace bytes moe_forward_shared needs; 0 for an invalid shape or an
+ * I_sh that is not a positive multiple of 64. */
+size_t moe_workspace_shared_bytes(const moe_shape *s, int32_t I_sh);
 
 /* Workspace bytes moe_route needs for this shape (0: none needed, or an
  * invalid shape).  Few tokens use a split-K router with per-chunk partial

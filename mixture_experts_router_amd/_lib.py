@@ -16,8 +16,9 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARGUMENT", -2: "MOE_ERR_UNSUPPORTED"
 
 # Entry points declared in include/moe.h.
 EXPORTS = ("moe_route", "moe_permute", "moe_grouped_gemm_gateup", "moe_grouped_gemm_down",
-           "moe_combine", "moe_forward", "moe_workspace_bytes", "moe_route_workspace_bytes",
-           "moe_permute_workspace_bytes", "moe_status_string")
+           "moe_combine", "moe_forward", "moe_forward_shared", "moe_workspace_bytes",
+           "moe_workspace_shared_bytes", "moe_route_workspace_bytes", "moe_permute_workspace_bytes",
+           "moe_status_string")
 
 
 class MoeShape(ctypes.Structure):
@@ -58,6 +59,8 @@ def load(path: str = LIB_PATH):
         "moe_grouped_gemm_down": [_S, _P, _P, _P, _P, _P, _P],
         "moe_combine": [_S, _P, _P, _P, _P, _P],
         "moe_forward": [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, c_size, _P, _P],
+        "moe_forward_shared": [_S, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P,
+                               c_size, _P, _P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -67,6 +70,8 @@ def load(path: str = LIB_PATH):
         f = getattr(lib, name)
         f.argtypes = [_S]
         f.restype = c_size
+    lib.moe_workspace_shared_bytes.argtypes = [_S, ctypes.c_int32]
+    lib.moe_workspace_shared_bytes.restype = c_size
     lib.moe_status_string.argtypes = [c_int]
     lib.moe_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -104,6 +109,10 @@ def _check(fn, st):
 
 def workspace_bytes(s: MoeShape) -> int:
     return load().moe_workspace_bytes(ctypes.byref(s))
+
+
+def workspace_shared_bytes(s: MoeShape, I_sh: int) -> int:
+    return load().moe_workspace_shared_bytes(ctypes.byref(s), I_sh)
 
 
 def route_workspace_bytes(s: MoeShape) -> int:
@@ -160,3 +169,17 @@ def forward(s, x, w_router, router_bias, w_gate_up, gu_scales, w_down, d_scales,
            lib.moe_forward(ctypes.byref(s), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w_gate_up),
                            _ptr(gu_scales), _ptr(w_down), _ptr(d_scales), _ptr(out), _ptr(topk_ids_out),
                            _ptr(topk_w_out), _ptr(ws), nbytes, _stream(stream), ev))
+
+
+def forward_shared(s, x, w_router, router_bias, w_gate_up, gu_scales, w_down, d_scales, I_sh, w_sh_gate_up,
+                   sh_gu_scales, w_sh_down, sh_d_scales, out, topk_ids_out=None, topk_w_out=None, ws=None,
+                   stream=None, stage_events=None):
+    """moe_forward_shared: the layer plus a dense GEGLU MLP (intermediate I_sh) on every token."""
+    lib = load()
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    ev = ctypes.cast(stage_events, _P) if stage_events is not None else None
+    _check("moe_forward_shared",
+           lib.moe_forward_shared(ctypes.byref(s), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w_gate_up),
+                                  _ptr(gu_scales), _ptr(w_down), _ptr(d_scales), I_sh, _ptr(w_sh_gate_up),
+                                  _ptr(sh_gu_scales), _ptr(w_sh_down), _ptr(sh_d_scales), _ptr(out),
+                                  _ptr(topk_ids_out), _ptr(topk_w_out), _ptr(ws), nbytes, _stream(stream), ev))

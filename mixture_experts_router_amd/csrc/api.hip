@@ -71,10 +71,12 @@ struct Workspace {
     float *w;
     int32_t *counts, *offsets, *block_hist, *sorted_ids, *inv;
     uint16_t *h, *y;
+    uint16_t *h_sh;          // dense MLP (I_sh > 0 only): h rows [T][I_sh]
+    float *y_sh32;           // and its down partial sums [nsplit][T][H]
     size_t bytes;
 };
 
-Workspace carve(const moe_shape *s, void *base) {
+Workspace carve(const moe_shape *s, void *base, int I_sh = 0) {
     const size_t T = s->T, E = s->E, A = T * s->k;
     char *p = static_cast<char *>(base);
     size_t off = 0;
@@ -96,6 +98,10 @@ Workspace carve(const moe_shape *s, void *base) {
     w.inv = reinterpret_cast<int32_t *>(take(A * sizeof(int32_t)));
     w.h = reinterpret_cast<uint16_t *>(take(A * s->I * sizeof(uint16_t)));
     w.y = reinterpret_cast<uint16_t *>(take(A * s->H * sizeof(uint16_t)));
+    w.h_sh = I_sh > 0 ? reinterpret_cast<uint16_t *>(take(T * (size_t)I_sh * sizeof(uint16_t))) : nullptr;
+    w.y_sh32 = I_sh > 0 ? reinterpret_cast<float *>(take((size_t)moe::shared_splits(I_sh, s->I) * T * s->H *
+                                                          sizeof(float)))
+                        : nullptr;
     w.bytes = off;
     return w;
 }
@@ -103,6 +109,74 @@ Workspace carve(const moe_shape *s, void *base) {
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 }  // namespace
+
+static int forward_impl(const moe_shape *s, const uint16_t *x, const uint16_t *w_router, const float *router_bias,
+                        const void *w_gate_up, const uint8_t *gu_scales, const void *w_down, const uint8_t *d_scales,
+                        int32_t I_sh, const void *w_sh_gate_up, const uint8_t *sh_gu_scales, const void *w_sh_down,
+                        const uint8_t *sh_d_scales, uint16_t *out, int32_t *topk_ids_out, float *topk_w_out, void *ws,
+                        size_t ws_bytes, moe_stream_t stream, const moe_event_t *stage_events) {
+    int st = check_shape(s);
+    if (st != MOE_OK) return st;
+    if (I_sh < 0) return MOE_ERR_INVALID_ARGUMENT;
+    if (I_sh > 0) {
+        if (I_sh % 64 != 0) return MOE_ERR_UNSUPPORTED;
+        if ((st = check_weights(s, w_sh_gate_up, sh_gu_scales)) != MOE_OK) return st;
+        if ((st = check_weights(s, w_sh_down, sh_d_scales)) != MOE_OK) return st;
+    }
+    if (!x || !w_router || !out) return MOE_ERR_INVALID_ARGUMENT;
+    if (!al16(x) || !al16(w_router) || !al16(out)) return MOE_ERR_INVALID_ARGUMENT;
+    if (router_bias && !al4(router_bias)) return MOE_ERR_INVALID_ARGUMENT;
+    if ((topk_ids_out && !al4(topk_ids_out)) || (topk_w_out && !al4(topk_w_out)))
+        return MOE_ERR_INVALID_ARGUMENT;
+    if ((st = check_weights(s, w_gate_up, gu_scales)) != MOE_OK) return st;
+    if ((st = check_weights(s, w_down, d_scales)) != MOE_OK) return st;
+    if (stage_events)
+        for (int i = 0; i <= MOE_FORWARD_STAGES; ++i)
+            if (!stage_events[i]) return MOE_ERR_INVALID_ARGUMENT;
+    const size_t need = carve(s, nullptr, I_sh).bytes;
+    if (!ws || ws_bytes < need || !al16(ws)) return MOE_ERR_WORKSPACE;
+
+    Workspace w = carve(s, ws, I_sh);
+    int32_t *ids = topk_ids_out ? topk_ids_out : w.ids;
+    float *wts = topk_w_out ? topk_w_out : w.w;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const int T = s->T, H = s->H, E = s->E, k = s->k, I = s->I, A = T * k;
+    const bool mx = s->w_format == MOE_W_MXFP4;
+
+    int stage = 0;
+    auto mark = [&]() -> int {
+        if (!stage_events) return MOE_OK;
+        return hip_status(hipEventRecord(static_cast<hipEvent_t>(stage_events[stage++]), hs));
+    };
+    if ((st = mark()) != MOE_OK) return st;
+    if (moe::route_permute_fits(T, k)) {
+        // few tokens: router, top-k and the permutation in one launch (the
+        // permute stage is empty)
+        st = hip_status(moe::launch_route_permute(x, w_router, w.part, w.done, router_bias, w.logits, ids, wts,
+                                                  w.counts, w.offsets, w.sorted_ids, w.inv, T, H, E, k, hs));
+        if (st != MOE_OK || (st = mark()) != MOE_OK) return st;
+        if ((st = mark()) != MOE_OK) return st;
+    } else {
+        st = launch_route(s, x, w_router, router_bias, w.logits, ids, wts, w.part, hs);
+        if (st != MOE_OK || (st = mark()) != MOE_OK) return st;
+        st = hip_status(
+            moe::launch_permute(ids, w.counts, w.offsets, w.sorted_ids, w.inv, w.block_hist, A, E, hs));
+        if (st != MOE_OK || (st = mark()) != MOE_OK) return st;
+    }
+    // the shared expert (if any) is an extra group of the same two launches
+    const moe::SharedGroup sh_gu{x, w_sh_gate_up, sh_gu_scales, w.h_sh, nullptr, T, I_sh};
+    const moe::SharedGroup sh_d{w.h_sh, w_sh_down, sh_d_scales, nullptr, w.y_sh32, T, I_sh};
+    st = hip_status(moe::launch_gateup(x, w.sorted_ids, k, w.offsets, w_gate_up, gu_scales, w.h, A, H, E, I, mx,
+                                       I_sh > 0 ? &sh_gu : nullptr, hs));
+    if (st != MOE_OK || (st = mark()) != MOE_OK) return st;
+    st = hip_status(moe::launch_down(w.h, w.offsets, w_down, d_scales, w.y, A, H, E, I, mx,
+                                     I_sh > 0 ? &sh_d : nullptr, hs));
+    if (st != MOE_OK || (st = mark()) != MOE_OK) return st;
+    st = hip_status(moe::launch_combine(w.y, w.inv, wts, w.y_sh32, I_sh > 0 ? moe::shared_splits(I_sh, I) : 0, out,
+                                        T, H, k, hs));
+    if (st != MOE_OK) return st;
+    return mark();
+}
 
 extern "C" {
 
@@ -180,7 +254,7 @@ int moe_grouped_gemm_gateup(const moe_shape *s, const uint16_t *x, const int32_t
     if (sorted_ids && !al4(sorted_ids)) return MOE_ERR_INVALID_ARGUMENT;
     if ((st = check_weights(s, w_gate_up, gu_scales)) != MOE_OK) return st;
     return hip_status(moe::launch_gateup(x, sorted_ids, s->k, offsets, w_gate_up, gu_scales, h,
-                                         s->T * s->k, s->H, s->E, s->I, s->w_format == MOE_W_MXFP4,
+                                         s->T * s->k, s->H, s->E, s->I, s->w_format == MOE_W_MXFP4, nullptr,
                                          static_cast<hipStream_t>(stream)));
 }
 
@@ -192,7 +266,7 @@ int moe_grouped_gemm_down(const moe_shape *s, const uint16_t *h, const int32_t *
     if (!al16(h) || !al16(y) || !al4(offsets)) return MOE_ERR_INVALID_ARGUMENT;
     if ((st = check_weights(s, w_down, d_scales)) != MOE_OK) return st;
     return hip_status(moe::launch_down(h, offsets, w_down, d_scales, y, s->T * s->k, s->H, s->E, s->I,
-                                       s->w_format == MOE_W_MXFP4, static_cast<hipStream_t>(stream)));
+                                       s->w_format == MOE_W_MXFP4, nullptr, static_cast<hipStream_t>(stream)));
 }
 
 int moe_combine(const moe_shape *s, const uint16_t *y, const int32_t *inv, const float *topk_w,
@@ -201,7 +275,7 @@ int moe_combine(const moe_shape *s, const uint16_t *y, const int32_t *inv, const
     if (st != MOE_OK) return st;
     if (!y || !inv || !topk_w || !out) return MOE_ERR_INVALID_ARGUMENT;
     if (!al16(y) || !al16(out) || !al4(inv) || !al4(topk_w)) return MOE_ERR_INVALID_ARGUMENT;
-    return hip_status(moe::launch_combine(y, inv, topk_w, out, s->T, s->H, s->k,
+    return hip_status(moe::launch_combine(y, inv, topk_w, nullptr, 0, out, s->T, s->H, s->k,
                                           static_cast<hipStream_t>(stream)));
 }
 
@@ -209,55 +283,24 @@ int moe_forward(const moe_shape *s, const uint16_t *x, const uint16_t *w_router,
                 const void *w_gate_up, const uint8_t *gu_scales, const void *w_down, const uint8_t *d_scales,
                 uint16_t *out, int32_t *topk_ids_out, float *topk_w_out, void *ws, size_t ws_bytes,
                 moe_stream_t stream, const moe_event_t *stage_events) {
-    int st = check_shape(s);
-    if (st != MOE_OK) return st;
-    if (!x || !w_router || !out) return MOE_ERR_INVALID_ARGUMENT;
-    if (!al16(x) || !al16(w_router) || !al16(out)) return MOE_ERR_INVALID_ARGUMENT;
-    if (router_bias && !al4(router_bias)) return MOE_ERR_INVALID_ARGUMENT;
-    if ((topk_ids_out && !al4(topk_ids_out)) || (topk_w_out && !al4(topk_w_out)))
-        return MOE_ERR_INVALID_ARGUMENT;
-    if ((st = check_weights(s, w_gate_up, gu_scales)) != MOE_OK) return st;
-    if ((st = check_weights(s, w_down, d_scales)) != MOE_OK) return st;
-    if (stage_events)
-        for (int i = 0; i <= MOE_FORWARD_STAGES; ++i)
-            if (!stage_events[i]) return MOE_ERR_INVALID_ARGUMENT;
-    const size_t need = carve(s, nullptr).bytes;
-    if (!ws || ws_bytes < need || !al16(ws)) return MOE_ERR_WORKSPACE;
+    return forward_impl(s, x, w_router, router_bias, w_gate_up, gu_scales, w_down, d_scales, 0, nullptr, nullptr,
+                        nullptr, nullptr, out, topk_ids_out, topk_w_out, ws, ws_bytes, stream, stage_events);
+}
 
-    Workspace w = carve(s, ws);
-    int32_t *ids = topk_ids_out ? topk_ids_out : w.ids;
-    float *wts = topk_w_out ? topk_w_out : w.w;
-    hipStream_t hs = static_cast<hipStream_t>(stream);
-    const int T = s->T, H = s->H, E = s->E, k = s->k, I = s->I, A = T * k;
-    const bool mx = s->w_format == MOE_W_MXFP4;
+int moe_forward_shared(const moe_shape *s, const uint16_t *x, const uint16_t *w_router, const float *router_bias,
+                       const void *w_gate_up, const uint8_t *gu_scales, const void *w_down, const uint8_t *d_scales,
+                       int32_t I_sh, const void *w_sh_gate_up, const uint8_t *sh_gu_scales, const void *w_sh_down,
+                       const uint8_t *sh_d_scales, uint16_t *out, int32_t *topk_ids_out, float *topk_w_out,
+                       void *ws, size_t ws_bytes, moe_stream_t stream, const moe_event_t *stage_events) {
+    if (I_sh <= 0) return MOE_ERR_INVALID_ARGUMENT;
+    return forward_impl(s, x, w_router, router_bias, w_gate_up, gu_scales, w_down, d_scales, I_sh, w_sh_gate_up,
+                        sh_gu_scales, w_sh_down, sh_d_scales, out, topk_ids_out, topk_w_out, ws, ws_bytes, stream,
+                        stage_events);
+}
 
-    int stage = 0;
-    auto mark = [&]() -> int {
-        if (!stage_events) return MOE_OK;
-        return hip_status(hipEventRecord(static_cast<hipEvent_t>(stage_events[stage++]), hs));
-    };
-    if ((st = mark()) != MOE_OK) return st;
-    if (moe::route_permute_fits(T, k)) {
-        // few tokens: router, top-k and the permutation in one launch (the
-        // permute stage is empty)
-        st = hip_status(moe::launch_route_permute(x, w_router, w.part, w.done, router_bias, w.logits, ids, wts,
-                                                  w.counts, w.offsets, w.sorted_ids, w.inv, T, H, E, k, hs));
-        if (st != MOE_OK || (st = mark()) != MOE_OK) return st;
-        if ((st = mark()) != MOE_OK) return st;
-    } else {
-        st = launch_route(s, x, w_router, router_bias, w.logits, ids, wts, w.part, hs);
-        if (st != MOE_OK || (st = mark()) != MOE_OK) return st;
-        st = hip_status(
-            moe::launch_permute(ids, w.counts, w.offsets, w.sorted_ids, w.inv, w.block_hist, A, E, hs));
-        if (st != MOE_OK || (st = mark()) != MOE_OK) return st;
-    }
-    st = hip_status(moe::launch_gateup(x, w.sorted_ids, k, w.offsets, w_gate_up, gu_scales, w.h, A, H, E, I, mx, hs));
-    if (st != MOE_OK || (st = mark()) != MOE_OK) return st;
-    st = hip_status(moe::launch_down(w.h, w.offsets, w_down, d_scales, w.y, A, H, E, I, mx, hs));
-    if (st != MOE_OK || (st = mark()) != MOE_OK) return st;
-    st = hip_status(moe::launch_combine(w.y, w.inv, wts, out, T, H, k, hs));
-    if (st != MOE_OK) return st;
-    return mark();
+size_t moe_workspace_shared_bytes(const moe_shape *s, int32_t I_sh) {
+    if (check_shape(s) != MOE_OK || I_sh <= 0 || I_sh % 64 != 0) return 0;
+    return carve(s, nullptr, I_sh).bytes;
 }
 
 }  // extern "C"

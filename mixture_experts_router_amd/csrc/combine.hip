@@ -15,44 +15,17 @@ namespace moe {
 __global__ __launch_bounds__(64) void combine_kernel(const uint16_t *__restrict__ y,
                                                      const int32_t *__restrict__ inv,
                                                      const float *__restrict__ w,
-                                                     uint16_t *__restrict__ out, int H, int k) {
-    const int t = blockIdx.x;
+                                                     const float *__restrict__ y_sh32, int nsplit,
+                                                     uint16_t *__restrict__ out, int T, int H, int k) {
     const int c = blockIdx.y * 64 + threadIdx.x;   // 16-byte chunk of the row
     if (c >= H / 8) return;
-    const int32_t *ti = inv + (size_t)t * k;
-    const float *tw = w + (size_t)t * k;
-    float acc[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] = 0.f;
-    // summed in ascending j
-    for (int j0 = 0; j0 < k; j0 += 8) {
-        u32x4 v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int j = min(j0 + u, k - 1);
-            v[u] = *reinterpret_cast<const u32x4 *>(y + (size_t)ti[j] * H + c * 8);
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            if (j0 + u >= k) break;
-            const float wj = tw[j0 + u];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                acc[2 * q] = fmaf(wj, bf16_to_f32(v[u][q] & 0xFFFFu), acc[2 * q]);
-                acc[2 * q + 1] = fmaf(wj, bf16_to_f32(v[u][q] >> 16), acc[2 * q + 1]);
-            }
-        }
-    }
-    u32x4 o;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
-    *reinterpret_cast<u32x4 *>(out + (size_t)t * H + c * 8) = o;
+    combine_chunk(y, inv, w, y_sh32, nsplit, out, blockIdx.x, c * 8, T, H, k);
 }
 
-hipError_t launch_combine(const uint16_t *y, const int32_t *inv, const float *w, uint16_t *out, int T,
-                          int H, int k, hipStream_t st) {
+hipError_t launch_combine(const uint16_t *y, const int32_t *inv, const float *w, const float *y_sh32, int nsplit,
+                          uint16_t *out, int T, int H, int k, hipStream_t st) {
     if (T == 0) return hipSuccess;
-    combine_kernel<<<dim3(T, (H / 8 + 63) / 64), 64, 0, st>>>(y, inv, w, out, H, k);
+    combine_kernel<<<dim3(T, (H / 8 + 63) / 64), 64, 0, st>>>(y, inv, w, y_sh32, nsplit, out, T, H, k);
     return hipGetLastError();
 }
 

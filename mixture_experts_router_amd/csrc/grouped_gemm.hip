@@ -56,6 +56,19 @@ struct GemmArgs {
     int dense_rows;
     float *out32;             // [T][E] logits
     const float *bias;        // [E] or nullptr
+    // Optional always-on group (a dense GEGLU MLP run as a shared expert):
+    // its tiles follow the first `routed_blocks` blocks; its rows are all
+    // sh_rows tokens in order (no gather), with its own operands and sizes.
+    int routed_blocks;
+    int sh_rows;              // 0: no shared group
+    int sh_n_tiles;           // N tiles per M tile of the shared group
+    const uint16_t *sh_a;     // [sh_rows][sh_K]
+    const void *sh_w;         // [sh_w_rows][sh_K] bf16, or MXFP4 codes
+    const uint8_t *sh_scales; // [sh_w_rows][sh_K / 32] or nullptr
+    uint16_t *sh_out;         // [sh_rows][sh_n_out] bf16 (gate/up)
+    float *sh_out32;          // [sh_splits][sh_rows][sh_n_out] fp32 partial sums (down)
+    int sh_K, sh_I, sh_w_rows, sh_n_out;
+    int sh_splits, sh_ksplit; // down: K cut into sh_splits ranges of sh_ksplit (last one shorter)
 };
 
 // Locate this workgroup's M tile: tile index -> (expert, first row).  Run by
@@ -204,8 +217,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
     // spread evenly over the XCDs.
     // Small row blocks share little: there the plain order (N tile fastest)
     // spreads each expert's weight slabs over all XCDs.
+    // Shared-group tiles come after the routed ones, in plain order.
+    const bool shared = !ROUTER && p.sh_rows > 0 && (int)blockIdx.x >= p.routed_blocks;
     int mslot, nt;
-    if (BM >= 64) {
+    int split = 0;
+    if (shared) {
+        const int idx = blockIdx.x - p.routed_blocks;
+        const int per_split = ((p.sh_rows + BM - 1) / BM) * p.sh_n_tiles;
+        split = idx / per_split;
+        mslot = (idx % per_split) / p.sh_n_tiles;
+        nt = idx % p.sh_n_tiles;
+    } else if (BM >= 64) {
         const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
         mslot = xcd + 8 * (j / p.n_tiles);
         nt = j % p.n_tiles;
@@ -213,6 +235,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
         mslot = blockIdx.x / p.n_tiles;
         nt = blockIdx.x % p.n_tiles;
     }
+    // This tile's group: operands and sizes (block-uniform).
+    const uint16_t *g_a = shared ? p.sh_a : p.a;
+    const int32_t *g_gather = shared ? nullptr : p.gather;
+    const void *g_w = shared ? p.sh_w : p.w;
+    const uint8_t *g_scales = shared ? p.sh_scales : p.scales;
+    uint16_t *g_out = shared ? p.sh_out : p.out;
+    const int g_I = shared ? p.sh_I : p.I;
+    const int g_w_rows = shared ? p.sh_w_rows : p.w_rows;
+    const int g_n_out = shared ? p.sh_n_out : p.n_out;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
@@ -224,6 +255,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
         m0 = mslot * BM;
         rows = min(BM, p.dense_rows - m0);
         seg = m0;
+    } else if (shared) {                        // every token, in order
+        e = 0;
+        m0 = mslot * BM;
+        rows = min(BM, p.sh_rows - m0);
+        seg = m0;
+        stream = p.sh_rows <= p.stream_max_rows;
     } else {
         if (wave == 0) find_tile<BM>(p.offsets, p.E, mslot, s_info);
         __syncthreads();
@@ -235,8 +272,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
         seg = __builtin_amdgcn_readfirstlane(s_info[3]) + m0;             // global row of tile token 0
         stream = n_e <= p.stream_max_rows;
     }
-    const int K = p.K;
-    const int KT = K / BK;
+    const int K = shared ? p.sh_K : p.K;                 // row length of both operands
+    const int kb = shared ? split * p.sh_ksplit : 0;     // this tile's K range [kb, kb + KT*BK)
+    const int KT = (shared && p.sh_splits > 1 ? min(p.sh_ksplit, K - kb) : K) / BK;
 
     // Weight row of tile row v (0 <= v < BN), clamped to a valid row.
     auto weight_row = [&](int v) -> int {
@@ -244,10 +282,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
             const int half = WN / 2;
             const int wn = v / WN, within = v % WN;
             const int n = nt * (BN / 2) + wn * half + (within % half);
-            return n < p.I ? (within < half ? n : p.I + n) : 0;
+            return n < g_I ? (within < half ? n : g_I + n) : 0;
         }
         const int r = nt * BN + v;
-        return r < p.n_out ? r : 0;
+        return r < g_n_out ? r : 0;
     };
 
     // ---- direct-to-LDS sources.  Instruction g fills rows RPD*g .. RPD*g +
@@ -262,16 +300,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
         const int g = q * NW + wave;
         const int row = RPD * (g < NA ? g : 0) + lr;
         const int rr = row < rows ? row : 0;
-        const size_t src = p.gather ? (size_t)(p.gather[seg + rr] / p.gather_k) : (size_t)(seg + rr);
-        a_src[q] = p.a + src * K + 8 * tswz<BK>(row, lc);
+        const size_t src = g_gather ? (size_t)(g_gather[seg + rr] / p.gather_k) : (size_t)(seg + rr);
+        a_src[q] = g_a + src * K + kb + 8 * tswz<BK>(row, lc);
     }
     const uint16_t *b_src[B_W > 0 ? B_W : 1];
 #pragma unroll
     for (int q = 0; q < B_W; ++q) {
         const int g = q * NW + wave;
         const int row = RPD * (g < NB ? g : 0) + lr;
-        const size_t rid = (size_t)e * p.w_rows + weight_row(row);
-        b_src[q] = reinterpret_cast<const uint16_t *>(p.w) + rid * K + 8 * tswz<BK>(row, lc);
+        const size_t rid = (size_t)e * g_w_rows + weight_row(row);
+        b_src[q] = reinterpret_cast<const uint16_t *>(g_w) + rid * K + kb + 8 * tswz<BK>(row, lc);
     }
     // Token-row groups past the tile's last valid row are not loaded (their
     // LDS rows keep stale data that only reaches outputs never stored).
@@ -307,13 +345,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
 #pragma unroll
         for (int i = 0; i < G::MB_PER; ++i) {
             const int c = (tid + NT * i) % (G::MB_CHUNKS > 0 ? G::MB_CHUNKS : 1);
-            const size_t rid = (size_t)e * p.w_rows + weight_row(c >> 1);
-            mb_src[i] = reinterpret_cast<const char *>(p.w) + rid * (K / 2) + (c & 1) * 16;
+            const size_t rid = (size_t)e * g_w_rows + weight_row(c >> 1);
+            mb_src[i] = reinterpret_cast<const char *>(g_w) + rid * (K / 2) + kb / 2 + (c & 1) * 16;
         }
 #pragma unroll
         for (int i = 0; i < G::MS_PER; ++i) {
             const int v = (tid + NT * i) % BN;
-            ms_src[i] = p.scales + ((size_t)e * p.w_rows + weight_row(v)) * (K / 32);
+            ms_src[i] = g_scales + ((size_t)e * g_w_rows + weight_row(v)) * (K / 32) + kb / 32;
         }
     }
     auto issue_mx = [&](int kt) {
@@ -460,7 +498,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
     for (int i = 0; i < MI; ++i) {
         const int t = wm * WTM + i * 16 + lrow;
         if (t >= rows) continue;
-        uint16_t *orow = p.out + (size_t)(seg + t) * p.n_out;
+        uint16_t *orow = g_out + (size_t)(seg + t) * g_n_out;
         if (ROUTER) {
             float *lrow_out = p.out32 + (size_t)(seg + t) * p.n_out;
 #pragma unroll
@@ -478,18 +516,26 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
 #pragma unroll
             for (int j = 0; j < HALF_T; ++j) {
                 const int n = nt * (BN / 2) + wn * (WN / 2) + j * 16 + 4 * lk;
-                if (n >= p.I) continue;
+                if (n >= g_I) continue;
                 const f32x4 g = acc[j][i], u = acc[j + HALF_T][i];
                 uint2 o;
                 o.x = pack_bf16x2(gelu_tanh(g[0]) * u[0], gelu_tanh(g[1]) * u[1]);
                 o.y = pack_bf16x2(gelu_tanh(g[2]) * u[2], gelu_tanh(g[3]) * u[3]);
                 *reinterpret_cast<uint2 *>(orow + n) = o;
             }
+        } else if (shared && p.sh_out32) {   // dense MLP down: fp32 partial sum of this K range
+            float *prow = p.sh_out32 + ((size_t)split * p.sh_rows + seg + t) * g_n_out;
+#pragma unroll
+            for (int j = 0; j < NI; ++j) {
+                const int n = nt * BN + wn * WN + j * 16 + 4 * lk;
+                if (n >= g_n_out) continue;
+                *reinterpret_cast<f32x4 *>(prow + n) = acc[j][i];
+            }
         } else {
 #pragma unroll
             for (int j = 0; j < NI; ++j) {
                 const int n = nt * BN + wn * WN + j * 16 + 4 * lk;
-                if (n >= p.n_out) continue;
+                if (n >= g_n_out) continue;
                 const f32x4 v = acc[j][i];
                 uint2 o;
                 o.x = pack_bf16x2(v[0], v[1]);
@@ -521,7 +567,15 @@ static hipError_t launch_cfg(GemmArgs a, int A, hipStream_t st) {
     a.stream_max_rows = (MODE != kRouter && !MX && A / a.E <= BM / 2) ? BM : 0;
     const int slots = MODE == kRouter ? (a.dense_rows + BM - 1) / BM : mtile_slots(A, a.E, BM);
     // whole rounds of 8 groups (one per XCD)
-    const long long blocks = (long long)a.n_tiles * ((slots + 7) / 8 * 8);
+    long long blocks = (long long)a.n_tiles * ((slots + 7) / 8 * 8);
+    a.routed_blocks = (int)blocks;
+    // every group's K must be whole steps (the kernel loops K / BK times)
+    if (a.K % BK != 0 || (MODE != kRouter && a.sh_rows > 0 && (a.sh_K % BK != 0 || a.sh_ksplit % BK != 0)))
+        return hipErrorInvalidValue;
+    if (MODE != kRouter && a.sh_rows > 0) {
+        a.sh_n_tiles = GEGLU ? (a.sh_I + BN / 2 - 1) / (BN / 2) : (a.sh_n_out + BN - 1) / BN;
+        blocks += (long long)a.sh_n_tiles * ((a.sh_rows + BM - 1) / BM) * max(1, a.sh_splits);
+    }
     if (blocks == 0) return hipSuccess;
     grouped_gemm_kernel<BM, BN, WM, WN, MODE, MX, NS, BK><<<dim3((unsigned)blocks), 64 * WM * WN, 0, st>>>(a);
     return hipGetLastError();
@@ -541,7 +595,10 @@ static hipError_t launch_sized(const GemmArgs &a, int A, hipStream_t st) {
     if (mean_rows <= 16) {
         // Weight rows read in 256-byte pieces per step where K allows it
         // (measured: 2% faster than 128-byte pieces at 2816 x 1408).
-        if (!MX && a.K % 128 == 0) return launch_cfg<16, 128, 1, 4, MODE, MX, 2, MX ? 64 : 128>(a, A, st);
+        // both groups' K ranges; with a shared group the smaller stages keep
+        // four workgroups per CU, so routed and shared tiles run in one round
+        const bool k128 = a.K % 128 == 0 && a.sh_rows == 0;
+        if (!MX && k128) return launch_cfg<16, 128, 1, 4, MODE, MX, 2, MX ? 64 : 128>(a, A, st);
         return launch_cfg<16, 128, 1, 4, MODE, MX, 2, 64>(a, A, st);
     }
     if (mean_rows <= 40) return launch_cfg<32, 128, 2, 2, MODE, MX, 2, 64>(a, A, st);
@@ -551,14 +608,44 @@ static hipError_t launch_sized(const GemmArgs &a, int A, hipStream_t st) {
 
 hipError_t launch_gateup(const uint16_t *x, const int32_t *sorted_ids, int k, const int32_t *offsets,
                          const void *w, const uint8_t *scales, uint16_t *h, int A, int H, int E, int I,
-                         bool mx, hipStream_t st) {
+                         bool mx, const SharedGroup *sh, hipStream_t st) {
     GemmArgs a{x, sorted_ids, k, offsets, w, scales, h, E, H, I, I, 2 * I, 0, 0, 0, nullptr, nullptr};
+    if (sh) {   // every token through the shared gate/up weights [2 I_sh][H]
+        a.sh_rows = sh->rows;
+        a.sh_a = x;
+        a.sh_w = sh->w;
+        a.sh_scales = sh->scales;
+        a.sh_out = sh->out;
+        a.sh_K = H;
+        a.sh_I = sh->I;
+        a.sh_w_rows = 2 * sh->I;
+        a.sh_n_out = sh->I;
+        a.sh_splits = 1;
+        a.sh_ksplit = H;
+    }
     return mx ? launch_sized<kGateUp, true>(a, A, st) : launch_sized<kGateUp, false>(a, A, st);
 }
 
 hipError_t launch_down(const uint16_t *h, const int32_t *offsets, const void *w, const uint8_t *scales,
-                       uint16_t *y, int A, int H, int E, int I, bool mx, hipStream_t st) {
+                       uint16_t *y, int A, int H, int E, int I, bool mx, const SharedGroup *sh, hipStream_t st) {
     GemmArgs a{h, nullptr, 1, offsets, w, scales, y, E, I, H, I, H, 0, 0, 0, nullptr, nullptr};
+    if (sh) {   // the shared h rows [rows][I_sh] through the shared down weights [H][I_sh]
+        a.sh_rows = sh->rows;
+        a.sh_a = sh->a;
+        a.sh_w = sh->w;
+        a.sh_scales = sh->scales;
+        a.sh_out = sh->out;
+        a.sh_out = nullptr;
+        a.sh_out32 = sh->out32;
+        a.sh_K = sh->I;
+        a.sh_I = sh->I;
+        a.sh_w_rows = H;
+        a.sh_n_out = H;
+        // K cut into ranges about as long as an expert's (I), so a shared
+        // tile takes as long as a routed one; partial sums stay fp32
+        a.sh_splits = shared_splits(sh->I, I);
+        a.sh_ksplit = shared_ksplit(sh->I, I);
+    }
     return mx ? launch_sized<kDown, true>(a, A, st) : launch_sized<kDown, false>(a, A, st);
 }
 

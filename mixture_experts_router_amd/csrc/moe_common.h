@@ -69,4 +69,50 @@ __device__ __forceinline__ float gelu_tanh(float z) {
     return __fdividef(z, 1.0f + __expf(-2.0f * u));
 }
 
+// One 16-byte output chunk of the weighted combine: out[t][c..c+7] =
+// (sum_s y_sh32[s][t][c..c+7], if given) + sum_{j<k} w[t*k+j] *
+// y[inv[t*k+j]][c..c+7]: fp32 adds over s in order, then fp32 fmas in
+// ascending j, one bf16 rounding.
+__device__ __forceinline__ void combine_chunk(const uint16_t *__restrict__ y, const int32_t *__restrict__ inv,
+                                              const float *__restrict__ w, const float *__restrict__ y_sh32,
+                                              int nsplit, uint16_t *__restrict__ out, int t, int c, int T, int H,
+                                              int k) {
+    const int32_t *ti = inv + (size_t)t * k;
+    const float *tw = w + (size_t)t * k;
+    float acc[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+    for (int sp = 0; y_sh32 && sp < nsplit; ++sp) {
+        const float *r = y_sh32 + ((size_t)sp * T + t) * H + c;
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(r), b = *reinterpret_cast<const f32x4 *>(r + 4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            acc[q] += a[q];
+            acc[4 + q] += b[q];
+        }
+    }
+    for (int j0 = 0; j0 < k; j0 += 8) {
+        u32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int j = min(j0 + u, k - 1);
+            v[u] = *reinterpret_cast<const u32x4 *>(y + (size_t)ti[j] * H + c);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (j0 + u >= k) break;
+            const float wj = tw[j0 + u];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc[2 * q] = fmaf(wj, bf16_to_f32(v[u][q] & 0xFFFFu), acc[2 * q]);
+                acc[2 * q + 1] = fmaf(wj, bf16_to_f32(v[u][q] >> 16), acc[2 * q + 1]);
+            }
+        }
+    }
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+    *reinterpret_cast<u32x4 *>(out + (size_t)t * H + c) = o;
+}
+
 }  // namespace moe

@@ -37,12 +37,39 @@ hipError_t launch_permute(const int32_t *ids, int32_t *counts, int32_t *offsets,
                           hipStream_t st);
 hipError_t launch_gather_rows(const uint16_t *x, const int32_t *sorted_ids, uint16_t *x_perm,
                               int A, int H, int k, hipStream_t st);
+// Optional always-on group of the grouped GEMMs: a dense GEGLU MLP applied
+// to every token (a shared expert), tiled in the same launch as the routed
+// experts.  Gate/up: a = x (unused field), w = [2 I][H], out = h_sh
+// [rows][I] bf16; down: a = h_sh, w = [H][I], out32 = fp32 partial sums
+// [shared_splits(I, I_expert)][rows][H] over consecutive K ranges.
+struct SharedGroup {
+    const uint16_t *a;
+    const void *w;
+    const uint8_t *scales;   // MXFP4 scales or nullptr
+    uint16_t *out;
+    float *out32;
+    int rows, I;
+};
+// K ranges of the dense MLP's down GEMM: about I_sh / I_expert of them, each
+// a whole number of 64-wide steps, none empty (the last may be shorter).
+inline int shared_ksplit(int I_sh, int I_expert) {
+    int n = (I_sh + I_expert / 2) / I_expert;
+    if (n < 1) n = 1;
+    const int units = I_sh / 64;
+    return 64 * ((units + n - 1) / n);
+}
+inline int shared_splits(int I_sh, int I_expert) {
+    const int ks = shared_ksplit(I_sh, I_expert);
+    return (I_sh + ks - 1) / ks;
+}
 hipError_t launch_gateup(const uint16_t *x, const int32_t *sorted_ids, int k, const int32_t *offsets,
                          const void *w, const uint8_t *scales, uint16_t *h, int A, int H, int E, int I,
-                         bool mx, hipStream_t st);
+                         bool mx, const SharedGroup *sh, hipStream_t st);
 hipError_t launch_down(const uint16_t *h, const int32_t *offsets, const void *w, const uint8_t *scales,
-                       uint16_t *y, int A, int H, int E, int I, bool mx, hipStream_t st);
-hipError_t launch_combine(const uint16_t *y, const int32_t *inv, const float *w, uint16_t *out, int T,
-                          int H, int k, hipStream_t st);
+                       uint16_t *y, int A, int H, int E, int I, bool mx, const SharedGroup *sh, hipStream_t st);
+// y_sh32 (optional, [nsplit][T][H] fp32): partial sums of a shared-expert
+// output, added (in order) with weight 1 before the routed rows.
+hipError_t launch_combine(const uint16_t *y, const int32_t *inv, const float *w, const float *y_sh32, int nsplit,
+                          uint16_t *out, int T, int H, int k, hipStream_t st);
 
 }  // namespace moe

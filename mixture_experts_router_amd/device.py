@@ -26,11 +26,13 @@ def bf16_bits(t) -> np.ndarray:
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def workspace(s, device="cuda"):
-    """moe_forward workspace, zero-filled: its leading MOE_WS_ZERO_BYTES hold
-    completion counters that must start at zero (each call leaves them zero)."""
+def workspace(s, device="cuda", I_sh: int = 0):
+    """moe_forward (I_sh = 0) or moe_forward_shared workspace, zero-filled:
+    its leading MOE_WS_ZERO_BYTES hold completion counters that must start at
+    zero (each call leaves them zero)."""
     import torch
-    return torch.zeros(_lib.workspace_bytes(s), dtype=torch.uint8, device=device)
+    n = _lib.workspace_shared_bytes(s, I_sh) if I_sh else _lib.workspace_bytes(s)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
 _hip = None

@@ -25,6 +25,13 @@ print no data for the layer, so every value here is synthetic:
 
 Weight storage is K-contiguous: router [E, H], gate/up [E, 2I, H] with rows
 0..I-1 the gate and I..2I-1 the up projection, down [E, H, I].
+
+Shapes with ``I_sh > 0`` add the dense GEGLU MLP that runs next to the MoE in
+every decoder block (optimisation report, section 1: intermediate 2112):
+gate/up [2 I_sh, H] and down [H, I_sh], drawn like the expert weights
+(sigma 0.02, bf16) from their own generator ``default_rng([seed, 2112])`` so
+that every other draw is unchanged, and quantised to MXFP4 like the experts
+when the experts are.
 """
 from __future__ import annotations
 
@@ -52,6 +59,7 @@ class Shape:
     zipf_s: float = 1.2
     x_sigma: float = 1.0
     w_sigma: float = 0.02
+    I_sh: int = 0           # intermediate size of the always-on dense MLP (0: none)
 
     @property
     def A(self) -> int:
@@ -68,6 +76,9 @@ CONFIGS = {
     "prefill": Shape(T=2048, H=2816, E=128, k=8, I=704),
     "skew": Shape(T=8192, H=2816, E=128, k=8, I=704, skew=True),
     "mxfp4": Shape(T=2048, H=2816, E=128, k=8, I=704, mxfp4=True),
+    # the decode layer with the block's dense MLP (intermediate 2112) as an
+    # always-on shared expert
+    "decode_shared": Shape(T=8, H=2816, E=128, k=8, I=704, I_sh=2112),
 }
 
 
@@ -155,6 +166,12 @@ class Inputs:
     w_down: np.ndarray            # uint16 [E, H, I], or uint8 packed MXFP4 [E, H, I/2]
     gu_scales: Optional[np.ndarray] = None   # uint8 [E, 2I, H/32] for MXFP4
     d_scales: Optional[np.ndarray] = None    # uint8 [E, H, I/32] for MXFP4
+    # dense MLP (shape.I_sh > 0): uint16 [2 I_sh, H] and [H, I_sh], or MXFP4
+    # codes [2 I_sh, H/2], [H, I_sh/2] with scales [2 I_sh, H/32], [H, I_sh/32]
+    w_sh_gate_up: Optional[np.ndarray] = None
+    w_sh_down: Optional[np.ndarray] = None
+    sh_gu_scales: Optional[np.ndarray] = None
+    sh_d_scales: Optional[np.ndarray] = None
     meta: dict = field(default_factory=dict)
 
 
@@ -246,6 +263,15 @@ def make(config, seed: int = 0) -> Inputs:
             mx = (gu_q, gu_s, d_q, d_s)
             _MX_CACHE[key] = mx
         inp.w_gate_up, inp.gu_scales, inp.w_down, inp.d_scales = mx
+    if s.I_sh > 0:
+        d = _Drawer(np.random.default_rng([seed, 2112]))
+        sh_gu = d.into(np.empty((2 * s.I_sh, H), dtype=np.uint16), s.w_sigma)
+        sh_d = d.into(np.empty((H, s.I_sh), dtype=np.uint16), s.w_sigma)
+        if s.mxfp4:
+            inp.w_sh_gate_up, inp.sh_gu_scales = mxfp4_quantize(sh_gu)
+            inp.w_sh_down, inp.sh_d_scales = mxfp4_quantize(sh_d)
+        else:
+            inp.w_sh_gate_up, inp.w_sh_down = sh_gu, sh_d
     return inp
 
 

@@ -23,6 +23,11 @@ gelu_pytorch_tanh):
   O7  per expert: G = X W_gu^T, h = gelu_tanh(G[:, :I]) * G[:, I:], Y = h W_d^T
   O8  out[t] = sum_j w[t, j] * Y[inv[t*k + j]]
   O9  MXFP4 expert weights decoded to fp64 before O7
+  O10 shapes with a dense MLP (I_sh > 0): out[t] += MLP(x[t]) with
+      MLP(x) = (gelu_tanh(x Wg^T) * (x Wu^T)) Wd^T, the same GEGLU form as an
+      expert, weight 1 (the block runs its dense MLP of intermediate 2112 next
+      to the MoE: optimisation report, section 1; the two outputs being
+      summed is this repository's reading, the pages do not spell it out)
 
 Readings of points the pages leave open (renormalised top-k softmax,
 lowest-index tie-break, gate = first I rows of the concatenated gate/up
@@ -44,7 +49,7 @@ __all__ = [
     "bf16_to_f64", "mxfp4_to_f64", "router_logits", "topk_softmax",
     "counts_offsets", "permutation", "gelu_tanh", "gateup_geglu",
     "down_proj", "combine", "expert_weights", "forward", "forward_tokens",
-    "dense_forward", "routing_margin",
+    "dense_forward", "routing_margin", "shared_weights", "shared_mlp",
 ]
 
 
@@ -94,6 +99,17 @@ def expert_weights(inp, e: int):
         wgu = bf16_to_f64(inp.w_gate_up[e])
         wd = bf16_to_f64(inp.w_down[e])
     return wgu, wd
+
+
+def shared_weights(inp):
+    """fp64 gate/up [2 I_sh, H] and down [H, I_sh] of the dense MLP (O10), or
+    None when the shape has none."""
+    if inp.shape.I_sh <= 0:
+        return None
+    if inp.shape.mxfp4:
+        return (mxfp4_to_f64(inp.w_sh_gate_up, inp.sh_gu_scales),
+                mxfp4_to_f64(inp.w_sh_down, inp.sh_d_scales))
+    return bf16_to_f64(inp.w_sh_gate_up), bf16_to_f64(inp.w_sh_down)
 
 
 # ---------------------------------------------------------------- O2
@@ -202,6 +218,14 @@ def down_proj(h: np.ndarray, wd64: np.ndarray) -> np.ndarray:
     return h @ wd64.T
 
 
+def shared_mlp(X: np.ndarray, wsh) -> np.ndarray:
+    """The dense MLP on rows X (O10): the expert GEGLU FFN with the dense
+    weights; zeros when wsh is None."""
+    if wsh is None:
+        return np.zeros_like(X)
+    return down_proj(gateup_geglu(X, wsh[0]), wsh[1])
+
+
 # ---------------------------------------------------------------- O8
 def combine(Y: np.ndarray, inv: np.ndarray, w: np.ndarray) -> np.ndarray:
     """out[t] = sum_j w[t, j] Y[inv[t*k + j]] (O8): the weighted sum of each
@@ -242,7 +266,7 @@ def forward(inp, logits_fp32: np.ndarray | None = None) -> dict:
         h = gateup_geglu(X, wgu)
         Hh[lo:hi] = h
         Y[lo:hi] = down_proj(h, wd)
-    out = combine(Y, inv, w)
+    out = combine(Y, inv, w) + shared_mlp(x64, shared_weights(inp))
     return dict(logits=L, route_logits=Lr, ids=ids, w=w, counts=counts,
                 offsets=offsets, sorted_ids=sorted_ids, inv=inv, h=Hh, y=Y,
                 out=out, margin=routing_margin(Lr, k))
@@ -268,6 +292,7 @@ def forward_tokens(inp, tokens) -> dict:
             wgu, wd = cache[e]
             h = gateup_geglu(x64[i:i + 1], wgu)
             out[i] += w[i, j] * down_proj(h, wd)[0]
+    out += shared_mlp(x64, shared_weights(inp))
     return dict(logits=L, ids=ids, w=w, out=out, margin=routing_margin(L, k))
 
 
@@ -300,4 +325,4 @@ def dense_forward(inp) -> np.ndarray:
             wgu, wd = expert_weights(inp, e)
             F = down_proj(gateup_geglu(x64[t:t + 1], wgu), wd)[0]
             out[t] += (math.exp(L[t, e] - m) / den) * F
-    return out
+    return out + shared_mlp(x64, shared_weights(inp))

@@ -34,7 +34,27 @@ def upload(inp):
     )
     s = inp.shape
     d["shape"] = moe.shape(s.T, s.H, s.E, s.k, s.I, mxfp4=s.mxfp4)
+    if s.I_sh > 0:
+        d["sh_gu"] = dev.to_device(inp.w_sh_gate_up)
+        d["sh_d"] = dev.to_device(inp.w_sh_down)
+        d["sh_gu_s"] = dev.to_device(inp.sh_gu_scales) if inp.sh_gu_scales is not None else None
+        d["sh_d_s"] = dev.to_device(inp.sh_d_scales) if inp.sh_d_scales is not None else None
     return d
+
+
+def run_forward_shared(inp, d=None, ws=None):
+    """moe_forward_shared on generator inputs whose shape has I_sh > 0."""
+    d = d or upload(inp)
+    s = inp.shape
+    sh = d["shape"]
+    out = torch.empty((s.T, s.H), dtype=torch.bfloat16, device="cuda")
+    ids = torch.empty((s.T, s.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((s.T, s.k), dtype=torch.float32, device="cuda")
+    ws = ws if ws is not None else dev.workspace(sh, I_sh=s.I_sh)
+    moe.forward_shared(sh, d["x"], d["w_router"], d["bias"], d["w_gu"], d["gu_s"], d["w_d"], d["d_s"], s.I_sh,
+                       d["sh_gu"], d["sh_gu_s"], d["sh_d"], d["sh_d_s"], out, ids, w, ws)
+    torch.cuda.synchronize()
+    return out, ids, w
 
 
 def run_forward(inp, d=None, ws=None):

@@ -130,3 +130,32 @@ def _load_fresh(path):
         return _lib.load(path)
     finally:
         _lib._lib = saved
+
+
+def test_forward_shared_argument_checks(lib):
+    s = S()
+    b = ctypes.byref(s)
+    F = FAKE
+    big = 1 << 40
+    args = lambda I_sh, gu=F, d=F, gus=None, ds=None: (b, F, F, None, F, None, F, None, I_sh, gu, gus, d, ds,
+                                                         F, None, None, F, big, None, None)
+    assert lib.moe_forward_shared(*args(0)) == -1            # no dense MLP: use moe_forward
+    assert lib.moe_forward_shared(*args(-64)) == -1
+    assert lib.moe_forward_shared(*args(100)) == -2          # not a multiple of 64
+    assert lib.moe_forward_shared(*args(128, gu=None)) == -1
+    assert lib.moe_forward_shared(*args(128, d=MIS)) == -1   # bf16 weights must be 16-byte aligned
+    assert lib.moe_forward_shared(*args(128, gus=F)) == -1   # bf16 weights come without scales
+    small = (b, F, F, None, F, None, F, None, 128, F, None, F, None, F, None, None, F, 64, None, None)
+    assert lib.moe_forward_shared(*small) == -3
+
+
+def test_shared_workspace_sizes(lib):
+    s = S(T=16)
+    base = lib.moe_workspace_bytes(ctypes.byref(s))
+    a = lib.moe_workspace_shared_bytes(ctypes.byref(s), 128)
+    b2 = lib.moe_workspace_shared_bytes(ctypes.byref(s), 256)
+    assert base < a < b2
+    assert a - base >= 16 * 128 * 2 + 16 * 256 * 2       # h and output rows of the dense MLP
+    assert lib.moe_workspace_shared_bytes(ctypes.byref(s), 0) == 0
+    assert lib.moe_workspace_shared_bytes(ctypes.byref(s), 100) == 0
+    assert lib.moe_workspace_shared_bytes(ctypes.byref(S(T=0)), 128) == 0

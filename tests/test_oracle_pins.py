@@ -35,6 +35,10 @@ def test_golden_layer_shape_matches_configs():
     assert mi.CONFIGS["prefill"].T == g["prefill_batch"] * g["prefill_seq_len"]
     assert mi.CONFIGS["decode"].T == g["decode_batch"]
     assert g["activation"] == "gelu_pytorch_tanh"
+    sh = mi.CONFIGS["decode_shared"]
+    assert (sh.H, sh.E, sh.k, sh.I, sh.T) == (g["hidden_size"], g["num_experts"], g["top_k"],
+                                              g["moe_intermediate_size"], g["decode_batch"])
+    assert sh.I_sh == g["dense_mlp_intermediate_size"]
 
 
 # ------------------------------------------------------------------ brute force
@@ -321,3 +325,55 @@ def test_router_logits_match_torch_linear_with_bias():
     ref = torch.nn.functional.linear(x, W, b).numpy()
     got = oracle.router_logits(oracle.bf16_to_f64(inp.x), oracle.bf16_to_f64(inp.w_router), inp.router_bias)
     assert np.allclose(got, ref, rtol=1e-14, atol=1e-14)
+
+
+# ---------------------------------------------------------------- O10 dense MLP
+def _torch_geglu_mlp(x_bits, gu_bits, d_bits):
+    """Textbook dense GEGLU MLP from torch.nn.functional in float64."""
+    x = torch.from_numpy(mi.bf16_bits_to_f32(x_bits).astype(np.float64))
+    wgu = torch.from_numpy(mi.bf16_bits_to_f32(gu_bits).astype(np.float64))
+    wd = torch.from_numpy(mi.bf16_bits_to_f32(d_bits).astype(np.float64))
+    I = wgu.shape[0] // 2
+    gate = torch.nn.functional.linear(x, wgu[:I])
+    up = torch.nn.functional.linear(x, wgu[I:])
+    return torch.nn.functional.linear(torch.nn.functional.gelu(gate, approximate="tanh") * up, wd).numpy()
+
+
+def _without_shared(inp):
+    import dataclasses
+    return dataclasses.replace(inp, shape=dataclasses.replace(inp.shape, I_sh=0), w_sh_gate_up=None,
+                               w_sh_down=None, sh_gu_scales=None, sh_d_scales=None)
+
+
+def test_shared_mlp_adds_a_textbook_geglu_mlp():
+    """forward with a dense MLP = forward without it + the torch GEGLU MLP."""
+    s = mi.Shape(T=11, H=64, E=6, k=2, I=32, I_sh=96)
+    inp = mi.make(s, seed=5)
+    with_sh = oracle.forward(inp)["out"]
+    without = oracle.forward(_without_shared(inp))["out"]
+    mlp = _torch_geglu_mlp(inp.x, inp.w_sh_gate_up, inp.w_sh_down)
+    assert _rel(with_sh - without, mlp) <= 1e-13
+    assert np.abs(mlp).max() > 0
+    # the brute force and the token-by-token path include it the same way
+    assert _rel(oracle.dense_forward(inp), with_sh) <= 1e-12
+    assert _rel(oracle.forward_tokens(inp, [0, 4, 10])["out"], with_sh[[0, 4, 10]]) <= 1e-13
+
+
+def test_zero_shared_weights_change_nothing():
+    s = mi.Shape(T=7, H=64, E=5, k=2, I=32, I_sh=64)
+    inp = mi.make(s, seed=6)
+    inp.w_sh_gate_up = np.zeros_like(inp.w_sh_gate_up)
+    assert (oracle.forward(inp)["out"] == oracle.forward(_without_shared(inp))["out"]).all()
+
+
+def test_shared_mlp_mxfp4_matches_its_decoded_weights():
+    """MXFP4 dense weights: the oracle's MLP equals the torch MLP on the
+    decoded (bf16-exact) weights."""
+    s = mi.Shape(T=6, H=64, E=4, k=2, I=32, I_sh=64, mxfp4=True)
+    inp = mi.make(s, seed=8)
+    gu = oracle.mxfp4_to_f64(inp.w_sh_gate_up, inp.sh_gu_scales)
+    d = oracle.mxfp4_to_f64(inp.w_sh_down, inp.sh_d_scales)
+    ref = _torch_geglu_mlp(inp.x, mi.f32_to_bf16_bits(gu.astype(np.float32)), mi.f32_to_bf16_bits(d.astype(np.float32)))
+    assert (mi.bf16_bits_to_f32(mi.f32_to_bf16_bits(gu.astype(np.float32))) == gu).all()   # exact in bf16
+    got = oracle.shared_mlp(oracle.bf16_to_f64(inp.x), oracle.shared_weights(inp))
+    assert _rel(got, ref) <= 1e-13
