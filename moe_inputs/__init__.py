@@ -60,6 +60,7 @@ class Shape:
     x_sigma: float = 1.0
     w_sigma: float = 0.02
     I_sh: int = 0           # intermediate size of the always-on dense MLP (0: none)
+    a4: bool = False        # with mxfp4: activations quantised to MXFP4 too (W4A4)
 
     @property
     def A(self) -> int:
@@ -79,6 +80,8 @@ CONFIGS = {
     # the decode layer with the block's dense MLP (intermediate 2112) as an
     # always-on shared expert
     "decode_shared": Shape(T=8, H=2816, E=128, k=8, I=704, I_sh=2112),
+    # the prefill with MXFP4 experts and MXFP4 activations (W4A4)
+    "w4a4": Shape(T=2048, H=2816, E=128, k=8, I=704, mxfp4=True, a4=True),
 }
 
 
@@ -241,6 +244,8 @@ _MX_CACHE: dict = {}
 def make(config, seed: int = 0) -> Inputs:
     """Draw the inputs of one configuration (a name from CONFIGS or a Shape)."""
     s = make_shape(config)
+    if s.a4 and not s.mxfp4:
+        raise ValueError("W4A4 (a4) needs MXFP4 weights (mxfp4)")
     T, H, E, k, I = s.T, s.H, s.E, s.k, s.I
     w_router, w_gu, w_d, state = _weights(s, seed)
     rng = np.random.default_rng(seed)

@@ -23,6 +23,12 @@ gelu_pytorch_tanh):
   O7  per expert: G = X W_gu^T, h = gelu_tanh(G[:, :I]) * G[:, I:], Y = h W_d^T
   O8  out[t] = sum_j w[t, j] * Y[inv[t*k + j]]
   O9  MXFP4 expert weights decoded to fp64 before O7
+  O11 W4A4 (MXFP4 weights and activations): x, and the bf16 h of every GEGLU,
+      are quantised per 32 consecutive K values to MXFP4 (the OCP MX v1.0
+      conversion: shared scale 2^(floor(log2 amax) - 2), elements rounded to
+      the nearest E2M1 value, ties to the even code, saturating at 6) before
+      their matmuls; the router keeps the bf16 x (the pages name w4a4 MXFP4
+      checkpoints: vLLM-Ascend Gemma4 tutorial, section 3.1)
   O10 shapes with a dense MLP (I_sh > 0): out[t] += MLP(x[t]) with
       MLP(x) = (gelu_tanh(x Wg^T) * (x Wu^T)) Wd^T, the same GEGLU form as an
       expert, weight 1 (the block runs its dense MLP of intermediate 2112 next
@@ -50,6 +56,7 @@ __all__ = [
     "counts_offsets", "permutation", "gelu_tanh", "gateup_geglu",
     "down_proj", "combine", "expert_weights", "forward", "forward_tokens",
     "dense_forward", "routing_margin", "shared_weights", "shared_mlp",
+    "mx_quantize", "mx_dequantize", "mx_round", "round_to_bf16",
 ]
 
 
@@ -99,6 +106,72 @@ def expert_weights(inp, e: int):
         wgu = bf16_to_f64(inp.w_gate_up[e])
         wd = bf16_to_f64(inp.w_down[e])
     return wgu, wd
+
+
+# ---------------------------------------------------------------- O11
+_E2M1_MAG = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]   # codes 0..7, code 8..15 negative
+
+
+def _e2m1_code(q: float) -> int:
+    """Nearest E2M1 code of q (already divided by the block scale): the
+    magnitude with the least distance, the even code on a tie, 6 for
+    everything beyond; the sign bit from q's sign (so -0.0 -> code 8)."""
+    m = abs(q)
+    best = 0
+    for c in range(1, 8):
+        d, db = abs(m - _E2M1_MAG[c]), abs(m - _E2M1_MAG[best])
+        if d < db or (d == db and c % 2 == 0):
+            best = c
+    return best | (8 if math.copysign(1.0, q) < 0 else 0)
+
+
+def mx_quantize(v) -> tuple:
+    """MXFP4 codes and E8M0 scale bytes of rows of values, per 32 along the
+    last axis (O11).  Returns (codes uint8 [..., K] one code per value,
+    scales uint8 [..., K/32]).  A block's scale exponent is floor(log2 amax)
+    - 2, clamped to [-127, 127]; an all-zero block gets exponent 0.  Each
+    value takes the grid magnitude at the least distance (an array of all
+    eight distances), the even code on a tie, and its own sign bit -- the
+    rule of `_e2m1_code`, which the tests compare this against."""
+    v = np.asarray(v, dtype=np.float64)
+    K = v.shape[-1]
+    if K % 32:
+        raise ValueError("MXFP4 blocks need K % 32 == 0")
+    blk = v.reshape(*v.shape[:-1], K // 32, 32)
+    amax = np.max(np.abs(blk), axis=-1)
+    ex = np.frexp(amax)[1].astype(np.int64) - 1 - 2          # floor(log2 amax) - 2
+    e = np.where(amax == 0.0, 0, np.clip(ex, -127, 127))
+    q = blk / np.ldexp(1.0, e)[..., None]                     # exact: a power of two
+    dist = np.abs(np.abs(q)[..., None] - np.asarray(_E2M1_MAG))    # [..., 32, 8]
+    best = dist.min(axis=-1, keepdims=True)
+    tie_pref = np.where(np.arange(8) % 2 == 0, 0, 1)          # even codes first on a tie
+    score = np.where(dist == best, tie_pref, 2)
+    code = np.argmin(score, axis=-1).astype(np.uint8)
+    code = code | np.where(np.signbit(q), 8, 0).astype(np.uint8)
+    return code.reshape(v.shape), (e + 127).astype(np.uint8)
+
+
+def mx_dequantize(codes, scales) -> np.ndarray:
+    """Values of one-code-per-value MXFP4 data (O11)."""
+    codes = np.asarray(codes, dtype=np.int64)
+    K = codes.shape[-1]
+    vals = _E2M1[codes].reshape(*codes.shape[:-1], K // 32, 32)
+    f = np.ldexp(1.0, np.asarray(scales, dtype=np.int64) - 127)
+    return (vals * f[..., None]).reshape(codes.shape)
+
+
+def mx_round(v) -> np.ndarray:
+    """v quantised to MXFP4 and decoded again."""
+    return mx_dequantize(*mx_quantize(v))
+
+
+def round_to_bf16(v) -> np.ndarray:
+    """fp64 -> fp32 (nearest even) -> bf16 (nearest even), as an fp32 kernel
+    rounds a value it holds in fp32."""
+    f = np.asarray(v, dtype=np.float64).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32).astype(np.float64)
 
 
 def shared_weights(inp):
@@ -218,12 +291,16 @@ def down_proj(h: np.ndarray, wd64: np.ndarray) -> np.ndarray:
     return h @ wd64.T
 
 
-def shared_mlp(X: np.ndarray, wsh) -> np.ndarray:
+def shared_mlp(X: np.ndarray, wsh, a4: bool = False) -> np.ndarray:
     """The dense MLP on rows X (O10): the expert GEGLU FFN with the dense
-    weights; zeros when wsh is None."""
+    weights (and, under W4A4, its h quantised like an expert's); zeros when
+    wsh is None."""
     if wsh is None:
         return np.zeros_like(X)
-    return down_proj(gateup_geglu(X, wsh[0]), wsh[1])
+    h = gateup_geglu(X, wsh[0])
+    if a4:
+        h = mx_round(round_to_bf16(h))
+    return down_proj(h, wsh[1])
 
 
 # ---------------------------------------------------------------- O8
@@ -254,6 +331,8 @@ def forward(inp, logits_fp32: np.ndarray | None = None) -> dict:
     ids, w = topk_softmax(Lr, k)
     counts, offsets = counts_offsets(ids, E)
     sorted_ids, inv = permutation(ids)
+    a4 = getattr(s, "a4", False)
+    xe = mx_round(x64) if a4 else x64     # what the expert matmuls read (O11)
     Y = np.zeros((T * k, H), dtype=np.float64)
     Hh = np.zeros((T * k, I), dtype=np.float64)
     for e in range(E):
@@ -261,12 +340,14 @@ def forward(inp, logits_fp32: np.ndarray | None = None) -> dict:
         if hi == lo:
             continue                      # empty expert: its weights are never read
         rows = sorted_ids[lo:hi]
-        X = x64[rows // k]
+        X = xe[rows // k]
         wgu, wd = expert_weights(inp, e)
         h = gateup_geglu(X, wgu)
+        if a4:
+            h = mx_round(round_to_bf16(h))
         Hh[lo:hi] = h
         Y[lo:hi] = down_proj(h, wd)
-    out = combine(Y, inv, w) + shared_mlp(x64, shared_weights(inp))
+    out = combine(Y, inv, w) + shared_mlp(xe, shared_weights(inp), a4)
     return dict(logits=L, route_logits=Lr, ids=ids, w=w, counts=counts,
                 offsets=offsets, sorted_ids=sorted_ids, inv=inv, h=Hh, y=Y,
                 out=out, margin=routing_margin(Lr, k))
@@ -282,6 +363,8 @@ def forward_tokens(inp, tokens) -> dict:
     x64 = bf16_to_f64(inp.x[tokens])
     L = router_logits(x64, bf16_to_f64(inp.w_router), inp.router_bias)
     ids, w = topk_softmax(L, k)
+    a4 = getattr(s, "a4", False)
+    xe = mx_round(x64) if a4 else x64
     out = np.zeros((len(tokens), s.H), dtype=np.float64)
     cache = {}
     for i in range(len(tokens)):
@@ -290,9 +373,11 @@ def forward_tokens(inp, tokens) -> dict:
             if e not in cache:
                 cache[e] = expert_weights(inp, e)
             wgu, wd = cache[e]
-            h = gateup_geglu(x64[i:i + 1], wgu)
+            h = gateup_geglu(xe[i:i + 1], wgu)
+            if a4:
+                h = mx_round(round_to_bf16(h))
             out[i] += w[i, j] * down_proj(h, wd)[0]
-    out += shared_mlp(x64, shared_weights(inp))
+    out += shared_mlp(xe, shared_weights(inp), a4)
     return dict(logits=L, ids=ids, w=w, out=out, margin=routing_margin(L, k))
 
 

@@ -377,3 +377,78 @@ def test_shared_mlp_mxfp4_matches_its_decoded_weights():
     assert (mi.bf16_bits_to_f32(mi.f32_to_bf16_bits(gu.astype(np.float32))) == gu).all()   # exact in bf16
     got = oracle.shared_mlp(oracle.bf16_to_f64(inp.x), oracle.shared_weights(inp))
     assert _rel(got, ref) <= 1e-13
+
+
+# ---------------------------------------------------------------- O11 W4A4
+def test_mx_quantizer_matches_scalar_rule_and_generator_encoder():
+    """The vectorised quantiser against the one-value rule, and against the
+    generator's independent encoder of the same OCP conversion."""
+    from oracle import moe_oracle as om
+    rng = np.random.default_rng(3)
+    v = (rng.standard_normal((40, 96)) * np.exp(rng.uniform(-6, 6, (40, 1)))).astype(np.float32)
+    v = mi.bf16_bits_to_f32(mi.f32_to_bf16_bits(v)).astype(np.float64)
+    codes, scales = oracle.mx_quantize(v)
+    for r in range(0, 40, 7):
+        for b in range(3):
+            e = int(scales[r, b]) - 127
+            for i in range(32):
+                assert codes[r, 32 * b + i] == om._e2m1_code(v[r, 32 * b + i] / 2.0 ** e)
+    packed, gscales = mi.mxfp4_quantize(mi.f32_to_bf16_bits(v.astype(np.float32)))
+    assert (gscales == scales).all()
+    assert (packed == (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)).all()
+
+
+def test_mx_quantizer_representable_values_ties_saturation_zero():
+    # every E2M1 value times a block scale that the block's amax selects comes back exactly
+    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    rng = np.random.default_rng(4)
+    for e in (-10, 0, 7):
+        blk = rng.choice(np.concatenate([grid, -grid]), size=32)
+        blk[5] = 6.0                                   # amax 6 * 2^e -> exponent e
+        vals = blk * 2.0 ** e
+        c, s = oracle.mx_quantize(vals[None])
+        assert s[0, 0] == e + 127
+        assert (oracle.mx_dequantize(c, s)[0] == vals).all()
+    # amax 7.9: floor(log2 7.9) = 2 -> exponent 0, so the values keep their
+    # size; every midpoint goes to its even code and 7.9 saturates at 6
+    blk = np.zeros(32)
+    blk[:9] = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.9, 4.0]
+    c, s = oracle.mx_quantize(blk[None])
+    assert s[0, 0] == 127
+    assert c[0, :9].tolist() == [0, 2, 2, 4, 4, 6, 6, 7, 6]
+    # amax 8 -> exponent 1: 8 / 2 = 4 (code 6), 4 / 2 = 2 (code 4)
+    blk[7] = 8.0
+    c, s = oracle.mx_quantize(blk[None])
+    assert s[0, 0] == 128 and c[0, 7] == 6 and c[0, 8] == 4
+    # zero block: scale byte 127, codes 0; negative zero keeps its sign bit
+    z = np.zeros((1, 32))
+    z[0, 3] = -0.0
+    cz, sz = oracle.mx_quantize(z)
+    assert sz[0, 0] == 127 and cz[0, 3] == 8 and cz[0, 0] == 0
+
+
+def test_w4a4_single_expert_is_a_quantised_textbook_ffn():
+    """E = 1, k = 1, W4A4: the torch GEGLU FFN on the quantised x, with h
+    rounded to bf16 and quantised before the down projection."""
+    s = mi.Shape(T=6, H=64, E=1, k=1, I=64, mxfp4=True, a4=True)
+    inp = mi.make(s, seed=12)
+    r = oracle.forward(inp)
+    xq = torch.from_numpy(oracle.mx_round(oracle.bf16_to_f64(inp.x)))
+    wgu = torch.from_numpy(oracle.mxfp4_to_f64(inp.w_gate_up[0], inp.gu_scales[0]))
+    wd = torch.from_numpy(oracle.mxfp4_to_f64(inp.w_down[0], inp.d_scales[0]))
+    g = torch.nn.functional.linear(xq, wgu[:64])
+    u = torch.nn.functional.linear(xq, wgu[64:])
+    h = torch.nn.functional.gelu(g, approximate="tanh") * u
+    hq = torch.from_numpy(oracle.mx_round(oracle.round_to_bf16(h.numpy())))
+    ref = torch.nn.functional.linear(hq, wd).numpy()
+    assert _rel(r["out"], ref) <= 1e-13
+    # quantising the activations changes the result (the path is exercised)
+    plain = oracle.forward(mi.make(mi.Shape(T=6, H=64, E=1, k=1, I=64, mxfp4=True), seed=12))["out"]
+    assert _rel(plain, ref) > 1e-4
+
+
+def test_round_to_bf16_matches_torch():
+    rng = np.random.default_rng(5)
+    v = rng.standard_normal(1000) * np.exp(rng.uniform(-20, 20, 1000))
+    ref = torch.from_numpy(v).to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    assert (oracle.round_to_bf16(v) == ref).all()
