@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/s + % HBM roofline (decode) / % bf16 MFMA peak (prefill)"
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+FP4_PEAK_TFLOPS = 10100.0       # MI355X dense fp4 (MXFP4) MFMA
 STAGES = ["route", "permute", "gateup", "down", "combine"]
 
 
@@ -38,7 +39,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--config", default="decode", help="tiny|decode|prefill|skew|mxfp4|decode_shared")
+    p.add_argument("--config", default="decode", help="tiny|decode|prefill|skew|mxfp4|decode_shared|w4a4")
     p.add_argument("--rotate", type=int, default=4, help="device copies of the weights cycled per step")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle timing")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -157,7 +158,7 @@ def main():
     t_gen = time.perf_counter()
     inp = mi.make(args.config, seed=0)
     s = inp.shape
-    sh = moe.shape(s.T, s.H, s.E, s.k, s.I, mxfp4=s.mxfp4)
+    sh = moe.shape(s.T, s.H, s.E, s.k, s.I, mxfp4=s.mxfp4, a4=s.a4)
     x = dev.to_device(inp.x)
     wr = dev.to_device(inp.w_router)
     bias = dev.to_device(inp.router_bias) if inp.router_bias is not None else None
@@ -243,13 +244,12 @@ def main():
     torch.cuda.synchronize()
     if not torch.equal(r_ids.cpu(), ids.cpu()):
         raise RuntimeError("moe_route and moe_forward disagree on the routing")
-    if s.I_sh:
-        # the shared-MLP tiles run inside the forward's gate/up launch only:
-        # take that launch's duration from the stage events (includes the
-        # gap an event adds)
+    if s.I_sh or s.a4:
+        # the dense-MLP tiles (and the W4A4 GEMMs) run inside moe_forward
+        # only: take the gate/up stage's duration from the stage events
+        # (includes the gap an event adds, and for W4A4 the quantisation of x)
         gateup_launch_us = stage_avg_us["gateup"]
-        print(f"# gate/up launch (experts + dense MLP, stage events): {gateup_launch_us:.1f} us",
-              file=sys.stderr, flush=True)
+        print(f"# gate/up stage (stage events): {gateup_launch_us:.1f} us", file=sys.stderr, flush=True)
     else:
         moe.gemm_gateup(sh, x, sorted_ids, offsets, copies[0][0], gus, h)
         torch.cuda.synchronize()
@@ -304,9 +304,10 @@ def main():
 
     tokens_per_s = s.T / (ms * 1e-3)
     gu_s = gateup_launch_us * 1e-6
-    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    mfma_peak = FP4_PEAK_TFLOPS if s.a4 else BF16_PEAK_TFLOPS   # the expert matmuls' own dtype
+    ridge = mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)
     if alg["gateup_flops"] / alg["gateup_bytes"] > ridge:
-        bound, unit, peak = "mfma", "TFLOP/s", BF16_PEAK_TFLOPS
+        bound, unit, peak = "mfma", "TFLOP/s", mfma_peak
         achieved = alg["gateup_flops"] / gu_s / 1e12
     else:
         bound, unit, peak = "hbm", "GB/s", HBM_PEAK_GBS
@@ -316,7 +317,7 @@ def main():
         "touched_experts": alg["U"],
         "alg_bytes": alg["layer_bytes"], "alg_flops": alg["layer_flops"],
         "hbm_frac": alg["layer_bytes"] / t_layer / (HBM_PEAK_GBS * 1e9),
-        "mfma_frac": alg["layer_flops"] / t_layer / (BF16_PEAK_TFLOPS * 1e12),
+        "mfma_frac": alg["layer_flops"] / t_layer / (mfma_peak * 1e12),
     }
     res = {
         "metric": METRIC,
@@ -329,15 +330,17 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "mxfp4" if s.a4 else "bf16",
         "data": "synthetic",
         "config": {"workload": f"Gemma-4-26B-A4B MoE FFN layer, {args.config}: T={s.T} tokens, "
                                f"hidden {s.H}, {s.E} experts, top-{s.k}, intermediate {s.I}, "
                                f"GEGLU, {'MXFP4' if s.mxfp4 else 'bf16'} expert weights"
+                               f"{' and MXFP4 activations (W4A4)' if s.a4 else ''}"
                                f"{', Zipf(1.2) router bias' if s.skew else ''}"
                                f"{f', plus the dense GEGLU MLP (intermediate {s.I_sh}) as a shared expert' if s.I_sh else ''}",
                    "T": s.T, "H": s.H, "E": s.E, "k": s.k, "I": s.I,
-                   "weights": "mxfp4" if s.mxfp4 else "bf16", "weight_copies": len(copies),
+                   "weights": ("mxfp4 weights and activations (W4A4)" if s.a4 else "mxfp4") if s.mxfp4 else "bf16",
+                   "weight_copies": len(copies),
                    **({"I_shared": s.I_sh} if s.I_sh else {})},
         "roofline": {
             "kernel": "grouped_gemm gate/up + GEGLU",

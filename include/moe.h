@@ -53,7 +53,8 @@
  *     exception crosses this interface.
  *   - Supported sizes: H % 64 == 0, I % 64 == 0, 1 <= k <= min(E, 32),
  *     E <= 1024, T*k < 2^30.  Pointers to bf16 arrays, x_perm, h and y must
- *     be 16-byte aligned, the other arrays 4-byte aligned.
+ *     be 16-byte aligned (W4A4 weight codes too), the other arrays 4-byte
+ *     aligned (MXFP4 scales: any address, 2-byte aligned for W4A4).
  */
 #ifndef MOE_H
 #define MOE_H
@@ -71,10 +72,20 @@ typedef struct moe_shape {
     int32_t E;        /* experts */
     int32_t k;        /* experts per token */
     int32_t I;        /* expert intermediate size */
-    int32_t w_format; /* MOE_W_BF16 or MOE_W_MXFP4 (expert weights only) */
+    int32_t w_format; /* MOE_W_BF16, MOE_W_MXFP4 or MOE_W_MXFP4_A4 */
 } moe_shape;
 
-enum { MOE_W_BF16 = 0, MOE_W_MXFP4 = 1 };
+/* Expert weight format.  MOE_W_MXFP4_A4 (W4A4): MXFP4 weights, and the
+ * expert matmuls' activations -- x, and each expert's bf16 h -- quantised to
+ * MXFP4 per 32 consecutive K values before they are multiplied (OCP MX v1.0
+ * conversion: scale 2^(floor(log2 amax) - 2), clamped exponent, 2^0 for an
+ * all-zero block; values to the nearest E2M1 code, ties to the even code,
+ * saturating at 6), on the gfx950 block-scaled FP4 matrix instructions.
+ * The router still reads the bf16 x.  The vLLM-Ascend Gemma4 tutorial,
+ * section 3.1, names w4a4 MXFP4 checkpoints.  W4A4 runs through moe_forward
+ * (no dense MLP) and moe_quantize_mx only; the per-step GEMM entry points
+ * return MOE_ERR_UNSUPPORTED for it. */
+enum { MOE_W_BF16 = 0, MOE_W_MXFP4 = 1, MOE_W_MXFP4_A4 = 2 };
 
 enum {
     MOE_OK = 0,
@@ -218,6 +229,18 @@ int moe_forward_shared(const moe_shape *s, const uint16_t *x,
                        int32_t *topk_ids_out, float *topk_w_out, void *ws,
                        size_t ws_bytes, moe_stream_t stream,
                        const moe_event_t *stage_events);
+
+/*
+ * moe_quantize_mx -- MXFP4 codes and E8M0 scales of bf16 rows, per 32
+ * consecutive values (the W4A4 activation conversion described with
+ * MOE_W_MXFP4_A4).
+ *   src     [rows][K] bf16, 16-byte aligned; K > 0, K % 32 == 0
+ *   codes   [rows][K/2] out, two codes per byte (even index low), 16-byte aligned
+ *   scales  [rows][K/32] out, E8M0 bytes
+ *   rows >= 0 (0 launches nothing)
+ */
+int moe_quantize_mx(const uint16_t *src, int64_t rows, int32_t K, uint8_t *codes,
+                    uint8_t *scales, moe_stream_t stream);
 
 /* Workspace bytes moe_forward needs for this shape; 0 for an invalid or
  * unsupported shape.  Monotone in T. */

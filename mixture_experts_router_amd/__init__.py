@@ -6,7 +6,7 @@ The layer runs in hand-written HIP kernels behind the C ABI of include/moe.h
 call raises if the library is missing.
 """
 from ._lib import (  # noqa: F401
-    EXPORTS, LIB_PATH, MOE_FORWARD_STAGES, MOE_W_BF16, MOE_W_MXFP4, MoeError, MoeShape,
+    EXPORTS, LIB_PATH, MOE_FORWARD_STAGES, MOE_W_BF16, MOE_W_MXFP4, MOE_W_MXFP4_A4, MoeError, MoeShape,
     combine, forward, forward_shared, gemm_down, gemm_gateup, load, permute, permute_workspace_bytes, route,
-    route_workspace_bytes, shape, workspace_bytes, workspace_shared_bytes,
+    quantize_mx, route_workspace_bytes, shape, workspace_bytes, workspace_shared_bytes,
 )

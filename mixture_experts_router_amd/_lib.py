@@ -9,7 +9,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe.so")
 
-MOE_W_BF16, MOE_W_MXFP4 = 0, 1
+MOE_W_BF16, MOE_W_MXFP4, MOE_W_MXFP4_A4 = 0, 1, 2
 MOE_FORWARD_STAGES = 5
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARGUMENT", -2: "MOE_ERR_UNSUPPORTED",
           -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP"}
@@ -18,7 +18,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARGUMENT", -2: "MOE_ERR_UNSUPPORTED"
 EXPORTS = ("moe_route", "moe_permute", "moe_grouped_gemm_gateup", "moe_grouped_gemm_down",
            "moe_combine", "moe_forward", "moe_forward_shared", "moe_workspace_bytes",
            "moe_workspace_shared_bytes", "moe_route_workspace_bytes", "moe_permute_workspace_bytes",
-           "moe_status_string")
+           "moe_quantize_mx", "moe_status_string")
 
 
 class MoeShape(ctypes.Structure):
@@ -70,6 +70,8 @@ def load(path: str = LIB_PATH):
         f = getattr(lib, name)
         f.argtypes = [_S]
         f.restype = c_size
+    lib.moe_quantize_mx.argtypes = [_P, ctypes.c_int64, ctypes.c_int32, _P, _P, _P]
+    lib.moe_quantize_mx.restype = c_int
     lib.moe_workspace_shared_bytes.argtypes = [_S, ctypes.c_int32]
     lib.moe_workspace_shared_bytes.restype = c_size
     lib.moe_status_string.argtypes = [c_int]
@@ -78,8 +80,9 @@ def load(path: str = LIB_PATH):
     return lib
 
 
-def shape(T, H, E, k, I, mxfp4=False) -> MoeShape:
-    return MoeShape(T, H, E, k, I, MOE_W_MXFP4 if mxfp4 else MOE_W_BF16)
+def shape(T, H, E, k, I, mxfp4=False, a4=False) -> MoeShape:
+    fmt = MOE_W_MXFP4_A4 if a4 else (MOE_W_MXFP4 if mxfp4 else MOE_W_BF16)
+    return MoeShape(T, H, E, k, I, fmt)
 
 
 def _ptr(t):
@@ -183,3 +186,10 @@ def forward_shared(s, x, w_router, router_bias, w_gate_up, gu_scales, w_down, d_
                                   _ptr(gu_scales), _ptr(w_down), _ptr(d_scales), I_sh, _ptr(w_sh_gate_up),
                                   _ptr(sh_gu_scales), _ptr(w_sh_down), _ptr(sh_d_scales), _ptr(out),
                                   _ptr(topk_ids_out), _ptr(topk_w_out), _ptr(ws), nbytes, _stream(stream), ev))
+
+
+def quantize_mx(src, codes, scales, stream=None):
+    """moe_quantize_mx: MXFP4 codes [rows][K/2] and scales [rows][K/32] of bf16 rows src [rows][K]."""
+    lib = load()
+    rows, K = src.shape
+    _check("moe_quantize_mx", lib.moe_quantize_mx(_ptr(src), rows, K, _ptr(codes), _ptr(scales), _stream(stream)))

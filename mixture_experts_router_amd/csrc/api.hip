@@ -19,7 +19,8 @@ int check_shape(const moe_shape *s) {
     if (!s) return MOE_ERR_INVALID_ARGUMENT;
     if (s->T < 1 || s->H < 1 || s->E < 1 || s->k < 1 || s->I < 1) return MOE_ERR_INVALID_ARGUMENT;
     if (s->k > s->E) return MOE_ERR_INVALID_ARGUMENT;
-    if (s->w_format != MOE_W_BF16 && s->w_format != MOE_W_MXFP4) return MOE_ERR_UNSUPPORTED;
+    if (s->w_format != MOE_W_BF16 && s->w_format != MOE_W_MXFP4 && s->w_format != MOE_W_MXFP4_A4)
+        return MOE_ERR_UNSUPPORTED;
     if (s->H % 64 != 0 || s->I % 64 != 0) return MOE_ERR_UNSUPPORTED;
     if (s->E > 1024 || s->k > 32) return MOE_ERR_UNSUPPORTED;
     if ((int64_t)s->T * s->k >= (int64_t{1} << 30)) return MOE_ERR_UNSUPPORTED;
@@ -58,7 +59,10 @@ int check_weights(const moe_shape *s, const void *w, const uint8_t *scales) {
     if (s->w_format == MOE_W_BF16) {
         if (scales || !al16(w)) return MOE_ERR_INVALID_ARGUMENT;
     } else {
-        if (!scales || !al4(w)) return MOE_ERR_INVALID_ARGUMENT;
+        // W4A4 streams the codes with 16-byte loads and the scales in pairs
+        if (!scales || !(s->w_format == MOE_W_MXFP4_A4 ? al16(w) : al4(w))) return MOE_ERR_INVALID_ARGUMENT;
+        if (s->w_format == MOE_W_MXFP4_A4 && (reinterpret_cast<uintptr_t>(scales) & 1u))
+            return MOE_ERR_INVALID_ARGUMENT;
     }
     return MOE_OK;
 }
@@ -71,6 +75,7 @@ struct Workspace {
     float *w;
     int32_t *counts, *offsets, *block_hist, *sorted_ids, *inv;
     uint16_t *h, *y;
+    uint8_t *xq, *xs, *hq, *hs;   // W4A4 only: MXFP4 codes and scales of x and h
     uint16_t *h_sh;          // dense MLP (I_sh > 0 only): h rows [T][I_sh]
     float *y_sh32;           // and its down partial sums [nsplit][T][H]
     size_t bytes;
@@ -98,6 +103,11 @@ Workspace carve(const moe_shape *s, void *base, int I_sh = 0) {
     w.inv = reinterpret_cast<int32_t *>(take(A * sizeof(int32_t)));
     w.h = reinterpret_cast<uint16_t *>(take(A * s->I * sizeof(uint16_t)));
     w.y = reinterpret_cast<uint16_t *>(take(A * s->H * sizeof(uint16_t)));
+    const bool a4 = s->w_format == MOE_W_MXFP4_A4;
+    w.xq = a4 ? reinterpret_cast<uint8_t *>(take(T * (size_t)s->H / 2)) : nullptr;
+    w.xs = a4 ? reinterpret_cast<uint8_t *>(take(T * (size_t)s->H / 32)) : nullptr;
+    w.hq = a4 ? reinterpret_cast<uint8_t *>(take(A * (size_t)s->I / 2)) : nullptr;
+    w.hs = a4 ? reinterpret_cast<uint8_t *>(take(A * (size_t)s->I / 32)) : nullptr;
     w.h_sh = I_sh > 0 ? reinterpret_cast<uint16_t *>(take(T * (size_t)I_sh * sizeof(uint16_t))) : nullptr;
     w.y_sh32 = I_sh > 0 ? reinterpret_cast<float *>(take((size_t)moe::shared_splits(I_sh, s->I) * T * s->H *
                                                           sizeof(float)))
@@ -118,8 +128,9 @@ static int forward_impl(const moe_shape *s, const uint16_t *x, const uint16_t *w
     int st = check_shape(s);
     if (st != MOE_OK) return st;
     if (I_sh < 0) return MOE_ERR_INVALID_ARGUMENT;
+    const bool a4 = s->w_format == MOE_W_MXFP4_A4;
     if (I_sh > 0) {
-        if (I_sh % 64 != 0) return MOE_ERR_UNSUPPORTED;
+        if (a4 || I_sh % 64 != 0) return MOE_ERR_UNSUPPORTED;
         if ((st = check_weights(s, w_sh_gate_up, sh_gu_scales)) != MOE_OK) return st;
         if ((st = check_weights(s, w_sh_down, sh_d_scales)) != MOE_OK) return st;
     }
@@ -162,6 +173,22 @@ static int forward_impl(const moe_shape *s, const uint16_t *x, const uint16_t *w
         st = hip_status(
             moe::launch_permute(ids, w.counts, w.offsets, w.sorted_ids, w.inv, w.block_hist, A, E, hs));
         if (st != MOE_OK || (st = mark()) != MOE_OK) return st;
+    }
+    if (a4) {
+        // W4A4: x and h quantised to MXFP4 before their matmuls (the
+        // quantisations belong to the gate/up and down stages)
+        st = hip_status(moe::launch_quantize_mx(x, T, H, w.xq, w.xs, hs));
+        if (st == MOE_OK)
+            st = hip_status(moe::launch_gateup_a4(w.xq, w.xs, w.sorted_ids, k, w.offsets, w_gate_up, gu_scales, w.h,
+                                                  A, H, E, I, hs));
+        if (st != MOE_OK || (st = mark()) != MOE_OK) return st;
+        st = hip_status(moe::launch_quantize_mx(w.h, A, I, w.hq, w.hs, hs));
+        if (st == MOE_OK)
+            st = hip_status(moe::launch_down_a4(w.hq, w.hs, w.offsets, w_down, d_scales, w.y, A, H, E, I, hs));
+        if (st != MOE_OK || (st = mark()) != MOE_OK) return st;
+        st = hip_status(moe::launch_combine(w.y, w.inv, wts, nullptr, 0, out, T, H, k, hs));
+        if (st != MOE_OK) return st;
+        return mark();
     }
     // the shared expert (if any) is an extra group of the same two launches
     const moe::SharedGroup sh_gu{x, w_sh_gate_up, sh_gu_scales, w.h_sh, nullptr, T, I_sh};
@@ -253,6 +280,7 @@ int moe_grouped_gemm_gateup(const moe_shape *s, const uint16_t *x, const int32_t
     if (!al16(x) || !al16(h) || !al4(offsets)) return MOE_ERR_INVALID_ARGUMENT;
     if (sorted_ids && !al4(sorted_ids)) return MOE_ERR_INVALID_ARGUMENT;
     if ((st = check_weights(s, w_gate_up, gu_scales)) != MOE_OK) return st;
+    if (s->w_format == MOE_W_MXFP4_A4) return MOE_ERR_UNSUPPORTED;
     return hip_status(moe::launch_gateup(x, sorted_ids, s->k, offsets, w_gate_up, gu_scales, h,
                                          s->T * s->k, s->H, s->E, s->I, s->w_format == MOE_W_MXFP4, nullptr,
                                          static_cast<hipStream_t>(stream)));
@@ -265,6 +293,7 @@ int moe_grouped_gemm_down(const moe_shape *s, const uint16_t *h, const int32_t *
     if (!h || !offsets || !y) return MOE_ERR_INVALID_ARGUMENT;
     if (!al16(h) || !al16(y) || !al4(offsets)) return MOE_ERR_INVALID_ARGUMENT;
     if ((st = check_weights(s, w_down, d_scales)) != MOE_OK) return st;
+    if (s->w_format == MOE_W_MXFP4_A4) return MOE_ERR_UNSUPPORTED;
     return hip_status(moe::launch_down(h, offsets, w_down, d_scales, y, s->T * s->k, s->H, s->E, s->I,
                                        s->w_format == MOE_W_MXFP4, nullptr, static_cast<hipStream_t>(stream)));
 }
@@ -296,6 +325,14 @@ int moe_forward_shared(const moe_shape *s, const uint16_t *x, const uint16_t *w_
     return forward_impl(s, x, w_router, router_bias, w_gate_up, gu_scales, w_down, d_scales, I_sh, w_sh_gate_up,
                         sh_gu_scales, w_sh_down, sh_d_scales, out, topk_ids_out, topk_w_out, ws, ws_bytes, stream,
                         stage_events);
+}
+
+int moe_quantize_mx(const uint16_t *src, int64_t rows, int32_t K, uint8_t *codes, uint8_t *scales,
+                    moe_stream_t stream) {
+    if (rows < 0 || K <= 0 || K % 32 != 0) return rows < 0 || K <= 0 ? MOE_ERR_INVALID_ARGUMENT : MOE_ERR_UNSUPPORTED;
+    if (rows == 0) return MOE_OK;
+    if (!src || !codes || !scales || !al16(src) || !al16(codes)) return MOE_ERR_INVALID_ARGUMENT;
+    return hip_status(moe::launch_quantize_mx(src, rows, K, codes, scales, static_cast<hipStream_t>(stream)));
 }
 
 size_t moe_workspace_shared_bytes(const moe_shape *s, int32_t I_sh) {

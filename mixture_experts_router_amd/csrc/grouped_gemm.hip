@@ -69,6 +69,8 @@ struct GemmArgs {
     float *sh_out32;          // [sh_splits][sh_rows][sh_n_out] fp32 partial sums (down)
     int sh_K, sh_I, sh_w_rows, sh_n_out;
     int sh_splits, sh_ksplit; // down: K cut into sh_splits ranges of sh_ksplit (last one shorter)
+    // W4A4: `a` holds MXFP4 codes [rows][K/2] and a_scales [rows][K/32]
+    const uint8_t *a_scales;
 };
 
 // Locate this workgroup's M tile: tile index -> (expert, first row).  Run by
@@ -111,7 +113,7 @@ __device__ __forceinline__ void find_tile(const int32_t *__restrict__ offsets, i
 
 enum GemmMode { kDown = 0, kGateUp = 1, kRouter = 2 };
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int MODE, bool MX, int NS_, int BK_>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int MODE, bool MX, int NS_, int BK_, bool A4_ = false>
 struct GemmTile {
     static constexpr bool GEGLU = MODE == kGateUp;
     static constexpr int BK = BK_;                // K per step (32, 64 or 128)
@@ -148,6 +150,9 @@ struct GemmTile {
     // MXFP4 codes go through registers one step ahead; the wait counts
     // assume at most one DMA step is issued after them.
     static_assert(!MX || NS <= 3, "MXFP4 pipeline depth");
+    // W4A4: both operands are MXFP4 codes loaded like bf16 tiles (128-byte
+    // rows = 256 K values per stage, two 16x16x128 scaled MFMA steps).
+    static_assert(!A4_ || (!MX && BK == 64), "W4A4 tiles: code rows of 128 bytes");
 };
 
 // s_waitcnt with vmcnt = VM and lgkmcnt = 0 (expcnt left at its maximum).
@@ -194,9 +199,9 @@ __device__ __forceinline__ void dma16(const void *g, const void *lds) {
         asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(l) : "memory", "m0");
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int MODE, bool MX, int NS_, int BK_>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int MODE, bool MX, int NS_, int BK_, bool A4 = false>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(GemmArgs p) {
-    using G = GemmTile<BM, BN, WAVES_M, WAVES_N, MODE, MX, NS_, BK_>;
+    using G = GemmTile<BM, BN, WAVES_M, WAVES_N, MODE, MX, NS_, BK_, A4>;
     constexpr bool GEGLU = MODE == kGateUp, ROUTER = MODE == kRouter;
     constexpr int BK = G::BK, NS = G::NS, WTM = G::WTM, WN = G::WN, MI = G::MI, NI = G::NI;
     constexpr int CH = G::CH, RPD = G::RPD, KK = G::KK;
@@ -274,7 +279,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
     }
     const int K = shared ? p.sh_K : p.K;                 // row length of both operands
     const int kb = shared ? split * p.sh_ksplit : 0;     // this tile's K range [kb, kb + KT*BK)
-    const int KT = (shared && p.sh_splits > 1 ? min(p.sh_ksplit, K - kb) : K) / BK;
+    // W4A4 rows hold K/2 bytes of codes (K/4 16-bit units) and a stage holds
+    // 256 K values; a last stage that runs past the row is masked (below).
+    const int rowu = A4 ? K / 4 : K;                     // row length in 16-bit units
+    const int KT = A4 ? (K + 255) / 256 : (shared && p.sh_splits > 1 ? min(p.sh_ksplit, K - kb) : K) / BK;
 
     // Weight row of tile row v (0 <= v < BN), clamped to a valid row.
     auto weight_row = [&](int v) -> int {
@@ -301,7 +309,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
         const int row = RPD * (g < NA ? g : 0) + lr;
         const int rr = row < rows ? row : 0;
         const size_t src = g_gather ? (size_t)(g_gather[seg + rr] / p.gather_k) : (size_t)(seg + rr);
-        a_src[q] = g_a + src * K + kb + 8 * tswz<BK>(row, lc);
+        a_src[q] = g_a + src * rowu + kb + (A4 ? 0 : 8 * tswz<BK>(row, lc));
     }
     const uint16_t *b_src[B_W > 0 ? B_W : 1];
 #pragma unroll
@@ -309,8 +317,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
         const int g = q * NW + wave;
         const int row = RPD * (g < NB ? g : 0) + lr;
         const size_t rid = (size_t)e * g_w_rows + weight_row(row);
-        b_src[q] = reinterpret_cast<const uint16_t *>(g_w) + rid * K + kb + 8 * tswz<BK>(row, lc);
+        b_src[q] = reinterpret_cast<const uint16_t *>(g_w) + rid * rowu + kb + (A4 ? 0 : 8 * tswz<BK>(row, lc));
     }
+    // W4A4: the lane's 16-byte chunk within a stage (the same for every load
+    // group: a group covers 8 rows, so row & 7 == lr), clamped into the row
+    // for the last, partial stage.
+    const int lane_col = 8 * tswz<BK>(lr, lc);
+    auto col_of = [&](int kt) -> int {
+        if (!A4) return kt * BK;
+        return min(kt * BK + lane_col, rowu - 8);
+    };
     // Token-row groups past the tile's last valid row are not loaded (their
     // LDS rows keep stale data that only reaches outputs never stored).
     const int na_valid = (rows + RPD - 1) / RPD;
@@ -320,7 +336,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
         for (int q = 0; q < A_W; ++q) {
             const int g = q * NW + wave;
             if (g < na_valid)
-                dma16<false>(a_src[q] + kt * BK, As[slot] + g * 512);
+                dma16<false>(a_src[q] + col_of(kt), As[slot] + g * 512);
         }
 #pragma unroll
         for (int q = 0; q < B_W; ++q) {
@@ -329,9 +345,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
                 // Weights of an expert with one row tile are read once: stream
                 // them past the caches.  Several row tiles re-read them: keep.
                 if (stream)
-                    dma16<true>(b_src[q] + kt * BK, Bs[slot] + g * 512);
+                    dma16<true>(b_src[q] + col_of(kt), Bs[slot] + g * 512);
                 else
-                    dma16<false>(b_src[q] + kt * BK, Bs[slot] + g * 512);
+                    dma16<false>(b_src[q] + col_of(kt), Bs[slot] + g * 512);
             }
         }
     };
@@ -384,6 +400,38 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
 
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
     const int lrow = lane & 15, lk = lane >> 4;
+
+    // ---- W4A4 block scales through registers, one step ahead.  W4A4
+    // fragments take the stage's 16-byte chunks in the order ch = 2 lk + kk
+    // (any order serves if both operands use it), so a lane's two blocks of
+    // a step, 8 kt + 2 lk and 8 kt + 2 lk + 1, are adjacent: one 16-bit load
+    // per row and step (bytes 0, 1 for kk = 0, 1).
+    const int nblk = K / 32;
+    const uint8_t *ws_row[A4 ? NI : 1];
+    const uint8_t *xs_row[A4 ? MI : 1];
+    uint32_t sw_c[A4 ? NI : 1], sx_c[A4 ? MI : 1], sw_n[A4 ? NI : 1], sx_n[A4 ? MI : 1];
+    if (A4) {
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+            ws_row[j] = g_scales + ((size_t)e * g_w_rows + weight_row(wn * WN + j * 16 + lrow)) * nblk;
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+            const int v = wm * WTM + i * 16 + lrow;
+            const int rr = v < rows ? v : 0;
+            const size_t src = g_gather ? (size_t)(g_gather[seg + rr] / p.gather_k) : (size_t)(seg + rr);
+            xs_row[i] = p.a_scales + src * nblk;
+        }
+    }
+    auto load_scales = [&](int kt, uint32_t *sw, uint32_t *sx) {
+        // blocks past the row (last, partial stage) re-read its last pair;
+        // they only scale zeros
+        const int b = min(8 * kt + 2 * lk, nblk - 2);   // even: nblk = K/32 is even (K % 64 == 0)
+#pragma unroll
+        for (int j = 0; j < NI; ++j) sw[j] = *reinterpret_cast<const uint16_t *>(ws_row[j] + b);
+#pragma unroll
+        for (int i = 0; i < MI; ++i) sx[i] = *reinterpret_cast<const uint16_t *>(xs_row[i] + b);
+    };
+
     f32x4 acc[NI][MI];
 #pragma unroll
     for (int j = 0; j < NI; ++j)
@@ -420,7 +468,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
         // Per MFMA K step of 32: the fragments, then the MFMAs.
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-            const int ch = kk * 4 + lk;
+            const int ch = A4 ? 2 * lk + kk : kk * 4 + lk;
             u32x4 wf[NI], xf[MI];
 #pragma unroll
             for (int j = 0; j < NI; ++j) {
@@ -443,10 +491,27 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
                 const int r = wm * WTM + i * 16 + lrow;
                 xf[i] = *reinterpret_cast<const u32x4 *>(&As[slot][r * BK + tswz<BK>(r, ch) * 8]);
             }
+            if constexpr (A4) {
+                // 32 codes (16 bytes) of the lane's row and block; blocks past
+                // K (last stage) multiply as zeros
+                if (kt * 256 + ch * 32 >= K) {
 #pragma unroll
-            for (int i = 0; i < MI; ++i)
+                    for (int j = 0; j < NI; ++j) wf[j] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-                for (int j = 0; j < NI; ++j) acc[j][i] = mfma16x16x32(wf[j], xf[i], acc[j][i]);
+                    for (int i = 0; i < MI; ++i) xf[i] = u32x4{0u, 0u, 0u, 0u};
+                }
+#pragma unroll
+                for (int i = 0; i < MI; ++i)
+#pragma unroll
+                    for (int j = 0; j < NI; ++j)
+                        acc[j][i] = mfma_fp4x128(wf[j], xf[i], acc[j][i], (sw_c[j] >> (8 * kk)) & 0xFFu,
+                                                 (sx_c[i] >> (8 * kk)) & 0xFFu);
+            } else {
+#pragma unroll
+                for (int i = 0; i < MI; ++i)
+#pragma unroll
+                    for (int j = 0; j < NI; ++j) acc[j][i] = mfma16x16x32(wf[j], xf[i], acc[j][i]);
+            }
         }
     };
 
@@ -467,6 +532,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
         wait_vm_lgkm0_rt(later * dma_per_step);
     };
     if (MX) issue_mx(0);
+    if (A4) load_scales(0, sw_n, sx_n);
 #pragma unroll
     for (int s0 = 0; s0 < NS - 1; ++s0)
         if (s0 < KT) issue_dma(s0);
@@ -482,6 +548,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
             }
             __builtin_amdgcn_s_barrier();
             if (MX && kt + 1 < KT) issue_mx(kt + 1);
+            if (A4) {
+#pragma unroll
+                for (int j = 0; j < NI; ++j) sw_c[j] = sw_n[j];
+#pragma unroll
+                for (int i = 0; i < MI; ++i) sx_c[i] = sx_n[i];
+                if (kt + 1 < KT) load_scales(kt + 1, sw_n, sx_n);   // before the DMA: in-order counts
+            }
             if (kt + NS - 1 < KT) issue_dma(kt + NS - 1);
             if (MUL) {
                 compute(kt);
@@ -553,7 +626,7 @@ static int mtile_slots(int A, int E, int BM) {
     return (int)(((long long)A + (long long)(BM - 1) * ne) / BM);
 }
 
-template <int BM, int BN, int WM, int WN, int MODE, bool MX, int NS, int BK>
+template <int BM, int BN, int WM, int WN, int MODE, bool MX, int NS, int BK, bool A4 = false>
 static hipError_t launch_cfg(GemmArgs a, int A, hipStream_t st) {
     constexpr bool GEGLU = MODE == kGateUp;
     const int ncols = GEGLU ? a.I : a.n_out;
@@ -570,14 +643,15 @@ static hipError_t launch_cfg(GemmArgs a, int A, hipStream_t st) {
     long long blocks = (long long)a.n_tiles * ((slots + 7) / 8 * 8);
     a.routed_blocks = (int)blocks;
     // every group's K must be whole steps (the kernel loops K / BK times)
-    if (a.K % BK != 0 || (MODE != kRouter && a.sh_rows > 0 && (a.sh_K % BK != 0 || a.sh_ksplit % BK != 0)))
+    if (A4 ? (a.K % 64 != 0 || a.sh_rows > 0)
+           : (a.K % BK != 0 || (MODE != kRouter && a.sh_rows > 0 && (a.sh_K % BK != 0 || a.sh_ksplit % BK != 0))))
         return hipErrorInvalidValue;
     if (MODE != kRouter && a.sh_rows > 0) {
         a.sh_n_tiles = GEGLU ? (a.sh_I + BN / 2 - 1) / (BN / 2) : (a.sh_n_out + BN - 1) / BN;
         blocks += (long long)a.sh_n_tiles * ((a.sh_rows + BM - 1) / BM) * max(1, a.sh_splits);
     }
     if (blocks == 0) return hipSuccess;
-    grouped_gemm_kernel<BM, BN, WM, WN, MODE, MX, NS, BK><<<dim3((unsigned)blocks), 64 * WM * WN, 0, st>>>(a);
+    grouped_gemm_kernel<BM, BN, WM, WN, MODE, MX, NS, BK, A4><<<dim3((unsigned)blocks), 64 * WM * WN, 0, st>>>(a);
     return hipGetLastError();
 }
 
@@ -604,6 +678,33 @@ static hipError_t launch_sized(const GemmArgs &a, int A, hipStream_t st) {
     if (mean_rows <= 40) return launch_cfg<32, 128, 2, 2, MODE, MX, 2, 64>(a, A, st);
     if (mean_rows <= 80) return launch_cfg<64, 128, 2, 2, MODE, MX, 2, 64>(a, A, st);
     return launch_cfg<256, 256, 4, 2, MODE, MX, MX ? 3 : 2, 64>(a, A, st);
+}
+
+// W4A4: the same tile choice as bf16 activations, K steps of 256 codes.
+template <int MODE>
+static hipError_t launch_sized_a4(const GemmArgs &a, int A, hipStream_t st) {
+    const int mean_rows = A / a.E;
+    if (mean_rows <= 16) return launch_cfg<16, 128, 1, 4, MODE, false, 2, 64, true>(a, A, st);
+    if (mean_rows <= 40) return launch_cfg<32, 128, 2, 2, MODE, false, 2, 64, true>(a, A, st);
+    if (mean_rows <= 80) return launch_cfg<64, 128, 2, 2, MODE, false, 2, 64, true>(a, A, st);
+    return launch_cfg<256, 256, 4, 2, MODE, false, 2, 64, true>(a, A, st);
+}
+
+hipError_t launch_gateup_a4(const uint8_t *xq, const uint8_t *xs, const int32_t *sorted_ids, int k,
+                            const int32_t *offsets, const void *w, const uint8_t *scales, uint16_t *h, int A, int H,
+                            int E, int I, hipStream_t st) {
+    GemmArgs a{reinterpret_cast<const uint16_t *>(xq), sorted_ids, k, offsets, w, scales, h, E, H, I, I, 2 * I,
+               0, 0, 0, nullptr, nullptr};
+    a.a_scales = xs;
+    return launch_sized_a4<kGateUp>(a, A, st);
+}
+
+hipError_t launch_down_a4(const uint8_t *hq, const uint8_t *hs, const int32_t *offsets, const void *w,
+                          const uint8_t *scales, uint16_t *y, int A, int H, int E, int I, hipStream_t st) {
+    GemmArgs a{reinterpret_cast<const uint16_t *>(hq), nullptr, 1, offsets, w, scales, y, E, I, H, I, H, 0, 0, 0,
+               nullptr, nullptr};
+    a.a_scales = hs;
+    return launch_sized_a4<kDown>(a, A, st);
 }
 
 hipError_t launch_gateup(const uint16_t *x, const int32_t *sorted_ids, int k, const int32_t *offsets,

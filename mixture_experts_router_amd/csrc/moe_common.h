@@ -50,6 +50,19 @@ __device__ __forceinline__ int tswz(int row, int chunk) {
     else return chunk ^ ((row >> 1) & 3);
 }
 
+// 16x16x128 MFMA on MXFP4 (E2M1) operands with per-lane E8M0 block scales,
+// fp32 accumulation.  Lane l supplies row l % 16 and K values 32*(l/16) ..
+// +31 as 16 bytes of codes (two per byte, the even K index in the low
+// nibble) plus that block's scale byte; the result layout is that of
+// mfma16x16x32 (checked on gfx950 against a plain host loop).
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x4 mfma_fp4x128(const u32x4 &a, const u32x4 &b, f32x4 c, uint32_t scale_a,
+                                              uint32_t scale_b) {
+    const i32x8 a8 = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+    const i32x8 b8 = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, c, 4, 4, 0, (int)scale_a, 0, (int)scale_b);
+}
+
 // 16x16x32 bf16 MFMA with fp32 accumulation.  Operand layout per lane l:
 // A row (l % 16), k = 8*(l/16) .. +7; B column (l % 16), same k range;
 // result rows 4*(l/16) + r (r = 0..3), column l % 16.

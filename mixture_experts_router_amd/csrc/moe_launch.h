@@ -67,6 +67,16 @@ hipError_t launch_gateup(const uint16_t *x, const int32_t *sorted_ids, int k, co
                          bool mx, const SharedGroup *sh, hipStream_t st);
 hipError_t launch_down(const uint16_t *h, const int32_t *offsets, const void *w, const uint8_t *scales,
                        uint16_t *y, int A, int H, int E, int I, bool mx, const SharedGroup *sh, hipStream_t st);
+// W4A4 grouped GEMMs: activations as MXFP4 codes [rows][K/2] + E8M0 scales
+// [rows][K/32] (launch_quantize_mx), weights MXFP4; K a multiple of 64.
+hipError_t launch_gateup_a4(const uint8_t *xq, const uint8_t *xs, const int32_t *sorted_ids, int k,
+                            const int32_t *offsets, const void *w, const uint8_t *scales, uint16_t *h, int A, int H,
+                            int E, int I, hipStream_t st);
+hipError_t launch_down_a4(const uint8_t *hq, const uint8_t *hs, const int32_t *offsets, const void *w,
+                          const uint8_t *scales, uint16_t *y, int A, int H, int E, int I, hipStream_t st);
+// MXFP4 codes and scales of bf16 rows [rows][K], K a multiple of 32.
+hipError_t launch_quantize_mx(const uint16_t *src, long long rows, int K, uint8_t *codes, uint8_t *scales,
+                              hipStream_t st);
 // y_sh32 (optional, [nsplit][T][H] fp32): partial sums of a shared-expert
 // output, added (in order) with weight 1 before the routed rows.
 hipError_t launch_combine(const uint16_t *y, const int32_t *inv, const float *w, const float *y_sh32, int nsplit,

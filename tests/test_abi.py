@@ -50,7 +50,7 @@ def S(T=16, H=256, E=8, k=2, I=128, f=0):
 
 @pytest.mark.parametrize("s,expect", [
     (S(T=0), -1), (S(H=0), -1), (S(E=0), -1), (S(k=0), -1), (S(I=0), -1), (S(k=9), -1),
-    (S(H=96), -2), (S(I=100), -2), (S(E=2000, k=8), -2), (S(E=64, k=33), -2), (S(f=2), -2),
+    (S(H=96), -2), (S(I=100), -2), (S(E=2000, k=8), -2), (S(E=64, k=33), -2), (S(f=3), -2),
     (S(T=1 << 28, k=8), -2),
 ])
 def test_bad_shapes_rejected_everywhere(lib, s, expect):
@@ -159,3 +159,24 @@ def test_shared_workspace_sizes(lib):
     assert lib.moe_workspace_shared_bytes(ctypes.byref(s), 0) == 0
     assert lib.moe_workspace_shared_bytes(ctypes.byref(s), 100) == 0
     assert lib.moe_workspace_shared_bytes(ctypes.byref(S(T=0)), 128) == 0
+
+
+def test_w4a4_argument_checks(lib):
+    s = S(f=2)
+    b = ctypes.byref(s)
+    F = FAKE
+    # the per-step GEMM entry points do not take W4A4
+    assert lib.moe_grouped_gemm_gateup(b, F, F, F, F, F, F, None) == -2
+    assert lib.moe_grouped_gemm_down(b, F, F, F, F, F, None) == -2
+    # W4A4 weight codes must be 16-byte aligned (plain MXFP4 needs 4)
+    big = 1 << 40
+    assert lib.moe_forward(b, F, F, None, F + 4, F, F, F, F, None, None, F, big, None, None) == -1
+    # no dense MLP with W4A4
+    assert lib.moe_forward_shared(b, F, F, None, F, F, F, F, 128, F, F, F, F, F, None, None, F, big, None,
+                                  None) == -2
+    # quantiser: K a positive multiple of 32, aligned pointers
+    assert lib.moe_quantize_mx(F, 4, 48, F, F, None) == -2
+    assert lib.moe_quantize_mx(F, 4, 0, F, F, None) == -1
+    assert lib.moe_quantize_mx(F, -1, 64, F, F, None) == -1
+    assert lib.moe_quantize_mx(MIS, 4, 64, F, F, None) == -1
+    assert lib.moe_quantize_mx(None, 0, 64, None, None, None) == 0     # nothing to do
