@@ -751,10 +751,13 @@ hipError_t launch_down(const uint16_t *h, const int32_t *offsets, const void *w,
 }
 
 // Router for many tokens: x [T][H] times W_r [E][H]^T as one dense group, 16
-// tokens x 64 experts per workgroup, six stages (five steps in flight).
+// tokens x 64 experts per workgroup; K steps of 128 where H allows (half
+// the steps of a latency-bound loop: measured 23 -> 18.5 us at 2048 tokens),
+// four stages.
 hipError_t launch_router_dense(const uint16_t *x, const uint16_t *wr, const float *bias, float *logits,
                                int T, int H, int E, hipStream_t st) {
     GemmArgs a{x, nullptr, 1, nullptr, wr, nullptr, nullptr, 1, H, E, 0, E, 0, 0, T, logits, bias};
+    if (H % 128 == 0) return launch_cfg<16, 64, 1, 4, kRouter, false, 4, 128>(a, T, st);
     return launch_cfg<16, 64, 1, 4, kRouter, false, 6, 64>(a, T, st);
 }
 
