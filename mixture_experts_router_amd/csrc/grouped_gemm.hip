@@ -153,6 +153,16 @@ struct GemmTile {
     // W4A4: both operands are MXFP4 codes loaded like bf16 tiles (128-byte
     // rows = 256 K values per stage, two 16x16x128 scaled MFMA steps).
     static_assert(!A4_ || (!MX && BK == 64), "W4A4 tiles: code rows of 128 bytes");
+    // W4A4 block scales of a stage: 8 bytes (blocks 8 kt .. 8 kt + 7) per
+    // weight row and per token row, one row per thread.
+    static constexpr bool SC_PAIR_M = MI >= 2;   // token rows paired like weight rows
+    static constexpr int SC_W = ((BN + 31) / 32) * 32 * 8;
+    static constexpr int SC_BYTES = SC_W + (SC_PAIR_M ? ((BM + 31) / 32) * 32 : BM) * 8;
+    static_assert(!A4_ || BN + BM <= NT, "W4A4: one scale row per thread");
+    // the scale stores wait for all of the wave's loads (the compiler cannot
+    // count the direct-to-LDS ones), which only a two-stage pipeline affords
+    static_assert(!A4_ || NS == 2, "W4A4: two stages");
+    static_assert(!A4_ || (NI % 2 == 0 && (!SC_PAIR_M || MI % 2 == 0)), "W4A4: scale rows in pairs");
 };
 
 // s_waitcnt with vmcnt = VM and lgkmcnt = 0 (expcnt left at its maximum).
@@ -212,6 +222,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
     __shared__ __attribute__((aligned(1024))) uint16_t As[NS][G::A_LDS];
     __shared__ __attribute__((aligned(1024))) uint16_t Bs[NS][G::B_LDS];
     __shared__ __attribute__((aligned(16))) uint8_t Ss[NS][MX ? 2 * BN : 1];
+    __shared__ __attribute__((aligned(16))) uint8_t Sc[NS][A4 ? G::SC_BYTES : 1];
     __shared__ int s_info[4];
 
     // XCD-aware tile order.  Workgroups go to the 8 XCDs round-robin (block
@@ -352,6 +363,26 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
         }
     };
 
+    // W4A4, last stage of a row whose length is not a multiple of 256: each
+    // lane zeroes the chunk it loaded if that chunk lies past the row's end
+    // (it holds a clamped re-read), so those blocks multiply as zeros.  Runs
+    // after the wave's own loads of the stage have landed.
+    auto zero_tail = [&](int kt) {
+        if (kt * 256 + 4 * lane_col < K) return;
+        const int slot = kt % NS;
+#pragma unroll
+        for (int q = 0; q < A_W; ++q) {
+            const int g = q * NW + wave;
+            if (g < na_valid) *reinterpret_cast<u32x4 *>(As[slot] + g * 512 + lane * 8) = u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int q = 0; q < B_W; ++q) {
+            const int g = q * NW + wave;
+            if (NB % NW == 0 || g < NB)
+                *reinterpret_cast<u32x4 *>(Bs[slot] + g * 512 + lane * 8) = u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+
     // ---- MXFP4 weights through registers (one set: committed, then reloaded).
     const char *mb_src[G::MB_PER];
     const uint8_t *ms_src[G::MS_PER];
@@ -401,35 +432,65 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
     const int lrow = lane & 15, lk = lane >> 4;
 
-    // ---- W4A4 block scales through registers, one step ahead.  W4A4
-    // fragments take the stage's 16-byte chunks in the order ch = 2 lk + kk
-    // (any order serves if both operands use it), so a lane's two blocks of
-    // a step, 8 kt + 2 lk and 8 kt + 2 lk + 1, are adjacent: one 16-bit load
-    // per row and step (bytes 0, 1 for kk = 0, 1).
+    // ---- W4A4 block scales, staged through LDS one step ahead.  Fragments
+    // take a stage's 16-byte chunks in the order ch = 2 lk + kk (any order
+    // serves if both operands use it), so a lane's two blocks of a step,
+    // 8 kt + 2 lk + kk (kk = 0, 1), are adjacent.  Each thread loads the 8
+    // scale bytes of one tile row per step (weight rows first, then token
+    // rows) and stores them so that one 32-bit LDS read gives a lane the
+    // scales of rows r and r + 16 (bytes 0, 1 and 2, 3; rows in groups of 32
+    // aligned to the wave's first row); the MFMA picks its byte itself.  A
+    // wave with a single 16-row token tile reads its 16 bits alone.
     const int nblk = K / 32;
-    const uint8_t *ws_row[A4 ? NI : 1];
-    const uint8_t *xs_row[A4 ? MI : 1];
-    uint32_t sw_c[A4 ? NI : 1], sx_c[A4 ? MI : 1], sw_n[A4 ? NI : 1], sx_n[A4 ? MI : 1];
+    const uint8_t *sc_src = nullptr;   // this thread's scale row
+    int sc_dst = -1;                   // its LDS byte offset (blocks 0, 1 of lane block 0)
+    bool sc_pair = true;
     if (A4) {
-#pragma unroll
-        for (int j = 0; j < NI; ++j)
-            ws_row[j] = g_scales + ((size_t)e * g_w_rows + weight_row(wn * WN + j * 16 + lrow)) * nblk;
-#pragma unroll
-        for (int i = 0; i < MI; ++i) {
-            const int v = wm * WTM + i * 16 + lrow;
+        if (tid < BN) {
+            sc_src = g_scales + ((size_t)e * g_w_rows + weight_row(tid)) * nblk;
+            sc_dst = ((tid >> 5) * 16 + (tid & 15)) * 16 + ((tid >> 4) & 1) * 2;
+        } else if (tid < BN + BM) {
+            const int v = tid - BN;
             const int rr = v < rows ? v : 0;
             const size_t src = g_gather ? (size_t)(g_gather[seg + rr] / p.gather_k) : (size_t)(seg + rr);
-            xs_row[i] = p.a_scales + src * nblk;
+            sc_src = p.a_scales + src * nblk;
+            sc_pair = G::SC_PAIR_M;
+            sc_dst = G::SC_W + (G::SC_PAIR_M ? ((v >> 5) * 16 + (v & 15)) * 16 + ((v >> 4) & 1) * 2 : v * 8);
         }
     }
-    auto load_scales = [&](int kt, uint32_t *sw, uint32_t *sx) {
+    uint32_t sc_v[2];   // the step's 8 bytes, in flight between load and store
+    auto load_scales = [&](int kt) {
+        if (sc_dst < 0) return;
         // blocks past the row (last, partial stage) re-read its last pair;
-        // they only scale zeros
-        const int b = min(8 * kt + 2 * lk, nblk - 2);   // even: nblk = K/32 is even (K % 64 == 0)
+        // they only scale zeros.  nblk = K/32 is even (K % 64 == 0).
+        uint32_t h[4];
 #pragma unroll
-        for (int j = 0; j < NI; ++j) sw[j] = *reinterpret_cast<const uint16_t *>(ws_row[j] + b);
+        for (int m = 0; m < 4; ++m)
+            h[m] = *reinterpret_cast<const uint16_t *>(sc_src + min(8 * kt + 2 * m, nblk - 2));
+        sc_v[0] = h[0] | (h[1] << 16);
+        sc_v[1] = h[2] | (h[3] << 16);
+    };
+    auto store_scales = [&](int kt) {
+        if (sc_dst < 0) return;
+        uint8_t *d = Sc[kt % NS] + sc_dst;
+        if (sc_pair) {   // lane block m at bytes 4 m, 4 m + 1 of the pair word
 #pragma unroll
-        for (int i = 0; i < MI; ++i) sx[i] = *reinterpret_cast<const uint16_t *>(xs_row[i] + b);
+            for (int m = 0; m < 4; ++m)
+                *reinterpret_cast<uint16_t *>(d + 4 * m) = (uint16_t)(sc_v[m >> 1] >> (16 * (m & 1)));
+        } else {
+            *reinterpret_cast<uint2 *>(d) = make_uint2(sc_v[0], sc_v[1]);
+        }
+    };
+    // a lane's scale words of weight pair q and token pair q (token tile q
+    // alone when unpaired)
+    auto read_sw = [&](int slot, int q) -> uint32_t {
+        return *reinterpret_cast<const uint32_t *>(Sc[slot] + (((wn * WN) >> 5) + q) * 256 + lrow * 16 + lk * 4);
+    };
+    auto read_sx = [&](int slot, int q) -> uint32_t {
+        if (G::SC_PAIR_M)
+            return *reinterpret_cast<const uint32_t *>(Sc[slot] + G::SC_W + (((wm * WTM) >> 5) + q) * 256 +
+                                                       lrow * 16 + lk * 4);
+        return *reinterpret_cast<const uint16_t *>(Sc[slot] + G::SC_W + (wm * WTM + lrow) * 8 + lk * 2);
     };
 
     f32x4 acc[NI][MI];
@@ -465,6 +526,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
     const bool wave_has_rows = wm * WTM < rows;   // scalar condition
     auto compute = [&](int kt) {
         const int slot = kt % NS;
+        constexpr int NSW = A4 ? NI / 2 : 1, NSX = A4 ? (G::SC_PAIR_M ? MI / 2 : MI) : 1;
+        uint32_t sw[NSW], sx[NSX];
+        if (A4) {
+#pragma unroll
+            for (int q = 0; q < NSW; ++q) sw[q] = read_sw(slot, q);
+#pragma unroll
+            for (int q = 0; q < NSX; ++q) sx[q] = read_sx(slot, q);
+        }
         // Per MFMA K step of 32: the fragments, then the MFMAs.
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
@@ -492,20 +561,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
                 xf[i] = *reinterpret_cast<const u32x4 *>(&As[slot][r * BK + tswz<BK>(r, ch) * 8]);
             }
             if constexpr (A4) {
-                // 32 codes (16 bytes) of the lane's row and block; blocks past
-                // K (last stage) multiply as zeros
-                if (kt * 256 + ch * 32 >= K) {
-#pragma unroll
-                    for (int j = 0; j < NI; ++j) wf[j] = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-                    for (int i = 0; i < MI; ++i) xf[i] = u32x4{0u, 0u, 0u, 0u};
-                }
 #pragma unroll
                 for (int i = 0; i < MI; ++i)
 #pragma unroll
                     for (int j = 0; j < NI; ++j)
-                        acc[j][i] = mfma_fp4x128(wf[j], xf[i], acc[j][i], (sw_c[j] >> (8 * kk)) & 0xFFu,
-                                                 (sx_c[i] >> (8 * kk)) & 0xFFu);
+                        acc[j][i] = mfma_fp4x128(wf[j], xf[i], acc[j][i], sw[j / 2], sx[G::SC_PAIR_M ? i / 2 : i],
+                                                 2 * (j & 1) + kk, (G::SC_PAIR_M ? 2 * (i & 1) : 0) + kk);
             } else {
 #pragma unroll
                 for (int i = 0; i < MI; ++i)
@@ -532,7 +593,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
         wait_vm_lgkm0_rt(later * dma_per_step);
     };
     if (MX) issue_mx(0);
-    if (A4) load_scales(0, sw_n, sx_n);
+    if (A4) {
+        load_scales(0);
+        store_scales(0);   // published by the first step's barrier
+    }
 #pragma unroll
     for (int s0 = 0; s0 < NS - 1; ++s0)
         if (s0 < KT) issue_dma(s0);
@@ -542,23 +606,30 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
         constexpr bool MUL = decltype(mul_c)::value;
         for (int kt = 0; kt < KT; ++kt) {
             wait_for(kt);
+            if (A4 && kt == KT - 1 && (K & 255)) {
+                zero_tail(kt);
+                wait_vm_lgkm0<63>();      // the zeroes are in LDS
+            }
             if (MX) {
                 commit_mx(kt);
                 wait_vm_lgkm0<63>();      // this wave's LDS writes are done
             }
             __builtin_amdgcn_s_barrier();
             if (MX && kt + 1 < KT) issue_mx(kt + 1);
-            if (A4) {
-#pragma unroll
-                for (int j = 0; j < NI; ++j) sw_c[j] = sw_n[j];
-#pragma unroll
-                for (int i = 0; i < MI; ++i) sx_c[i] = sx_n[i];
-                if (kt + 1 < KT) load_scales(kt + 1, sw_n, sx_n);   // before the DMA: in-order counts
-            }
+            // scales of step kt + 1: loaded before the DMA (so in-order
+            // counts cover them), stored after this step's MFMAs are issued
+            const bool next_sc = A4 && kt + 1 < KT;
+            if (next_sc) load_scales(kt + 1);
             if (kt + NS - 1 < KT) issue_dma(kt + NS - 1);
             if (MUL) {
                 compute(kt);
                 if (ROUTER && ((kt % (256 / BK)) == 256 / BK - 1 || kt == KT - 1)) flush();
+            }
+            if (next_sc) {
+                // keep the store (and the wait for its loads that comes with
+                // it) behind the MFMAs
+                __builtin_amdgcn_sched_barrier(0);
+                store_scales(kt + 1);
             }
         }
     };

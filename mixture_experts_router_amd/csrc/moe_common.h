@@ -56,11 +56,30 @@ __device__ __forceinline__ int tswz(int row, int chunk) {
 // nibble) plus that block's scale byte; the result layout is that of
 // mfma16x16x32 (checked on gfx950 against a plain host loop).
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+// The scale bytes are byte SA of scale_a and byte SB of scale_b (the
+// instruction's own byte select, so a register can hold four scales).
+template <int SA, int SB>
 __device__ __forceinline__ f32x4 mfma_fp4x128(const u32x4 &a, const u32x4 &b, f32x4 c, uint32_t scale_a,
                                               uint32_t scale_b) {
     const i32x8 a8 = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
     const i32x8 b8 = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0};
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, c, 4, 4, 0, (int)scale_a, 0, (int)scale_b);
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, c, 4, 4, SA, (int)scale_a, SB, (int)scale_b);
+}
+
+// The same with the byte selects as arguments; in unrolled loops they are
+// constants and the switch folds away.
+__device__ __forceinline__ f32x4 mfma_fp4x128(const u32x4 &a, const u32x4 &b, f32x4 c, uint32_t scale_a,
+                                              uint32_t scale_b, int sa, int sb) {
+#define MOE_FP4_CASE(x, y) \
+    case 4 * x + y: return mfma_fp4x128<x, y>(a, b, c, scale_a, scale_b);
+    switch (4 * sa + sb) {
+        MOE_FP4_CASE(0, 0) MOE_FP4_CASE(0, 1) MOE_FP4_CASE(0, 2) MOE_FP4_CASE(0, 3)
+        MOE_FP4_CASE(1, 0) MOE_FP4_CASE(1, 1) MOE_FP4_CASE(1, 2) MOE_FP4_CASE(1, 3)
+        MOE_FP4_CASE(2, 0) MOE_FP4_CASE(2, 1) MOE_FP4_CASE(2, 2) MOE_FP4_CASE(2, 3)
+        MOE_FP4_CASE(3, 0) MOE_FP4_CASE(3, 1) MOE_FP4_CASE(3, 2)
+        default: return mfma_fp4x128<3, 3>(a, b, c, scale_a, scale_b);
+    }
+#undef MOE_FP4_CASE
 }
 
 // 16x16x32 bf16 MFMA with fp32 accumulation.  Operand layout per lane l:
