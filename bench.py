@@ -39,7 +39,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--config", default="decode", help="tiny|decode|prefill|skew|mxfp4|decode_shared|w4a4")
+    p.add_argument("--config", default="decode", help="tiny|decode|prefill|skew|mxfp4|decode_shared|w4a4|nvfp4_decode")
     p.add_argument("--rotate", type=int, default=4, help="device copies of the weights cycled per step")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle timing")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -58,6 +58,9 @@ def algorithmic(inp, ids):
     if s.mxfp4:
         gu_bytes = 2 * I * (H // 2 + H // 32)
         d_bytes = H * (I // 2 + I // 32)
+    elif s.nvfp4:   # codes, an E4M3 byte per 16 values, the fp32 matrix scale
+        gu_bytes = 2 * I * (H // 2 + H // 16) + 4
+        d_bytes = H * (I // 2 + I // 16) + 4
     else:
         gu_bytes = 2 * I * H * 2
         d_bytes = H * I * 2
@@ -158,7 +161,7 @@ def main():
     t_gen = time.perf_counter()
     inp = mi.make(args.config, seed=0)
     s = inp.shape
-    sh = moe.shape(s.T, s.H, s.E, s.k, s.I, mxfp4=s.mxfp4, a4=s.a4)
+    sh = moe.shape(s.T, s.H, s.E, s.k, s.I, mxfp4=s.mxfp4, a4=s.a4, nvfp4=s.nvfp4)
     x = dev.to_device(inp.x)
     wr = dev.to_device(inp.w_router)
     bias = dev.to_device(inp.router_bias) if inp.router_bias is not None else None
@@ -166,6 +169,9 @@ def main():
     d0 = dev.to_device(inp.w_down)
     gus = dev.to_device(inp.gu_scales) if s.mxfp4 else None
     ds = dev.to_device(inp.d_scales) if s.mxfp4 else None
+    if s.nvfp4:   # one buffer per matrix: the fp32 expert scales, then the E4M3 codes
+        gus = dev.to_device(moe.nvfp4_scale_buffer(inp.gu_global, inp.gu_scales))
+        ds = dev.to_device(moe.nvfp4_scale_buffer(inp.d_global, inp.d_scales))
     copies = [(gu0, d0)] + [(gu0.clone(), d0.clone()) for _ in range(max(0, args.rotate - 1))]
     if s.I_sh:   # the dense MLP's weights rotate with the experts'
         sg0, sd0 = dev.to_device(inp.w_sh_gate_up), dev.to_device(inp.w_sh_down)
@@ -334,12 +340,13 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"Gemma-4-26B-A4B MoE FFN layer, {args.config}: T={s.T} tokens, "
                                f"hidden {s.H}, {s.E} experts, top-{s.k}, intermediate {s.I}, "
-                               f"GEGLU, {'MXFP4' if s.mxfp4 else 'bf16'} expert weights"
+                               f"GEGLU, {'MXFP4' if s.mxfp4 else ('NVFP4' if s.nvfp4 else 'bf16')} expert weights"
                                f"{' and MXFP4 activations (W4A4)' if s.a4 else ''}"
                                f"{', Zipf(1.2) router bias' if s.skew else ''}"
                                f"{f', plus the dense GEGLU MLP (intermediate {s.I_sh}) as a shared expert' if s.I_sh else ''}",
                    "T": s.T, "H": s.H, "E": s.E, "k": s.k, "I": s.I,
-                   "weights": ("mxfp4 weights and activations (W4A4)" if s.a4 else "mxfp4") if s.mxfp4 else "bf16",
+                   "weights": (("mxfp4 weights and activations (W4A4)" if s.a4 else "mxfp4") if s.mxfp4
+                               else ("nvfp4" if s.nvfp4 else "bf16")),
                    "weight_copies": len(copies),
                    **({"I_shared": s.I_sh} if s.I_sh else {})},
         "roofline": {

@@ -27,6 +27,15 @@
  *     E2M1/E8M0 encodings are the OCP Microscaling Formats v1.0 ones.  The
  *     router weight is always bf16.  Decoded weights must be normal bf16
  *     numbers (scale bytes 2..250 guarantee it); 0xFF scales are undefined.
+ *     NVFP4 weights (w_format MOE_W_NVFP4, the format of the
+ *     Gemma-4-26B-A4B-NVFP4 checkpoint of the verification report) have the
+ *     same E2M1 codes with one FP8 E4M3 scale per 16 consecutive K values
+ *     and one fp32 scale per expert matrix; a weight is E2M1(code) x
+ *     E4M3(block scale) x matrix scale.  Their scale argument is one buffer:
+ *     MOE_NVFP4_HEADER_BYTES(E) bytes holding the E fp32 matrix scales, then
+ *     the E4M3 codes [E][rows][K/16].  E4M3 is the OCP 8-bit floating point
+ *     format (exponent bias 7, largest value 448, no infinities); its NaN
+ *     codes (0x7F, 0xFF) are undefined as scales.
  *   - Assignment a = t*k + j is slot j of token t.  A = T*k.
  *   - Routing: the k largest logits, ties to the lower expert index, slots in
  *     (logit descending, index ascending) order; w = softmax over the k
@@ -54,7 +63,8 @@
  *   - Supported sizes: H % 64 == 0, I % 64 == 0, 1 <= k <= min(E, 32),
  *     E <= 1024, T*k < 2^30.  Pointers to bf16 arrays, x_perm, h and y must
  *     be 16-byte aligned (W4A4 weight codes too), the other arrays 4-byte
- *     aligned (MXFP4 scales: any address, 2-byte aligned for W4A4).
+ *     aligned (MXFP4 scales: any address, 2-byte aligned for W4A4; NVFP4
+ *     scale buffers 4-byte aligned).
  */
 #ifndef MOE_H
 #define MOE_H
@@ -72,7 +82,7 @@ typedef struct moe_shape {
     int32_t E;        /* experts */
     int32_t k;        /* experts per token */
     int32_t I;        /* expert intermediate size */
-    int32_t w_format; /* MOE_W_BF16, MOE_W_MXFP4 or MOE_W_MXFP4_A4 */
+    int32_t w_format; /* MOE_W_BF16, MOE_W_MXFP4, MOE_W_MXFP4_A4 or MOE_W_NVFP4 */
 } moe_shape;
 
 /* Expert weight format.  MOE_W_MXFP4_A4 (W4A4): MXFP4 weights, and the
@@ -84,8 +94,14 @@ typedef struct moe_shape {
  * The router still reads the bf16 x.  The vLLM-Ascend Gemma4 tutorial,
  * section 3.1, names w4a4 MXFP4 checkpoints.  W4A4 runs through moe_forward
  * (no dense MLP) and moe_quantize_mx only; the per-step GEMM entry points
- * return MOE_ERR_UNSUPPORTED for it. */
-enum { MOE_W_BF16 = 0, MOE_W_MXFP4 = 1, MOE_W_MXFP4_A4 = 2 };
+ * return MOE_ERR_UNSUPPORTED for it.  MOE_W_NVFP4: NVFP4 expert weights
+ * (above) with bf16 activations, through moe_forward and the per-step GEMM
+ * entry points; not with a dense MLP. */
+enum { MOE_W_BF16 = 0, MOE_W_MXFP4 = 1, MOE_W_MXFP4_A4 = 2, MOE_W_NVFP4 = 3 };
+
+/* Bytes in front of the E4M3 codes of an NVFP4 scale buffer: the E fp32
+ * matrix scales, padded to a multiple of 256. */
+#define MOE_NVFP4_HEADER_BYTES(E) ((((size_t)(E) * 4u + 255u) / 256u) * 256u)
 
 enum {
     MOE_OK = 0,
@@ -143,8 +159,9 @@ int moe_permute(const moe_shape *s, const int32_t *topk_ids, const uint16_t *x,
  *                sorted_ids != NULL: x [T][H] bf16, row p = x[sorted_ids[p] / k]
  *   sorted_ids   [T*k] int32 or NULL (see x)
  *   offsets      [E+1] int32
- *   w_gate_up    bf16 [E][2I][H], or MXFP4 codes [E][2I][H/2]
- *   gu_scales    NULL for bf16; MXFP4 scales [E][2I][H/32]
+ *   w_gate_up    bf16 [E][2I][H], or MXFP4 / NVFP4 codes [E][2I][H/2]
+ *   gu_scales    NULL for bf16; MXFP4 scales [E][2I][H/32]; NVFP4 scale
+ *                buffer (E fp32, then E4M3 codes [E][2I][H/16])
  *   h            [T*k][I] bf16 out
  */
 int moe_grouped_gemm_gateup(const moe_shape *s, const uint16_t *x,
@@ -156,8 +173,9 @@ int moe_grouped_gemm_gateup(const moe_shape *s, const uint16_t *x,
  * moe_grouped_gemm_down -- per expert: y rows = h rows W_d[e]^T, fp32
  * accumulation, bf16 out.
  *   h            [T*k][I] bf16;  offsets [E+1] int32
- *   w_down       bf16 [E][H][I], or MXFP4 codes [E][H][I/2]
- *   d_scales     NULL for bf16; MXFP4 scales [E][H][I/32]
+ *   w_down       bf16 [E][H][I], or MXFP4 / NVFP4 codes [E][H][I/2]
+ *   d_scales     NULL for bf16; MXFP4 scales [E][H][I/32]; NVFP4 scale
+ *                buffer (E fp32, then E4M3 codes [E][H][I/16])
  *   y            [T*k][H] bf16 out
  */
 int moe_grouped_gemm_down(const moe_shape *s, const uint16_t *h,

@@ -9,7 +9,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe.so")
 
-MOE_W_BF16, MOE_W_MXFP4, MOE_W_MXFP4_A4 = 0, 1, 2
+MOE_W_BF16, MOE_W_MXFP4, MOE_W_MXFP4_A4, MOE_W_NVFP4 = 0, 1, 2, 3
 MOE_FORWARD_STAGES = 5
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARGUMENT", -2: "MOE_ERR_UNSUPPORTED",
           -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP"}
@@ -80,9 +80,29 @@ def load(path: str = LIB_PATH):
     return lib
 
 
-def shape(T, H, E, k, I, mxfp4=False, a4=False) -> MoeShape:
-    fmt = MOE_W_MXFP4_A4 if a4 else (MOE_W_MXFP4 if mxfp4 else MOE_W_BF16)
+def shape(T, H, E, k, I, mxfp4=False, a4=False, nvfp4=False) -> MoeShape:
+    if nvfp4:
+        fmt = MOE_W_NVFP4
+    else:
+        fmt = MOE_W_MXFP4_A4 if a4 else (MOE_W_MXFP4 if mxfp4 else MOE_W_BF16)
     return MoeShape(T, H, E, k, I, fmt)
+
+
+def nvfp4_header_bytes(E: int) -> int:
+    """MOE_NVFP4_HEADER_BYTES(E): bytes of fp32 matrix scales, padded to 256,
+    in front of the E4M3 codes of an NVFP4 scale buffer."""
+    return (E * 4 + 255) // 256 * 256
+
+
+def nvfp4_scale_buffer(matrix_scales, block_scales):
+    """Host bytes of one NVFP4 scale argument: the E fp32 matrix scales
+    (padded to nvfp4_header_bytes(E)) followed by the E4M3 codes
+    [E][rows][K/16] (numpy arrays in, a flat uint8 numpy array out)."""
+    import numpy as np
+    g = np.ascontiguousarray(matrix_scales, dtype=np.float32).reshape(-1)
+    head = np.zeros(nvfp4_header_bytes(g.size), dtype=np.uint8)
+    head[:g.size * 4] = g.view(np.uint8)
+    return np.concatenate([head, np.ascontiguousarray(block_scales, dtype=np.uint8).reshape(-1)])
 
 
 def _ptr(t):

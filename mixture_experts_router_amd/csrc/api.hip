@@ -19,7 +19,8 @@ int check_shape(const moe_shape *s) {
     if (!s) return MOE_ERR_INVALID_ARGUMENT;
     if (s->T < 1 || s->H < 1 || s->E < 1 || s->k < 1 || s->I < 1) return MOE_ERR_INVALID_ARGUMENT;
     if (s->k > s->E) return MOE_ERR_INVALID_ARGUMENT;
-    if (s->w_format != MOE_W_BF16 && s->w_format != MOE_W_MXFP4 && s->w_format != MOE_W_MXFP4_A4)
+    if (s->w_format != MOE_W_BF16 && s->w_format != MOE_W_MXFP4 && s->w_format != MOE_W_MXFP4_A4 &&
+        s->w_format != MOE_W_NVFP4)
         return MOE_ERR_UNSUPPORTED;
     if (s->H % 64 != 0 || s->I % 64 != 0) return MOE_ERR_UNSUPPORTED;
     if (s->E > 1024 || s->k > 32) return MOE_ERR_UNSUPPORTED;
@@ -63,8 +64,26 @@ int check_weights(const moe_shape *s, const void *w, const uint8_t *scales) {
         if (!scales || !(s->w_format == MOE_W_MXFP4_A4 ? al16(w) : al4(w))) return MOE_ERR_INVALID_ARGUMENT;
         if (s->w_format == MOE_W_MXFP4_A4 && (reinterpret_cast<uintptr_t>(scales) & 1u))
             return MOE_ERR_INVALID_ARGUMENT;
+        // NVFP4: the fp32 header and one 32-bit load of 4 scales per row and step
+        if (s->w_format == MOE_W_NVFP4 && !al4(scales)) return MOE_ERR_INVALID_ARGUMENT;
     }
     return MOE_OK;
+}
+
+// The grouped GEMMs' view of an expert weight argument: format, block
+// scales and (NVFP4) the per-expert fp32 scales in front of them.
+struct WeightView {
+    moe::WeightFormat fmt;
+    const uint8_t *scales;
+    const float *global;
+};
+
+WeightView weight_view(const moe_shape *s, const uint8_t *scales) {
+    if (s->w_format == MOE_W_NVFP4)
+        return {moe::WeightFormat::kNVFP4, scales + MOE_NVFP4_HEADER_BYTES(s->E),
+                reinterpret_cast<const float *>(scales)};
+    if (s->w_format == MOE_W_MXFP4) return {moe::WeightFormat::kMXFP4, scales, nullptr};
+    return {moe::WeightFormat::kBF16, scales, nullptr};
 }
 
 struct Workspace {
@@ -130,7 +149,7 @@ static int forward_impl(const moe_shape *s, const uint16_t *x, const uint16_t *w
     if (I_sh < 0) return MOE_ERR_INVALID_ARGUMENT;
     const bool a4 = s->w_format == MOE_W_MXFP4_A4;
     if (I_sh > 0) {
-        if (a4 || I_sh % 64 != 0) return MOE_ERR_UNSUPPORTED;
+        if (a4 || s->w_format == MOE_W_NVFP4 || I_sh % 64 != 0) return MOE_ERR_UNSUPPORTED;
         if ((st = check_weights(s, w_sh_gate_up, sh_gu_scales)) != MOE_OK) return st;
         if ((st = check_weights(s, w_sh_down, sh_d_scales)) != MOE_OK) return st;
     }
@@ -152,7 +171,7 @@ static int forward_impl(const moe_shape *s, const uint16_t *x, const uint16_t *w
     float *wts = topk_w_out ? topk_w_out : w.w;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const int T = s->T, H = s->H, E = s->E, k = s->k, I = s->I, A = T * k;
-    const bool mx = s->w_format == MOE_W_MXFP4;
+    const WeightView gu = weight_view(s, gu_scales), dn = weight_view(s, d_scales);
 
     int stage = 0;
     auto mark = [&]() -> int {
@@ -193,10 +212,10 @@ static int forward_impl(const moe_shape *s, const uint16_t *x, const uint16_t *w
     // the shared expert (if any) is an extra group of the same two launches
     const moe::SharedGroup sh_gu{x, w_sh_gate_up, sh_gu_scales, w.h_sh, nullptr, T, I_sh};
     const moe::SharedGroup sh_d{w.h_sh, w_sh_down, sh_d_scales, nullptr, w.y_sh32, T, I_sh};
-    st = hip_status(moe::launch_gateup(x, w.sorted_ids, k, w.offsets, w_gate_up, gu_scales, w.h, A, H, E, I, mx,
-                                       I_sh > 0 ? &sh_gu : nullptr, hs));
+    st = hip_status(moe::launch_gateup(x, w.sorted_ids, k, w.offsets, w_gate_up, gu.scales, gu.global, w.h, A, H,
+                                       E, I, gu.fmt, I_sh > 0 ? &sh_gu : nullptr, hs));
     if (st != MOE_OK || (st = mark()) != MOE_OK) return st;
-    st = hip_status(moe::launch_down(w.h, w.offsets, w_down, d_scales, w.y, A, H, E, I, mx,
+    st = hip_status(moe::launch_down(w.h, w.offsets, w_down, dn.scales, dn.global, w.y, A, H, E, I, dn.fmt,
                                      I_sh > 0 ? &sh_d : nullptr, hs));
     if (st != MOE_OK || (st = mark()) != MOE_OK) return st;
     st = hip_status(moe::launch_combine(w.y, w.inv, wts, w.y_sh32, I_sh > 0 ? moe::shared_splits(I_sh, I) : 0, out,
@@ -281,8 +300,9 @@ int moe_grouped_gemm_gateup(const moe_shape *s, const uint16_t *x, const int32_t
     if (sorted_ids && !al4(sorted_ids)) return MOE_ERR_INVALID_ARGUMENT;
     if ((st = check_weights(s, w_gate_up, gu_scales)) != MOE_OK) return st;
     if (s->w_format == MOE_W_MXFP4_A4) return MOE_ERR_UNSUPPORTED;
-    return hip_status(moe::launch_gateup(x, sorted_ids, s->k, offsets, w_gate_up, gu_scales, h,
-                                         s->T * s->k, s->H, s->E, s->I, s->w_format == MOE_W_MXFP4, nullptr,
+    const WeightView wv = weight_view(s, gu_scales);
+    return hip_status(moe::launch_gateup(x, sorted_ids, s->k, offsets, w_gate_up, wv.scales, wv.global, h,
+                                         s->T * s->k, s->H, s->E, s->I, wv.fmt, nullptr,
                                          static_cast<hipStream_t>(stream)));
 }
 
@@ -294,8 +314,9 @@ int moe_grouped_gemm_down(const moe_shape *s, const uint16_t *h, const int32_t *
     if (!al16(h) || !al16(y) || !al4(offsets)) return MOE_ERR_INVALID_ARGUMENT;
     if ((st = check_weights(s, w_down, d_scales)) != MOE_OK) return st;
     if (s->w_format == MOE_W_MXFP4_A4) return MOE_ERR_UNSUPPORTED;
-    return hip_status(moe::launch_down(h, offsets, w_down, d_scales, y, s->T * s->k, s->H, s->E, s->I,
-                                       s->w_format == MOE_W_MXFP4, nullptr, static_cast<hipStream_t>(stream)));
+    const WeightView wv = weight_view(s, d_scales);
+    return hip_status(moe::launch_down(h, offsets, w_down, wv.scales, wv.global, y, s->T * s->k, s->H, s->E, s->I,
+                                       wv.fmt, nullptr, static_cast<hipStream_t>(stream)));
 }
 
 int moe_combine(const moe_shape *s, const uint16_t *y, const int32_t *inv, const float *topk_w,

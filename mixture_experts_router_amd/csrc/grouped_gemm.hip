@@ -46,7 +46,7 @@ struct GemmArgs {
     int gather_k;             // k: row p reads a[gather[p] / k]
     const int32_t *offsets;   // [E + 1]
     const void *w;            // bf16 [E][rows][K] or MXFP4 codes [E][rows][K/2]
-    const uint8_t *scales;    // MXFP4 scales [E][rows][K/32] or nullptr
+    const uint8_t *scales;    // MXFP4 scales [E][rows][K/32], NVFP4 [E][rows][K/16], or nullptr
     uint16_t *out;            // [A][n_out] bf16
     int E, K, n_out, I;       // I: gate/up split (gate/up only)
     int w_rows;               // weight rows per expert (2I or H)
@@ -71,6 +71,9 @@ struct GemmArgs {
     int sh_splits, sh_ksplit; // down: K cut into sh_splits ranges of sh_ksplit (last one shorter)
     // W4A4: `a` holds MXFP4 codes [rows][K/2] and a_scales [rows][K/32]
     const uint8_t *a_scales;
+    // NVFP4 weights: `scales` holds E4M3 codes [E][rows][K/16] and w_global
+    // the fp32 scale of each expert's matrix [E]
+    const float *w_global;
 };
 
 // Locate this workgroup's M tile: tile index -> (expert, first row).  Run by
@@ -113,7 +116,8 @@ __device__ __forceinline__ void find_tile(const int32_t *__restrict__ offsets, i
 
 enum GemmMode { kDown = 0, kGateUp = 1, kRouter = 2 };
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int MODE, bool MX, int NS_, int BK_, bool A4_ = false>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int MODE, bool MX, int NS_, int BK_, bool A4_ = false,
+          bool NV_ = false>
 struct GemmTile {
     static constexpr bool GEGLU = MODE == kGateUp;
     static constexpr int BK = BK_;                // K per step (32, 64 or 128)
@@ -153,6 +157,10 @@ struct GemmTile {
     // W4A4: both operands are MXFP4 codes loaded like bf16 tiles (128-byte
     // rows = 256 K values per stage, two 16x16x128 scaled MFMA steps).
     static_assert(!A4_ || (!MX && BK == 64), "W4A4 tiles: code rows of 128 bytes");
+    // NVFP4 weights take the MXFP4 route with four E4M3 scales per row and
+    // step (blocks of 16), kept in LDS as fp32
+    static_assert(!NV_ || (MX && !A4_), "NVFP4 is a variant of the MXFP4 weight path");
+    static constexpr int SS_BYTES = MX ? (NV_ ? 16 * BN : 2 * BN) : 1;
     // W4A4 block scales of a stage: 8 bytes (blocks 8 kt .. 8 kt + 7) per
     // weight row and per token row, one row per thread.
     static constexpr bool SC_PAIR_M = MI >= 2;   // token rows paired like weight rows
@@ -209,19 +217,21 @@ __device__ __forceinline__ void dma16(const void *g, const void *lds) {
         asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(l) : "memory", "m0");
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int MODE, bool MX, int NS_, int BK_, bool A4 = false>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int MODE, bool MX, int NS_, int BK_, bool A4 = false,
+          bool NV = false>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(GemmArgs p) {
-    using G = GemmTile<BM, BN, WAVES_M, WAVES_N, MODE, MX, NS_, BK_, A4>;
+    using G = GemmTile<BM, BN, WAVES_M, WAVES_N, MODE, MX, NS_, BK_, A4, NV>;
     constexpr bool GEGLU = MODE == kGateUp, ROUTER = MODE == kRouter;
     constexpr int BK = G::BK, NS = G::NS, WTM = G::WTM, WN = G::WN, MI = G::MI, NI = G::NI;
     constexpr int CH = G::CH, RPD = G::RPD, KK = G::KK;
     constexpr int NA = G::NA, NB = G::NB, A_W = G::A_W, B_W = G::B_W, NW = G::NW, NT = G::NT;
 
     // bf16 tiles: [row][8 chunks of 16 B], chunk index XOR-swizzled by row.
-    // MXFP4 codes: [chunk (8 words of 4 B)][row]; scales: [2 blocks][row].
+    // MXFP4 codes: [chunk (8 words of 4 B)][row]; scales: [2 blocks][row]
+    // (NVFP4: fp32 [4 blocks][row]).
     __shared__ __attribute__((aligned(1024))) uint16_t As[NS][G::A_LDS];
     __shared__ __attribute__((aligned(1024))) uint16_t Bs[NS][G::B_LDS];
-    __shared__ __attribute__((aligned(16))) uint8_t Ss[NS][MX ? 2 * BN : 1];
+    __shared__ __attribute__((aligned(16))) uint8_t Ss[NS][G::SS_BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t Sc[NS][A4 ? G::SC_BYTES : 1];
     __shared__ int s_info[4];
 
@@ -398,14 +408,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
 #pragma unroll
         for (int i = 0; i < G::MS_PER; ++i) {
             const int v = (tid + NT * i) % BN;
-            ms_src[i] = g_scales + ((size_t)e * g_w_rows + weight_row(v)) * (K / 32) + kb / 32;
+            constexpr int BLK = NV ? 16 : 32;   // K values per scale
+            ms_src[i] = g_scales + ((size_t)e * g_w_rows + weight_row(v)) * (K / BLK) + kb / BLK;
         }
     }
     auto issue_mx = [&](int kt) {
 #pragma unroll
         for (int i = 0; i < G::MB_PER; ++i) mb[i] = *reinterpret_cast<const u32x4 *>(mb_src[i] + kt * (BK / 2));
 #pragma unroll
-        for (int i = 0; i < G::MS_PER; ++i) ms[i] = *reinterpret_cast<const uint16_t *>(ms_src[i] + kt * 2);
+        for (int i = 0; i < G::MS_PER; ++i)
+            ms[i] = NV ? *reinterpret_cast<const uint32_t *>(ms_src[i] + kt * 4)
+                       : *reinterpret_cast<const uint16_t *>(ms_src[i] + kt * 2);
     };
     auto commit_mx = [&](int kt) {
         const int slot = kt % NS;
@@ -423,8 +436,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
         for (int i = 0; i < G::MS_PER; ++i) {
             const int v = tid + NT * i;
             if (v < BN) {
-                Ss[slot][v] = (uint8_t)(ms[i] & 0xFFu);
-                Ss[slot][BN + v] = (uint8_t)(ms[i] >> 8);
+                if (NV) {   // the step's four E4M3 block scales, as fp32
+                    float *sf = reinterpret_cast<float *>(Ss[slot]);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) sf[q * BN + v] = e4m3_to_f32((ms[i] >> (8 * q)) & 0xFFu);
+                } else {
+                    Ss[slot][v] = (uint8_t)(ms[i] & 0xFFu);
+                    Ss[slot][BN + v] = (uint8_t)(ms[i] >> 8);
+                }
             }
         }
     };
@@ -542,7 +561,24 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
 #pragma unroll
             for (int j = 0; j < NI; ++j) {
                 const int r = wn * WN + j * 16 + lrow;
-                if (MX) {
+                if (MX && NV) {
+                    // E2M1 -> bf16 at scale 1, then times the block's E4M3
+                    // scale: the product has at most 6 significant bits, so
+                    // it is exactly a bf16 value (the lane's 8 codes are K
+                    // 8 ch .. 8 ch + 7, block 2 kk + lk / 2 of the step)
+                    const uint32_t codes = reinterpret_cast<const uint32_t *>(Bs[slot])[ch * BN + r];
+                    const float sc = reinterpret_cast<const float *>(Ss[slot])[(2 * kk + (lk >> 1)) * BN + r];
+                    u32x4 v;
+                    v[0] = bf16x2_scale_exact(
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, 1.0f, 0)), sc);
+                    v[1] = bf16x2_scale_exact(
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, 1.0f, 1)), sc);
+                    v[2] = bf16x2_scale_exact(
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, 1.0f, 2)), sc);
+                    v[3] = bf16x2_scale_exact(
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, 1.0f, 3)), sc);
+                    wf[j] = v;
+                } else if (MX) {
                     const uint32_t codes = reinterpret_cast<const uint32_t *>(Bs[slot])[ch * BN + r];
                     const float sc = __uint_as_float((uint32_t)Ss[slot][kk * BN + r] << 23);
                     u32x4 v;
@@ -637,7 +673,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
     else run(std::false_type{});
 
     // ---- epilogue: lane holds weight rows 4*lk .. 4*lk+3 of tile j for the
-    // token lrow of token tile i.
+    // token lrow of token tile i.  NVFP4: the expert matrix's fp32 scale
+    // multiplies the fp32 sums (before the GEGLU).
+    const float gsc = NV ? p.w_global[e] : 1.0f;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
         const int t = wm * WTM + i * 16 + lrow;
@@ -661,7 +699,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
             for (int j = 0; j < HALF_T; ++j) {
                 const int n = nt * (BN / 2) + wn * (WN / 2) + j * 16 + 4 * lk;
                 if (n >= g_I) continue;
-                const f32x4 g = acc[j][i], u = acc[j + HALF_T][i];
+                f32x4 g = acc[j][i], u = acc[j + HALF_T][i];
+                if (NV) {
+                    g *= gsc;
+                    u *= gsc;
+                }
                 uint2 o;
                 o.x = pack_bf16x2(gelu_tanh(g[0]) * u[0], gelu_tanh(g[1]) * u[1]);
                 o.y = pack_bf16x2(gelu_tanh(g[2]) * u[2], gelu_tanh(g[3]) * u[3]);
@@ -680,7 +722,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
             for (int j = 0; j < NI; ++j) {
                 const int n = nt * BN + wn * WN + j * 16 + 4 * lk;
                 if (n >= g_n_out) continue;
-                const f32x4 v = acc[j][i];
+                f32x4 v = acc[j][i];
+                if (NV) v *= gsc;
                 uint2 o;
                 o.x = pack_bf16x2(v[0], v[1]);
                 o.y = pack_bf16x2(v[2], v[3]);
@@ -697,7 +740,7 @@ static int mtile_slots(int A, int E, int BM) {
     return (int)(((long long)A + (long long)(BM - 1) * ne) / BM);
 }
 
-template <int BM, int BN, int WM, int WN, int MODE, bool MX, int NS, int BK, bool A4 = false>
+template <int BM, int BN, int WM, int WN, int MODE, bool MX, int NS, int BK, bool A4 = false, bool NV = false>
 static hipError_t launch_cfg(GemmArgs a, int A, hipStream_t st) {
     constexpr bool GEGLU = MODE == kGateUp;
     const int ncols = GEGLU ? a.I : a.n_out;
@@ -722,13 +765,13 @@ static hipError_t launch_cfg(GemmArgs a, int A, hipStream_t st) {
         blocks += (long long)a.sh_n_tiles * ((a.sh_rows + BM - 1) / BM) * max(1, a.sh_splits);
     }
     if (blocks == 0) return hipSuccess;
-    grouped_gemm_kernel<BM, BN, WM, WN, MODE, MX, NS, BK, A4><<<dim3((unsigned)blocks), 64 * WM * WN, 0, st>>>(a);
+    grouped_gemm_kernel<BM, BN, WM, WN, MODE, MX, NS, BK, A4, NV><<<dim3((unsigned)blocks), 64 * WM * WN, 0, st>>>(a);
     return hipGetLastError();
 }
 
 // Row-block size from the mean rows per expert (a function of the shape
 // only, so the launch does not depend on the routing).
-template <int MODE, bool MX>
+template <int MODE, bool MX, bool NV = false>
 static hipError_t launch_sized(const GemmArgs &a, int A, hipStream_t st) {
     const int mean_rows = A / a.E;
     // Small row blocks stream weights: two stages keep LDS small enough for
@@ -738,17 +781,18 @@ static hipError_t launch_sized(const GemmArgs &a, int A, hipStream_t st) {
     // per-CU load path; bf16 in two stages of 64 KB, MXFP4 (small weight
     // tiles) in three.  (Measured: K steps of 32 in four stages are slower.)
     if (mean_rows <= 16) {
-        // Weight rows read in 256-byte pieces per step where K allows it
-        // (measured: 2% faster than 128-byte pieces at 2816 x 1408).
-        // both groups' K ranges; with a shared group the smaller stages keep
-        // four workgroups per CU, so routed and shared tiles run in one round
-        const bool k128 = a.K % 128 == 0 && a.sh_rows == 0;
-        if (!MX && k128) return launch_cfg<16, 128, 1, 4, MODE, MX, 2, MX ? 64 : 128>(a, A, st);
-        return launch_cfg<16, 128, 1, 4, MODE, MX, 2, 64>(a, A, st);
+        // bf16 weight rows are read in 256-byte pieces per step where K
+        // allows it (measured: 2% faster than 128-byte pieces at 2816 x
+        // 1408).  Not with a shared group: its K need not be a multiple of
+        // 128, and the smaller stages keep four workgroups per CU, so routed
+        // and shared tiles run in one round.
+        if constexpr (!MX)
+            if (a.K % 128 == 0 && a.sh_rows == 0) return launch_cfg<16, 128, 1, 4, MODE, MX, 2, 128>(a, A, st);
+        return launch_cfg<16, 128, 1, 4, MODE, MX, 2, 64, false, NV>(a, A, st);
     }
-    if (mean_rows <= 40) return launch_cfg<32, 128, 2, 2, MODE, MX, 2, 64>(a, A, st);
-    if (mean_rows <= 80) return launch_cfg<64, 128, 2, 2, MODE, MX, 2, 64>(a, A, st);
-    return launch_cfg<256, 256, 4, 2, MODE, MX, MX ? 3 : 2, 64>(a, A, st);
+    if (mean_rows <= 40) return launch_cfg<32, 128, 2, 2, MODE, MX, 2, 64, false, NV>(a, A, st);
+    if (mean_rows <= 80) return launch_cfg<64, 128, 2, 2, MODE, MX, 2, 64, false, NV>(a, A, st);
+    return launch_cfg<256, 256, 4, 2, MODE, MX, MX ? 3 : 2, 64, false, NV>(a, A, st);
 }
 
 // W4A4: the same tile choice as bf16 activations, K steps of 256 codes.
@@ -779,9 +823,10 @@ hipError_t launch_down_a4(const uint8_t *hq, const uint8_t *hs, const int32_t *o
 }
 
 hipError_t launch_gateup(const uint16_t *x, const int32_t *sorted_ids, int k, const int32_t *offsets,
-                         const void *w, const uint8_t *scales, uint16_t *h, int A, int H, int E, int I,
-                         bool mx, const SharedGroup *sh, hipStream_t st) {
+                         const void *w, const uint8_t *scales, const float *w_global, uint16_t *h, int A, int H,
+                         int E, int I, WeightFormat fmt, const SharedGroup *sh, hipStream_t st) {
     GemmArgs a{x, sorted_ids, k, offsets, w, scales, h, E, H, I, I, 2 * I, 0, 0, 0, nullptr, nullptr};
+    a.w_global = w_global;
     if (sh) {   // every token through the shared gate/up weights [2 I_sh][H]
         a.sh_rows = sh->rows;
         a.sh_a = x;
@@ -795,12 +840,15 @@ hipError_t launch_gateup(const uint16_t *x, const int32_t *sorted_ids, int k, co
         a.sh_splits = 1;
         a.sh_ksplit = H;
     }
-    return mx ? launch_sized<kGateUp, true>(a, A, st) : launch_sized<kGateUp, false>(a, A, st);
+    if (fmt == WeightFormat::kNVFP4) return sh ? hipErrorInvalidValue : launch_sized<kGateUp, true, true>(a, A, st);
+    return fmt == WeightFormat::kMXFP4 ? launch_sized<kGateUp, true>(a, A, st) : launch_sized<kGateUp, false>(a, A, st);
 }
 
 hipError_t launch_down(const uint16_t *h, const int32_t *offsets, const void *w, const uint8_t *scales,
-                       uint16_t *y, int A, int H, int E, int I, bool mx, const SharedGroup *sh, hipStream_t st) {
+                       const float *w_global, uint16_t *y, int A, int H, int E, int I, WeightFormat fmt,
+                       const SharedGroup *sh, hipStream_t st) {
     GemmArgs a{h, nullptr, 1, offsets, w, scales, y, E, I, H, I, H, 0, 0, 0, nullptr, nullptr};
+    a.w_global = w_global;
     if (sh) {   // the shared h rows [rows][I_sh] through the shared down weights [H][I_sh]
         a.sh_rows = sh->rows;
         a.sh_a = sh->a;
@@ -818,7 +866,8 @@ hipError_t launch_down(const uint16_t *h, const int32_t *offsets, const void *w,
         a.sh_splits = shared_splits(sh->I, I);
         a.sh_ksplit = shared_ksplit(sh->I, I);
     }
-    return mx ? launch_sized<kDown, true>(a, A, st) : launch_sized<kDown, false>(a, A, st);
+    if (fmt == WeightFormat::kNVFP4) return sh ? hipErrorInvalidValue : launch_sized<kDown, true, true>(a, A, st);
+    return fmt == WeightFormat::kMXFP4 ? launch_sized<kDown, true>(a, A, st) : launch_sized<kDown, false>(a, A, st);
 }
 
 // Router for many tokens: x [T][H] times W_r [E][H]^T as one dense group, 16

@@ -82,6 +82,24 @@ __device__ __forceinline__ f32x4 mfma_fp4x128(const u32x4 &a, const u32x4 &b, f3
 #undef MOE_FP4_CASE
 }
 
+// FP8 E4M3 code -> fp32 (OCP 8-bit floating point: exponent bias 7, three
+// mantissa bits, exponent field 0 subnormal m * 2^-9, no infinities).  The
+// NaN codes S.1111.111 are not valid scales; they decode to +-480.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+    const uint32_t ef = (b >> 3) & 15u, m = b & 7u;
+    const float v = ef ? __uint_as_float(((ef + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+    return (b & 0x80u) ? -v : v;
+}
+
+// A packed bf16 pair times s, for products that are exactly bf16 values
+// (an E2M1 value times an E4M3 scale): the fp32 products are truncated to
+// their top 16 bits, which loses nothing.
+__device__ __forceinline__ uint32_t bf16x2_scale_exact(uint32_t w, float s) {
+    const float lo = __uint_as_float(w << 16) * s;
+    const float hi = __uint_as_float(w & 0xFFFF0000u) * s;
+    return (__float_as_uint(hi) & 0xFFFF0000u) | (__float_as_uint(lo) >> 16);
+}
+
 // 16x16x32 bf16 MFMA with fp32 accumulation.  Operand layout per lane l:
 // A row (l % 16), k = 8*(l/16) .. +7; B column (l % 16), same k range;
 // result rows 4*(l/16) + r (r = 0..3), column l % 16.

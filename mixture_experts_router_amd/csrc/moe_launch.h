@@ -62,11 +62,16 @@ inline int shared_splits(int I_sh, int I_expert) {
     const int ks = shared_ksplit(I_sh, I_expert);
     return (I_sh + ks - 1) / ks;
 }
+// Expert weight formats of the grouped GEMMs: bf16; MXFP4 (scales: E8M0
+// [E][rows][K/32]); NVFP4 (scales: E4M3 [E][rows][K/16], w_global: the fp32
+// scale of each expert's matrix [E]; no shared group).
+enum class WeightFormat { kBF16, kMXFP4, kNVFP4 };
 hipError_t launch_gateup(const uint16_t *x, const int32_t *sorted_ids, int k, const int32_t *offsets,
-                         const void *w, const uint8_t *scales, uint16_t *h, int A, int H, int E, int I,
-                         bool mx, const SharedGroup *sh, hipStream_t st);
+                         const void *w, const uint8_t *scales, const float *w_global, uint16_t *h, int A, int H,
+                         int E, int I, WeightFormat fmt, const SharedGroup *sh, hipStream_t st);
 hipError_t launch_down(const uint16_t *h, const int32_t *offsets, const void *w, const uint8_t *scales,
-                       uint16_t *y, int A, int H, int E, int I, bool mx, const SharedGroup *sh, hipStream_t st);
+                       const float *w_global, uint16_t *y, int A, int H, int E, int I, WeightFormat fmt,
+                       const SharedGroup *sh, hipStream_t st);
 // W4A4 grouped GEMMs: activations as MXFP4 codes [rows][K/2] + E8M0 scales
 // [rows][K/32] (launch_quantize_mx), weights MXFP4; K a multiple of 64.
 hipError_t launch_gateup_a4(const uint8_t *xq, const uint8_t *xs, const int32_t *sorted_ids, int k,

@@ -21,7 +21,16 @@ print no data for the layer, so every value here is synthetic:
 * MXFP4 experts quantise the bf16 expert weights per 32-element block along K
   with the OCP Microscaling Formats v1.0 conversion (shared E8M0 scale
   2^(floor(log2 amax) - 2), elements rounded to nearest-even E2M1 and
-  saturated at +-6), two codes per byte, low nibble = even K index.
+  saturated at +-6), two codes per byte, low nibble = even K index;
+* NVFP4 experts (the format of the Gemma-4-26B-A4B-NVFP4 checkpoint the
+  verification report runs) store E2M1 codes like MXFP4 with one FP8 E4M3
+  scale per 16 consecutive K elements and one fp32 scale per expert matrix.
+  Their synthetic values come from the same bf16 weights: the expert scale is
+  amax / (6 * 448) (so the largest block scale lands on the largest E4M3
+  value), each block scale is the block's amax / (6 * expert scale) rounded
+  to the nearest E4M3 value (ties to the even code, saturating at 448), and
+  each element is w / (block scale * expert scale) rounded to the nearest
+  E2M1 value as above.
 
 Weight storage is K-contiguous: router [E, H], gate/up [E, 2I, H] with rows
 0..I-1 the gate and I..2I-1 the up projection, down [E, H, I].
@@ -42,7 +51,8 @@ import numpy as np
 
 __all__ = [
     "Shape", "CONFIGS", "make", "make_shape", "f32_to_bf16_bits",
-    "bf16_bits_to_f32", "mxfp4_quantize", "random_bf16", "random_ids",
+    "bf16_bits_to_f32", "mxfp4_quantize", "nvfp4_quantize", "e4m3_encode",
+    "random_bf16", "random_ids",
 ]
 
 
@@ -61,6 +71,7 @@ class Shape:
     w_sigma: float = 0.02
     I_sh: int = 0           # intermediate size of the always-on dense MLP (0: none)
     a4: bool = False        # with mxfp4: activations quantised to MXFP4 too (W4A4)
+    nvfp4: bool = False     # expert weights stored as NVFP4 (E2M1, E4M3 per 16, fp32 per expert)
 
     @property
     def A(self) -> int:
@@ -82,6 +93,8 @@ CONFIGS = {
     "decode_shared": Shape(T=8, H=2816, E=128, k=8, I=704, I_sh=2112),
     # the prefill with MXFP4 experts and MXFP4 activations (W4A4)
     "w4a4": Shape(T=2048, H=2816, E=128, k=8, I=704, mxfp4=True, a4=True),
+    # the decode layer with NVFP4 expert weights (bf16 activations)
+    "nvfp4_decode": Shape(T=8, H=2816, E=128, k=8, I=704, nvfp4=True),
 }
 
 
@@ -150,6 +163,55 @@ def mxfp4_quantize(w_bits: np.ndarray):
     return packed, scale_byte
 
 
+def e4m3_encode(v: np.ndarray) -> np.ndarray:
+    """Nearest FP8 E4M3 code (OCP 8-bit floating point: exponent bias 7,
+    three mantissa bits, largest finite value 448, no infinities) of
+    non-negative values, ties to the even code, saturating at 448."""
+    v = np.minimum(np.asarray(v, dtype=np.float64), 448.0)
+    out = np.zeros(v.shape, dtype=np.int64)
+    pos = v > 0
+    e = np.floor(np.log2(np.where(pos, v, 1.0))).astype(np.int64)
+    sub = pos & (e < -6)
+    # subnormals m * 2^-9 (m = 8 is the smallest normal, code 8, so the
+    # codes run on without a seam)
+    out = np.where(sub, np.rint(v * 2.0 ** 9).astype(np.int64), out)
+    nrm = pos & ~sub
+    m = np.rint((v / np.ldexp(1.0, np.where(nrm, e, 0)) - 1.0) * 8.0).astype(np.int64)
+    carry = m == 8
+    e2 = np.where(carry, e + 1, e)
+    m2 = np.where(carry, 0, m)
+    out = np.where(nrm, ((e2 + 7) << 3) | m2, out)
+    return np.minimum(out, 0x7E).astype(np.uint8)
+
+
+def _e4m3_value(code: np.ndarray) -> np.ndarray:
+    """Value of non-negative E4M3 codes below 0x7F (input preparation only)."""
+    c = np.asarray(code, dtype=np.int64)
+    e, m = c >> 3, c & 7
+    return np.where(e == 0, m * 2.0 ** -9, np.ldexp(1.0 + m / 8.0, e - 7))
+
+
+def nvfp4_quantize(w_bits: np.ndarray):
+    """Quantise one bf16 weight matrix [..., K] (uint16 bits) to NVFP4 along
+    the last axis.  Returns (packed codes uint8 [..., K/2], E4M3 scale codes
+    uint8 [..., K/16], the matrix's fp32 scale as a numpy float32).  A block
+    whose scale rounds to zero gets all-zero codes."""
+    w = bf16_bits_to_f32(w_bits).astype(np.float64)
+    K = w.shape[-1]
+    if K % 16:
+        raise ValueError("NVFP4 needs K % 16 == 0")
+    amax = float(np.max(np.abs(w)))
+    g = np.float32(amax / (6.0 * 448.0)) if amax > 0 else np.float32(1.0)
+    blocks = w.reshape(*w.shape[:-1], K // 16, 16)
+    bmax = np.max(np.abs(blocks), axis=-1)
+    sc = e4m3_encode(bmax / (6.0 * float(g)))
+    step = _e4m3_value(sc) * float(g)
+    q = np.where(step[..., None] > 0, blocks / np.where(step > 0, step, 1.0)[..., None], 0.0)
+    codes = _e2m1_encode(q.astype(np.float32)).reshape(*w.shape[:-1], K)
+    packed = (codes[..., 0::2] | (codes[..., 1::2] << np.uint8(4))).astype(np.uint8)
+    return packed, sc, g
+
+
 def zipf_log_prior(E: int, s: float) -> np.ndarray:
     """Router bias b_e = ln p_e with p_r proportional to r^-s, r = e + 1."""
     r = np.arange(1, E + 1, dtype=np.float64)
@@ -167,8 +229,10 @@ class Inputs:
     router_bias: Optional[np.ndarray]   # float32 [E] or None
     w_gate_up: np.ndarray         # uint16 [E, 2I, H], or uint8 packed MXFP4 [E, 2I, H/2]
     w_down: np.ndarray            # uint16 [E, H, I], or uint8 packed MXFP4 [E, H, I/2]
-    gu_scales: Optional[np.ndarray] = None   # uint8 [E, 2I, H/32] for MXFP4
-    d_scales: Optional[np.ndarray] = None    # uint8 [E, H, I/32] for MXFP4
+    gu_scales: Optional[np.ndarray] = None   # uint8 [E, 2I, H/32] for MXFP4, E4M3 [E, 2I, H/16] for NVFP4
+    d_scales: Optional[np.ndarray] = None    # uint8 [E, H, I/32] for MXFP4, E4M3 [E, H, I/16] for NVFP4
+    gu_global: Optional[np.ndarray] = None   # float32 [E]: NVFP4 per-expert scale of gate/up
+    d_global: Optional[np.ndarray] = None    # float32 [E]: NVFP4 per-expert scale of down
     # dense MLP (shape.I_sh > 0): uint16 [2 I_sh, H] and [H, I_sh], or MXFP4
     # codes [2 I_sh, H/2], [H, I_sh/2] with scales [2 I_sh, H/32], [H, I_sh/32]
     w_sh_gate_up: Optional[np.ndarray] = None
@@ -246,6 +310,8 @@ def make(config, seed: int = 0) -> Inputs:
     s = make_shape(config)
     if s.a4 and not s.mxfp4:
         raise ValueError("W4A4 (a4) needs MXFP4 weights (mxfp4)")
+    if s.nvfp4 and (s.mxfp4 or s.I_sh > 0):
+        raise ValueError("NVFP4 experts exclude MXFP4 and the dense MLP")
     T, H, E, k, I = s.T, s.H, s.E, s.k, s.I
     w_router, w_gu, w_d, state = _weights(s, seed)
     rng = np.random.default_rng(seed)
@@ -268,6 +334,22 @@ def make(config, seed: int = 0) -> Inputs:
             mx = (gu_q, gu_s, d_q, d_s)
             _MX_CACHE[key] = mx
         inp.w_gate_up, inp.gu_scales, inp.w_down, inp.d_scales = mx
+    if s.nvfp4:
+        key = ("nv", s.H, s.E, s.I, s.w_sigma, seed)
+        nv = _MX_CACHE.get(key)
+        if nv is None:
+            gu_q = np.empty((E, 2 * I, H // 2), dtype=np.uint8)
+            gu_s = np.empty((E, 2 * I, H // 16), dtype=np.uint8)
+            d_q = np.empty((E, H, I // 2), dtype=np.uint8)
+            d_s = np.empty((E, H, I // 16), dtype=np.uint8)
+            gu_g = np.empty(E, dtype=np.float32)
+            d_g = np.empty(E, dtype=np.float32)
+            for e in range(E):
+                gu_q[e], gu_s[e], gu_g[e] = nvfp4_quantize(w_gu[e])
+                d_q[e], d_s[e], d_g[e] = nvfp4_quantize(w_d[e])
+            nv = (gu_q, gu_s, gu_g, d_q, d_s, d_g)
+            _MX_CACHE[key] = nv
+        inp.w_gate_up, inp.gu_scales, inp.gu_global, inp.w_down, inp.d_scales, inp.d_global = nv
     if s.I_sh > 0:
         d = _Drawer(np.random.default_rng([seed, 2112]))
         sh_gu = d.into(np.empty((2 * s.I_sh, H), dtype=np.uint16), s.w_sigma)

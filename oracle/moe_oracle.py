@@ -29,6 +29,10 @@ gelu_pytorch_tanh):
       the nearest E2M1 value, ties to the even code, saturating at 6) before
       their matmuls; the router keeps the bf16 x (the pages name w4a4 MXFP4
       checkpoints: vLLM-Ascend Gemma4 tutorial, section 3.1)
+  O12 NVFP4 expert weights (the format of the Gemma-4-26B-A4B-NVFP4
+      checkpoint of the verification report) decoded to fp64 before O7:
+      E2M1 element x FP8 E4M3 scale of its 16-element block x the matrix's
+      fp32 scale
   O10 shapes with a dense MLP (I_sh > 0): out[t] += MLP(x[t]) with
       MLP(x) = (gelu_tanh(x Wg^T) * (x Wu^T)) Wd^T, the same GEGLU form as an
       expert, weight 1 (the block runs its dense MLP of intermediate 2112 next
@@ -42,7 +46,8 @@ design notes of the repository.
 
 Parity status: O2-O8 are pinned by the dense brute force (`dense_forward`) and
 by closed-form special cases in the CPU test suite; O9 is pinned by the E2M1
-table of the OCP Microscaling Formats v1.0 specification.  Against the real
+table of the OCP Microscaling Formats v1.0 specification; O12's E4M3 table by
+torch's float8_e4m3fn decoding of all finite codes.  Against the real
 Gemma-4 layer parity is unpinned: the pages print no activations or weights.
 """
 from __future__ import annotations
@@ -57,6 +62,7 @@ __all__ = [
     "down_proj", "combine", "expert_weights", "forward", "forward_tokens",
     "dense_forward", "routing_margin", "shared_weights", "shared_mlp",
     "mx_quantize", "mx_dequantize", "mx_round", "round_to_bf16",
+    "e4m3_to_f64", "nvfp4_to_f64",
 ]
 
 
@@ -97,8 +103,56 @@ def mxfp4_to_f64(packed, scales) -> np.ndarray:
     return vals.reshape(*codes.shape[:-1], K)
 
 
+# ---------------------------------------------------------------- O12
+def _e4m3_table() -> np.ndarray:
+    """Values of the 256 FP8 E4M3 codes (OCP 8-bit floating point
+    specification, E4M3: sign bit, four exponent bits with bias 7, three
+    mantissa bits; exponent field 0 is subnormal, 2^-6 * m/8; no
+    infinities; S.1111.111 is NaN, so 448 is the largest finite value)."""
+    t = np.empty(256, dtype=np.float64)
+    for c in range(256):
+        sign = -1.0 if c & 0x80 else 1.0
+        ef, m = (c >> 3) & 0xF, c & 0x7
+        if ef == 0xF and m == 0x7:
+            t[c] = np.nan
+        elif ef == 0:
+            t[c] = sign * math.ldexp(m / 8.0, -6)
+        else:
+            t[c] = sign * math.ldexp(1.0 + m / 8.0, ef - 7)
+    return t
+
+
+_E4M3 = _e4m3_table()
+
+
+def e4m3_to_f64(codes) -> np.ndarray:
+    """Exact values of FP8 E4M3 codes (O12)."""
+    return _E4M3[np.asarray(codes, dtype=np.uint8)]
+
+
+def nvfp4_to_f64(packed, scales, glob) -> np.ndarray:
+    """Decode one NVFP4 matrix to fp64 (O12).
+
+    packed [..., K/2] holds two E2M1 codes per byte, the even K index in the
+    low nibble (as for MXFP4); scales [..., K/16] one E4M3 code per 16
+    consecutive K elements; glob the matrix's fp32 scale.  Element value =
+    E2M1(code) * E4M3(scale) * glob."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    codes = np.stack([packed & 0x0F, packed >> 4], axis=-1).reshape(*packed.shape[:-1], packed.shape[-1] * 2)
+    K = codes.shape[-1]
+    sc = e4m3_to_f64(scales)
+    if np.any(np.isnan(sc)):
+        raise ValueError("E4M3 NaN code used as a scale")
+    vals = _E2M1[codes].reshape(*codes.shape[:-1], K // 16, 16) * sc[..., None]
+    return vals.reshape(*codes.shape[:-1], K) * float(np.float32(glob))
+
+
 def expert_weights(inp, e: int):
     """fp64 gate/up [2I, H] and down [H, I] weights of expert e."""
+    if getattr(inp.shape, "nvfp4", False):
+        wgu = nvfp4_to_f64(inp.w_gate_up[e], inp.gu_scales[e], inp.gu_global[e])
+        wd = nvfp4_to_f64(inp.w_down[e], inp.d_scales[e], inp.d_global[e])
+        return wgu, wd
     if inp.shape.mxfp4:
         wgu = mxfp4_to_f64(inp.w_gate_up[e], inp.gu_scales[e])
         wd = mxfp4_to_f64(inp.w_down[e], inp.d_scales[e])

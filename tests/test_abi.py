@@ -50,7 +50,7 @@ def S(T=16, H=256, E=8, k=2, I=128, f=0):
 
 @pytest.mark.parametrize("s,expect", [
     (S(T=0), -1), (S(H=0), -1), (S(E=0), -1), (S(k=0), -1), (S(I=0), -1), (S(k=9), -1),
-    (S(H=96), -2), (S(I=100), -2), (S(E=2000, k=8), -2), (S(E=64, k=33), -2), (S(f=3), -2),
+    (S(H=96), -2), (S(I=100), -2), (S(E=2000, k=8), -2), (S(E=64, k=33), -2), (S(f=4), -2),
     (S(T=1 << 28, k=8), -2),
 ])
 def test_bad_shapes_rejected_everywhere(lib, s, expect):
@@ -180,3 +180,34 @@ def test_w4a4_argument_checks(lib):
     assert lib.moe_quantize_mx(F, -1, 64, F, F, None) == -1
     assert lib.moe_quantize_mx(MIS, 4, 64, F, F, None) == -1
     assert lib.moe_quantize_mx(None, 0, 64, None, None, None) == 0     # nothing to do
+
+
+def test_nvfp4_argument_checks(lib):
+    s = S(f=3)
+    b = ctypes.byref(s)
+    F = FAKE
+    big = 1 << 40
+    # NVFP4 needs a scale buffer, 4-byte aligned (fp32 header, 32-bit scale loads)
+    assert lib.moe_forward(b, F, F, None, F, None, F, F, F, None, None, F, big, None, None) == -1
+    assert lib.moe_forward(b, F, F, None, F, F + 2, F, F, F, None, None, F, big, None, None) == -1
+    assert lib.moe_grouped_gemm_gateup(b, F, F, F, F, F + 2, F, None) == -1
+    assert lib.moe_grouped_gemm_down(b, F, F, F, None, F, None) == -1
+    # codes 4-byte aligned
+    assert lib.moe_forward(b, F, F, None, F + 2, F, F, F, F, None, None, F, big, None, None) == -1
+    # no dense MLP with NVFP4 experts
+    assert lib.moe_forward_shared(b, F, F, None, F, F, F, F, 128, F, F, F, F, F, None, None, F, big, None,
+                                  None) == -2
+    # same workspace as bf16 (the weights are read in place)
+    assert lib.moe_workspace_bytes(b) == lib.moe_workspace_bytes(ctypes.byref(S(f=0)))
+
+
+def test_nvfp4_header_size():
+    text = open(HEADER).read()
+    assert "#define MOE_NVFP4_HEADER_BYTES(E)" in text
+    for E, n in [(1, 256), (8, 256), (64, 256), (65, 512), (128, 512), (1024, 4096)]:
+        assert moe.nvfp4_header_bytes(E) == n
+    import numpy as np
+    buf = moe.nvfp4_scale_buffer(np.array([1.5, -2.0], np.float32), np.arange(6, dtype=np.uint8).reshape(2, 1, 3))
+    assert buf.size == 256 + 6
+    assert buf[:8].view(np.float32).tolist() == [1.5, -2.0]
+    assert (buf[8:256] == 0).all() and buf[256:].tolist() == list(range(6))

@@ -452,3 +452,102 @@ def test_round_to_bf16_matches_torch():
     v = rng.standard_normal(1000) * np.exp(rng.uniform(-20, 20, 1000))
     ref = torch.from_numpy(v).to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
     assert (oracle.round_to_bf16(v) == ref).all()
+
+
+# ------------------------------------------------------------------ NVFP4 (O12)
+def _golden_e4m3():
+    vals = {}
+    for line in open(os.path.join(GOLDEN, "ocp_fp8_e4m3.txt")):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            c, v = line.split()
+            vals[int(c, 16)] = float(v)
+    return vals
+
+
+def test_e4m3_table_matches_published_landmarks_and_torch():
+    t = oracle.e4m3_to_f64(np.arange(256))
+    for c, v in _golden_e4m3().items():
+        assert t[c] == v
+    # torch's float8_e4m3fn decoding (an independent implementation of the
+    # same OCP format) agrees on every finite code; 0x7F and 0xFF are NaN
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    fin = ~np.isnan(ref)
+    assert fin.sum() == 254
+    assert (t[fin] == ref[fin]).all()
+    assert np.isnan(t[~fin]).all()
+    assert np.signbit(t[0x80]) and t[0x80] == 0.0
+
+
+def test_nvfp4_decode_hand_built_row():
+    e2m1 = _golden_e2m1()
+    # one row of K = 32: two 16-element blocks; codes 0..15 in each block
+    codes = np.arange(32, dtype=np.uint8) % 16
+    packed = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
+    scales = np.array([0x38, 0x3C], dtype=np.uint8)      # 1.0 and 1.5
+    v = oracle.nvfp4_to_f64(packed, scales, np.float32(0.25))
+    for i in range(32):
+        s = 1.0 if i < 16 else 1.5
+        assert v[i] == e2m1[i % 16] * s * 0.25
+    # the per-matrix scale is taken as fp32
+    v2 = oracle.nvfp4_to_f64(packed, scales, 0.1)
+    assert v2[2] == e2m1[2] * 1.0 * float(np.float32(0.1))
+    with pytest.raises(ValueError):
+        oracle.nvfp4_to_f64(packed, np.array([0x7F, 0x38], np.uint8), 1.0)
+
+
+def test_nvfp4_element_times_block_scale_is_exact_in_bf16():
+    # every E2M1 value times every finite E4M3 value has at most 6
+    # significant bits and lies inside bf16's normal range: exactly a bf16
+    e2m1 = np.array(sorted(_golden_e2m1().values()))
+    sc = oracle.e4m3_to_f64(np.arange(0x7F))
+    prod = (e2m1[:, None] * sc[None, :]).ravel()
+    assert (oracle.round_to_bf16(prod) == prod).all()
+
+
+def test_nvfp4_quantiser_round_trip_on_grid_values():
+    # weights that are exactly element x block scale x matrix scale, with one
+    # element per block at 6 x block scale, come back unchanged
+    rng = np.random.default_rng(5)
+    rows, K = 6, 64
+    g = 2.0 ** -12            # a power of two keeps every product a bf16 value
+    sc_codes = rng.integers(0x20, 0x60, size=(rows, K // 16))
+    sc = oracle.e4m3_to_f64(sc_codes)
+    e2m1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    el = e2m1[rng.integers(0, 8, size=(rows, K))] * rng.choice([-1.0, 1.0], size=(rows, K))
+    el.reshape(rows, K // 16, 16)[:, :, 0] = 6.0
+    sc[0, 0] = oracle.e4m3_to_f64(np.array([0x7E]))[0]     # the matrix max: 6 * 448 * g
+    w = (el.reshape(rows, K // 16, 16) * sc[..., None]).reshape(rows, K) * g
+    bits = mi.f32_to_bf16_bits(w.astype(np.float32))
+    assert (mi.bf16_bits_to_f32(bits).astype(np.float64) == w).all()
+    packed, s_codes, glob = mi.nvfp4_quantize(bits)
+    assert glob == np.float32(g)
+    back = oracle.nvfp4_to_f64(packed, s_codes, glob)
+    assert (back == w).all()
+
+
+def test_nvfp4_quantiser_error_bound():
+    w = mi.random_bf16((8, 256), sigma=0.02, seed=9)
+    packed, s_codes, glob = mi.nvfp4_quantize(w)
+    deq = oracle.nvfp4_to_f64(packed, s_codes, glob)
+    wf = mi.bf16_bits_to_f32(w).astype(np.float64)
+    step = np.repeat(oracle.e4m3_to_f64(s_codes), 16, axis=1) * float(glob)
+    sat = np.abs(wf) > 6 * step
+    # within half the largest element spacing (2 x block step) of each value
+    assert (np.abs(deq - wf)[~sat] <= step[~sat]).all()
+    # a block's scale is its amax / 6 rounded to E4M3: the saturated excess is
+    # at most the E4M3 rounding (relative 2^-4)
+    assert (np.abs(wf[sat]) <= 6 * step[sat] * (1 + 2.0 ** -4)).all()
+
+
+def test_nvfp4_single_expert_is_a_dense_geglu_ffn_on_decoded_weights():
+    s = mi.Shape(T=5, H=64, E=1, k=1, I=32, nvfp4=True)
+    inp = mi.make(s, seed=4)
+    wgu, wd = oracle.expert_weights(inp, 0)
+    assert wgu.shape == (64, 64) and wd.shape == (64, 32)
+    x = torch.tensor(oracle.bf16_to_f64(inp.x))
+    g = torch.tensor(wgu)
+    h = torch.nn.functional.gelu(x @ g[:32].T, approximate="tanh") * (x @ g[32:].T)
+    ref = (h @ torch.tensor(wd).T).numpy()
+    out = oracle.forward(inp)["out"]
+    assert _rel(out, ref) < 1e-12
