@@ -39,7 +39,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--config", default="decode", help="tiny|decode|prefill|skew|mxfp4|decode_shared|w4a4|nvfp4_decode")
+    p.add_argument("--config", default="decode", help="tiny|decode|prefill|skew|mxfp4|decode_shared|w4a4|mxfp4_decode|nvfp4_decode")
     p.add_argument("--rotate", type=int, default=4, help="device copies of the weights cycled per step")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle timing")
     p.add_argument("--no-cpu-baseline", action="store_true")

@@ -137,9 +137,11 @@ struct GemmTile {
     static constexpr int NB = MX ? 0 : BN / RPD;  // bf16 weight-tile instructions per stage
     static constexpr int A_W = (NA + NW - 1) / NW;   // per wave (upper bound)
     static constexpr int B_W = (NB + NW - 1) / NW;
-    // MXFP4 weights: BN rows x 2 chunks of 16 bytes (64 codes) + 2 scale bytes,
-    // staged through registers.
-    static constexpr int MB_CHUNKS = MX ? BN * 2 : 0;
+    // MXFP4 / NVFP4 weights: BN rows x BK/32 chunks of 16 bytes (BK codes)
+    // plus their block scales (BK/32 E8M0 or BK/16 E4M3 bytes), staged
+    // through registers.
+    static constexpr int CPR = BK / 32;           // 16-byte code chunks per row and step
+    static constexpr int MB_CHUNKS = MX ? BN * CPR : 0;
     static constexpr int MB_PER = MX ? (MB_CHUNKS + NT - 1) / NT : 1;
     static constexpr int MS_PER = MX ? (BN + NT - 1) / NT : 1;
     static constexpr int A_LDS = BM * BK;                      // uint16 per stage
@@ -147,9 +149,9 @@ struct GemmTile {
     static_assert(NW == 4 || NW == 8, "four or eight waves");
     static_assert(MI >= 1 && NI >= 1, "tile too small");
     static_assert(!GEGLU || (NI % 2 == 0), "GEGLU pairs gate and up tiles");
-    static_assert(BK == 32 || BK == 64 || BK == 128, "K step");
+    static_assert(BK == 32 || BK == 64 || BK == 128 || (MX && BK == 256), "K step");
     static_assert(BM % RPD == 0 && BN % RPD == 0, "whole 1 KB load groups");
-    static_assert(!MX || BK == 64, "MXFP4 tiles use K steps of 64");
+    static_assert(!MX || BK == 64 || BK == 256, "4-bit weight tiles use K steps of 64 or 256");
     static_assert(NS >= 2 && NS <= 8, "stages");
     // MXFP4 codes go through registers one step ahead; the wait counts
     // assume at most one DMA step is issued after them.
@@ -160,7 +162,10 @@ struct GemmTile {
     // NVFP4 weights take the MXFP4 route with four E4M3 scales per row and
     // step (blocks of 16), kept in LDS as fp32
     static_assert(!NV_ || (MX && !A4_), "NVFP4 is a variant of the MXFP4 weight path");
-    static constexpr int SS_BYTES = MX ? (NV_ ? 16 * BN : 2 * BN) : 1;
+    static constexpr int SC_BLK = NV_ ? 16 : 32;                 // K values per block scale
+    static constexpr int SC_PER = BK / SC_BLK;                   // scale bytes per row and step
+    static constexpr int SCW = SC_PER >= 4 ? SC_PER / 4 : 1;     // ... in 32-bit words
+    static constexpr int SS_BYTES = MX ? SC_PER * BN : 1;
     // W4A4 block scales of a stage: 8 bytes (blocks 8 kt .. 8 kt + 7) per
     // weight row and per token row, one row per thread.
     static constexpr bool SC_PAIR_M = MI >= 2;   // token rows paired like weight rows
@@ -397,28 +402,38 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
     const char *mb_src[G::MB_PER];
     const uint8_t *ms_src[G::MS_PER];
     u32x4 mb[G::MB_PER];
-    uint32_t ms[G::MS_PER];
+    uint32_t ms[G::MS_PER][G::SCW];
     if (MX) {
 #pragma unroll
         for (int i = 0; i < G::MB_PER; ++i) {
             const int c = (tid + NT * i) % (G::MB_CHUNKS > 0 ? G::MB_CHUNKS : 1);
-            const size_t rid = (size_t)e * g_w_rows + weight_row(c >> 1);
-            mb_src[i] = reinterpret_cast<const char *>(g_w) + rid * (K / 2) + kb / 2 + (c & 1) * 16;
+            const size_t rid = (size_t)e * g_w_rows + weight_row(c / G::CPR);
+            mb_src[i] = reinterpret_cast<const char *>(g_w) + rid * (K / 2) + kb / 2 + (c % G::CPR) * 16;
         }
 #pragma unroll
         for (int i = 0; i < G::MS_PER; ++i) {
             const int v = (tid + NT * i) % BN;
-            constexpr int BLK = NV ? 16 : 32;   // K values per scale
-            ms_src[i] = g_scales + ((size_t)e * g_w_rows + weight_row(v)) * (K / BLK) + kb / BLK;
+            ms_src[i] = g_scales + ((size_t)e * g_w_rows + weight_row(v)) * (K / G::SC_BLK) + kb / G::SC_BLK;
         }
     }
     auto issue_mx = [&](int kt) {
 #pragma unroll
         for (int i = 0; i < G::MB_PER; ++i) mb[i] = *reinterpret_cast<const u32x4 *>(mb_src[i] + kt * (BK / 2));
+        // scale rows are K/32 (E8M0) or K/16 (E4M3) bytes: 2- and 4-byte
+        // aligned for K % 64 == 0
 #pragma unroll
         for (int i = 0; i < G::MS_PER; ++i)
-            ms[i] = NV ? *reinterpret_cast<const uint32_t *>(ms_src[i] + kt * 4)
-                       : *reinterpret_cast<const uint16_t *>(ms_src[i] + kt * 2);
+#pragma unroll
+            for (int w = 0; w < G::SCW; ++w) {
+                const uint8_t *src = ms_src[i] + kt * G::SC_PER + 4 * w;
+                if (NV) {
+                    ms[i][w] = *reinterpret_cast<const uint32_t *>(src);
+                } else {
+                    const uint32_t lo = *reinterpret_cast<const uint16_t *>(src);
+                    ms[i][w] = G::SC_PER >= 4 ? lo | ((uint32_t)*reinterpret_cast<const uint16_t *>(src + 2) << 16)
+                                              : lo;
+                }
+            }
     };
     auto commit_mx = [&](int kt) {
         const int slot = kt % NS;
@@ -427,23 +442,18 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
         for (int i = 0; i < G::MB_PER; ++i) {
             const int c = tid + NT * i;
             if (c < G::MB_CHUNKS) {
-                const int v = c >> 1, half = c & 1;
+                const int v = c / G::CPR, part = c % G::CPR;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) words[(half * 4 + q) * BN + v] = mb[i][q];
+                for (int q = 0; q < 4; ++q) words[(part * 4 + q) * BN + v] = mb[i][q];
             }
         }
 #pragma unroll
         for (int i = 0; i < G::MS_PER; ++i) {
             const int v = tid + NT * i;
-            if (v < BN) {
-                if (NV) {   // the step's four E4M3 block scales, as fp32
-                    float *sf = reinterpret_cast<float *>(Ss[slot]);
+            if (v < BN) {   // the step's block scales, one byte per block: [block][row]
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) sf[q * BN + v] = e4m3_to_f32((ms[i] >> (8 * q)) & 0xFFu);
-                } else {
-                    Ss[slot][v] = (uint8_t)(ms[i] & 0xFFu);
-                    Ss[slot][BN + v] = (uint8_t)(ms[i] >> 8);
-                }
+                for (int b = 0; b < G::SC_PER; ++b)
+                    Ss[slot][b * BN + v] = (uint8_t)((ms[i][b / 4] >> (8 * (b % 4))) & 0xFFu);
             }
         }
     };
@@ -567,17 +577,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
                     // it is exactly a bf16 value (the lane's 8 codes are K
                     // 8 ch .. 8 ch + 7, block 2 kk + lk / 2 of the step)
                     const uint32_t codes = reinterpret_cast<const uint32_t *>(Bs[slot])[ch * BN + r];
-                    const float sc = reinterpret_cast<const float *>(Ss[slot])[(2 * kk + (lk >> 1)) * BN + r];
-                    u32x4 v;
-                    v[0] = bf16x2_scale_exact(
-                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, 1.0f, 0)), sc);
-                    v[1] = bf16x2_scale_exact(
-                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, 1.0f, 1)), sc);
-                    v[2] = bf16x2_scale_exact(
-                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, 1.0f, 2)), sc);
-                    v[3] = bf16x2_scale_exact(
-                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, 1.0f, 3)), sc);
-                    wf[j] = v;
+                    const float sc = e4m3_to_f32(Ss[slot][(2 * kk + (lk >> 1)) * BN + r]);
+                    wf[j] = e2m1x8_times_scale(codes, sc);
                 } else if (MX) {
                     const uint32_t codes = reinterpret_cast<const uint32_t *>(Bs[slot])[ch * BN + r];
                     const float sc = __uint_as_float((uint32_t)Ss[slot][kk * BN + r] << 23);
@@ -785,9 +786,15 @@ static hipError_t launch_sized(const GemmArgs &a, int A, hipStream_t st) {
         // allows it (measured: 2% faster than 128-byte pieces at 2816 x
         // 1408).  Not with a shared group: its K need not be a multiple of
         // 128, and the smaller stages keep four workgroups per CU, so routed
-        // and shared tiles run in one round.
-        if constexpr (!MX)
+        // and shared tiles run in one round.  4-bit weights take 256 K values
+        // per step where K allows it (128-byte pieces of code rows, four
+        // times the bytes in flight of 64-wide steps).
+        if constexpr (!MX) {
             if (a.K % 128 == 0 && a.sh_rows == 0) return launch_cfg<16, 128, 1, 4, MODE, MX, 2, 128>(a, A, st);
+        } else {
+            if (a.K % 256 == 0 && a.sh_rows == 0)
+                return launch_cfg<16, 128, 1, 4, MODE, MX, 2, 256, false, NV>(a, A, st);
+        }
         return launch_cfg<16, 128, 1, 4, MODE, MX, 2, 64, false, NV>(a, A, st);
     }
     if (mean_rows <= 40) return launch_cfg<32, 128, 2, 2, MODE, MX, 2, 64, false, NV>(a, A, st);

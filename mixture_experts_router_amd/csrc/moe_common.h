@@ -42,10 +42,13 @@ __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7
 // conflict-free; XOR with row & 3, (row >> 2) & 3 or none cost 4 extra cycles.
 // Rows of 128 bf16 (256 bytes = 16 chunks): XOR with row & 15 is
 // conflict-free; XOR with row & 7 or (row >> 1) & 7 costs one extra cycle
-// per read, none seven.
+// per read, none seven.  Rows of 256 bf16 (512 bytes, 16-row token tiles of
+// the 4-bit weight path) take the same XOR with row & 15: a fragment read
+// touches 16 rows, whose chunks then fall in 16 different 16-byte slots of
+// every 256 bytes, as for 256-byte rows.
 template <int BK>
 __device__ __forceinline__ int tswz(int row, int chunk) {
-    if constexpr (BK == 128) return chunk ^ (row & 15);
+    if constexpr (BK == 128 || BK == 256) return chunk ^ (row & 15);
     else if constexpr (BK == 64) return chunk ^ (row & 7);
     else return chunk ^ ((row >> 1) & 3);
 }
@@ -91,13 +94,21 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
     return (b & 0x80u) ? -v : v;
 }
 
-// A packed bf16 pair times s, for products that are exactly bf16 values
-// (an E2M1 value times an E4M3 scale): the fp32 products are truncated to
-// their top 16 bits, which loses nothing.
-__device__ __forceinline__ uint32_t bf16x2_scale_exact(uint32_t w, float s) {
-    const float lo = __uint_as_float(w << 16) * s;
-    const float hi = __uint_as_float(w & 0xFFFF0000u) * s;
-    return (__float_as_uint(hi) & 0xFFFF0000u) | (__float_as_uint(lo) >> 16);
+// Eight E2M1 codes (a 32-bit word, the lower K index in the low nibble)
+// times an fp32 factor, as eight bf16 values in K order.  Each code goes to
+// fp32 exactly, is multiplied in fp32 and rounded to bf16; for an E4M3 factor
+// the product has at most 6 significant bits, so the rounding is exact.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+template <int Q>   // codes 2Q and 2Q + 1 (byte Q)
+__device__ __forceinline__ uint32_t e2m1x2_times_scale(uint32_t codes, float s) {
+    const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, Q);
+    const bf16x2_t b = {(__bf16)(v[0] * s), (__bf16)(v[1] * s)};
+    return __builtin_bit_cast(uint32_t, b);
+}
+__device__ __forceinline__ u32x4 e2m1x8_times_scale(uint32_t codes, float s) {
+    return u32x4{e2m1x2_times_scale<0>(codes, s), e2m1x2_times_scale<1>(codes, s),
+                 e2m1x2_times_scale<2>(codes, s), e2m1x2_times_scale<3>(codes, s)};
 }
 
 // 16x16x32 bf16 MFMA with fp32 accumulation.  Operand layout per lane l:

@@ -93,7 +93,8 @@ CONFIGS = {
     "decode_shared": Shape(T=8, H=2816, E=128, k=8, I=704, I_sh=2112),
     # the prefill with MXFP4 experts and MXFP4 activations (W4A4)
     "w4a4": Shape(T=2048, H=2816, E=128, k=8, I=704, mxfp4=True, a4=True),
-    # the decode layer with NVFP4 expert weights (bf16 activations)
+    # the decode layer with MXFP4 / NVFP4 expert weights (bf16 activations)
+    "mxfp4_decode": Shape(T=8, H=2816, E=128, k=8, I=704, mxfp4=True),
     "nvfp4_decode": Shape(T=8, H=2816, E=128, k=8, I=704, nvfp4=True),
 }
 

@@ -22,6 +22,10 @@ SMALL = {
     "ragged": mi.Shape(T=300, H=512, E=16, k=4, I=192),
     "ragged-skew": mi.Shape(T=300, H=512, E=16, k=4, I=192, skew=True),
     "ragged-mxfp4": mi.Shape(T=300, H=512, E=16, k=4, I=192, mxfp4=True),
+    # 16-row tiles: 4-bit gate/up in 256-wide K steps, down (K = 704) in 64-wide ones
+    "decode-like-mxfp4": mi.Shape(T=8, H=768, E=64, k=8, I=704, mxfp4=True),
+    # 16-row tiles with H % 256 != 0: 64-wide steps for both GEMMs
+    "k576-mxfp4": mi.Shape(T=12, H=576, E=16, k=4, I=128, mxfp4=True),
     "one-token": mi.Shape(T=1, H=256, E=8, k=2, I=128),
     "k-equals-E": mi.Shape(T=40, H=256, E=8, k=8, I=128),
     "many-experts": mi.Shape(T=130, H=256, E=300, k=6, I=64),

@@ -136,10 +136,13 @@ def test_down(gpu, T, H, E, k, I, mx):
     assert rel <= REL_L2 and ratio <= 1.0
 
 
-def test_mxfp4_equals_bf16_on_dequantised_weights(gpu):
+@pytest.mark.parametrize("T", [300, 24])
+def test_mxfp4_equals_bf16_on_dequantised_weights(gpu, T):
     """MXFP4 decodes exactly to bf16, so the MXFP4 kernels must reproduce the
-    bf16 kernels fed the decoded weights, bitwise."""
-    T, H, E, k, I = 300, 512, 16, 4, 192
+    bf16 kernels fed the decoded weights, bitwise (T=300: 64-row tiles with
+    64-wide K steps; T=24: 16-row tiles, 4-bit gate/up in 256-wide steps
+    against bf16 in 128-wide steps -- the MFMAs still run in K order)."""
+    H, E, k, I = 512, 16, 4, 192
     inp, ids, counts, offsets, sorted_ids, inv = _setup(T, H, E, k, I, True, seed=5)
     A = T * k
     dq_gu = np.stack([oracle.expert_weights(inp, e)[0] for e in range(E)]).astype(np.float32)
@@ -192,3 +195,40 @@ def test_combine(gpu, T, H, k):
         np.abs(oracle.bf16_to_f64(yb)), inv, wts.astype(np.float64)) + 1e-30
     assert (np.abs(got - ref) <= bound).all()
     assert (dev.bf16_bits(out) == dev.bf16_bits(out2)).all()
+
+
+@pytest.mark.parametrize("T", [300, 24])
+def test_nvfp4_equals_bf16_on_dequantised_weights(gpu, T):
+    """With every expert's fp32 scale 1, NVFP4 weights decode exactly to bf16
+    (E2M1 x E4M3), so the NVFP4 kernels must reproduce the bf16 kernels fed
+    the decoded weights, bitwise."""
+    H, E, k, I = 512, 16, 4, 192
+    inp = mi.make(mi.Shape(T=T, H=H, E=E, k=k, I=I, nvfp4=True), seed=6)
+    ids = _ids_with_ragged_counts(T, E, k, 6)
+    counts, offsets = oracle.counts_offsets(ids, E)
+    sorted_ids, inv = oracle.permutation(ids)
+    A = T * k
+    ones = np.ones(E, dtype=np.float32)
+    dq_gu = np.stack([oracle.nvfp4_to_f64(inp.w_gate_up[e], inp.gu_scales[e], 1.0) for e in range(E)])
+    dq_d = np.stack([oracle.nvfp4_to_f64(inp.w_down[e], inp.d_scales[e], 1.0) for e in range(E)])
+    bits_gu = mi.f32_to_bf16_bits(dq_gu.astype(np.float32))
+    bits_d = mi.f32_to_bf16_bits(dq_d.astype(np.float32))
+    assert (mi.bf16_bits_to_f32(bits_gu) == dq_gu).all() and (mi.bf16_bits_to_f32(bits_d) == dq_d).all()
+    off = torch.from_numpy(offsets).cuda()
+    si = torch.from_numpy(sorted_ids).cuda()
+    x = dev.to_device(inp.x)
+    s_nv = moe.shape(T, H, E, k, I, nvfp4=True)
+    s_bf = moe.shape(T, H, E, k, I)
+    h_nv = torch.empty((A, I), dtype=torch.bfloat16, device="cuda")
+    h_bf = torch.empty_like(h_nv)
+    gpu.gemm_gateup(s_nv, x, si, off, dev.to_device(inp.w_gate_up),
+                    dev.to_device(moe.nvfp4_scale_buffer(ones, inp.gu_scales)), h_nv)
+    gpu.gemm_gateup(s_bf, x, si, off, dev.to_device(bits_gu), None, h_bf)
+    y_nv = torch.empty((A, H), dtype=torch.bfloat16, device="cuda")
+    y_bf = torch.empty_like(y_nv)
+    gpu.gemm_down(s_nv, h_bf, off, dev.to_device(inp.w_down),
+                  dev.to_device(moe.nvfp4_scale_buffer(ones, inp.d_scales)), y_nv)
+    gpu.gemm_down(s_bf, h_bf, off, dev.to_device(bits_d), None, y_bf)
+    torch.cuda.synchronize()
+    assert (dev.bf16_bits(h_nv) == dev.bf16_bits(h_bf)).all()
+    assert (dev.bf16_bits(y_nv) == dev.bf16_bits(y_bf)).all()

@@ -19,6 +19,7 @@ NV = {
     "big-tiles-nv": mi.Shape(T=600, H=512, E=16, k=4, I=320, nvfp4=True),     # 256-row tiles
     "decode-like-nv": mi.Shape(T=8, H=768, E=64, k=8, I=704, nvfp4=True),     # 16-row tiles, the model's I
     "skew-nv": mi.Shape(T=200, H=256, E=16, k=4, I=64, nvfp4=True, skew=True),
+    "k576-nv": mi.Shape(T=12, H=576, E=16, k=4, I=128, nvfp4=True),            # H % 256 != 0
 }
 
 
