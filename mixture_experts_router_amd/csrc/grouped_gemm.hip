@@ -120,7 +120,7 @@ template <int BM, int BN, int WAVES_M, int WAVES_N, int MODE, bool MX, int NS_, 
           bool NV_ = false>
 struct GemmTile {
     static constexpr bool GEGLU = MODE == kGateUp;
-    static constexpr int BK = BK_;                // K per step (32, 64 or 128)
+    static constexpr int BK = BK_;                // K per step (32, 64, 128; 4-bit weights 64 or 256)
     static constexpr int CH = BK / 8;             // 16-byte chunks per tile row
     static constexpr int RPD = 64 / CH;           // tile rows per 1 KB direct-to-LDS load
     static constexpr int KK = BK / 32;            // MFMA K steps per step
@@ -133,17 +133,26 @@ struct GemmTile {
     static constexpr int NI = WN / 16;            // weight-row tiles per wave (MFMA A operand)
     // Direct-to-LDS loads move 1 KB per wave instruction (64 lanes x 16 B):
     // RPD rows of BK bf16.
+    static constexpr int SC_BLK = NV_ ? 16 : 32;                 // 4-bit weights: K values per block scale
+    static constexpr int SC_PER = BK / SC_BLK;                   // scale bytes per row and step
+    // 4-bit weights in 256-wide steps go straight to LDS like the tokens:
+    // code rows of 128 bytes (8 rows per 1 KB load) and their scale bytes
+    // (4 bytes per lane, [row][SC_PER] in LDS).  In 64-wide steps they are
+    // staged through registers.
+    static constexpr bool WDMA = MX && BK == 256;
     static constexpr int NA = BM / RPD;           // token-tile instructions per stage
-    static constexpr int NB = MX ? 0 : BN / RPD;  // bf16 weight-tile instructions per stage
+    static constexpr int NB = MX ? (WDMA ? BN / 8 : 0) : BN / RPD;   // weight-tile instructions per stage
+    static constexpr int NSC = WDMA ? BN * SC_PER / 256 : 0;        // scale instructions per stage
     static constexpr int A_W = (NA + NW - 1) / NW;   // per wave (upper bound)
     static constexpr int B_W = (NB + NW - 1) / NW;
-    // MXFP4 / NVFP4 weights: BN rows x BK/32 chunks of 16 bytes (BK codes)
-    // plus their block scales (BK/32 E8M0 or BK/16 E4M3 bytes), staged
-    // through registers.
+    static constexpr int S_W = (NSC + NW - 1) / NW;
+    // MXFP4 / NVFP4 weights through registers: BN rows x BK/32 chunks of 16
+    // bytes (BK codes) plus their block scales (BK/32 E8M0 or BK/16 E4M3
+    // bytes).
     static constexpr int CPR = BK / 32;           // 16-byte code chunks per row and step
-    static constexpr int MB_CHUNKS = MX ? BN * CPR : 0;
-    static constexpr int MB_PER = MX ? (MB_CHUNKS + NT - 1) / NT : 1;
-    static constexpr int MS_PER = MX ? (BN + NT - 1) / NT : 1;
+    static constexpr int MB_CHUNKS = MX && !WDMA ? BN * CPR : 0;
+    static constexpr int MB_PER = MB_CHUNKS ? (MB_CHUNKS + NT - 1) / NT : 1;
+    static constexpr int MS_PER = MX && !WDMA ? (BN + NT - 1) / NT : 1;
     static constexpr int A_LDS = BM * BK;                      // uint16 per stage
     static constexpr int B_LDS = MX ? BN * BK / 4 : BN * BK;   // uint16 per stage
     static_assert(NW == 4 || NW == 8, "four or eight waves");
@@ -155,16 +164,15 @@ struct GemmTile {
     static_assert(NS >= 2 && NS <= 8, "stages");
     // MXFP4 codes go through registers one step ahead; the wait counts
     // assume at most one DMA step is issued after them.
-    static_assert(!MX || NS <= 3, "MXFP4 pipeline depth");
+    static_assert(!MX || WDMA || NS <= 3, "MXFP4 pipeline depth");
+    static_assert(!WDMA || (BN % 8 == 0 && (BN * SC_PER) % 256 == 0), "whole 4-bit load groups");
     // W4A4: both operands are MXFP4 codes loaded like bf16 tiles (128-byte
     // rows = 256 K values per stage, two 16x16x128 scaled MFMA steps).
     static_assert(!A4_ || (!MX && BK == 64), "W4A4 tiles: code rows of 128 bytes");
     // NVFP4 weights take the MXFP4 route with four E4M3 scales per row and
     // step (blocks of 16), kept in LDS as fp32
     static_assert(!NV_ || (MX && !A4_), "NVFP4 is a variant of the MXFP4 weight path");
-    static constexpr int SC_BLK = NV_ ? 16 : 32;                 // K values per block scale
-    static constexpr int SC_PER = BK / SC_BLK;                   // scale bytes per row and step
-    static constexpr int SCW = SC_PER >= 4 ? SC_PER / 4 : 1;     // ... in 32-bit words
+    static constexpr int SCW = SC_PER >= 4 ? SC_PER / 4 : 1;     // scale bytes per row and step in 32-bit words
     static constexpr int SS_BYTES = MX ? SC_PER * BN : 1;
     // W4A4 block scales of a stage: 8 bytes (blocks 8 kt .. 8 kt + 7) per
     // weight row and per token row, one row per thread.
@@ -220,6 +228,13 @@ __device__ __forceinline__ void dma16(const void *g, const void *lds) {
         asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g), "s"(l) : "memory", "m0");
     else
         asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(l) : "memory", "m0");
+}
+
+// 4-byte direct global->LDS load of one wave: lane l's 4 bytes from `g`
+// land at lds + 4 l (same rules as dma16).
+__device__ __forceinline__ void dma4(const void *g, const void *lds) {
+    const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(l) : "memory", "m0");
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int MODE, bool MX, int NS_, int BK_, bool A4 = false,
@@ -308,7 +323,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
     // W4A4 rows hold K/2 bytes of codes (K/4 16-bit units) and a stage holds
     // 256 K values; a last stage that runs past the row is masked (below).
     const int rowu = A4 ? K / 4 : K;                     // row length in 16-bit units
-    const int KT = A4 ? (K + 255) / 256 : (shared && p.sh_splits > 1 ? min(p.sh_ksplit, K - kb) : K) / BK;
+    // 4-bit weights straight to LDS (256-wide steps) also end with a partial
+    // stage when K is not a multiple of 256.
+    const int KT = A4 || G::WDMA ? (K + 255) / 256
+                                 : (shared && p.sh_splits > 1 ? min(p.sh_ksplit, K - kb) : K) / BK;
 
     // Weight row of tile row v (0 <= v < BN), clamped to a valid row.
     auto weight_row = [&](int v) -> int {
@@ -329,22 +347,54 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
     // past the matrix reads row 0; both only feed outputs never stored.
     const int lr = lane / CH, lc = lane % CH;
     const uint16_t *a_src[A_W];
+    int a_ch[G::WDMA ? A_W : 1];   // 4-bit weight path: the lane's chunk column, clamped per step
 #pragma unroll
     for (int q = 0; q < A_W; ++q) {
         const int g = q * NW + wave;
         const int row = RPD * (g < NA ? g : 0) + lr;
         const int rr = row < rows ? row : 0;
         const size_t src = g_gather ? (size_t)(g_gather[seg + rr] / p.gather_k) : (size_t)(seg + rr);
-        a_src[q] = g_a + src * rowu + kb + (A4 ? 0 : 8 * tswz<BK>(row, lc));
+        if (G::WDMA) {
+            a_src[q] = g_a + src * rowu + kb;
+            a_ch[q] = 8 * tswz<BK>(row, lc);
+        } else {
+            a_src[q] = g_a + src * rowu + kb + (A4 ? 0 : 8 * tswz<BK>(row, lc));
+        }
     }
+    constexpr bool WDMA = G::WDMA;
     const uint16_t *b_src[B_W > 0 ? B_W : 1];
 #pragma unroll
     for (int q = 0; q < B_W; ++q) {
         const int g = q * NW + wave;
-        const int row = RPD * (g < NB ? g : 0) + lr;
-        const size_t rid = (size_t)e * g_w_rows + weight_row(row);
-        b_src[q] = reinterpret_cast<const uint16_t *>(g_w) + rid * rowu + kb + (A4 ? 0 : 8 * tswz<BK>(row, lc));
+        if (WDMA) {   // 8 code rows of 128 bytes: lane l -> row 8 g + l / 8, chunk l % 8 (swizzled by row & 7)
+            const int row = 8 * (g < NB ? g : 0) + (lane >> 3);
+            const size_t rid = (size_t)e * g_w_rows + weight_row(row);
+            b_src[q] = reinterpret_cast<const uint16_t *>(reinterpret_cast<const char *>(g_w) + rid * (K / 2) + kb / 2);
+        } else {
+            const int row = RPD * (g < NB ? g : 0) + lr;
+            const size_t rid = (size_t)e * g_w_rows + weight_row(row);
+            b_src[q] = reinterpret_cast<const uint16_t *>(g_w) + rid * rowu + kb + (A4 ? 0 : 8 * tswz<BK>(row, lc));
+        }
     }
+    // Scale rows of direct-loaded 4-bit weights: SC_PER bytes per row and
+    // step, 4 per lane, 256 / SC_PER rows per load.
+    const uint8_t *s_src[G::S_W > 0 ? G::S_W : 1];
+#pragma unroll
+    for (int q = 0; q < G::S_W; ++q) {
+        constexpr int LPR = G::SC_PER / 4;   // lanes per row
+        const int g = q * NW + wave;
+        const int row = (256 / G::SC_PER) * (g < G::NSC ? g : 0) + lane / LPR;
+        const size_t rid = (size_t)e * g_w_rows + weight_row(row);
+        s_src[q] = g_scales + rid * (K / G::SC_BLK) + kb / G::SC_BLK;
+    }
+    // The lane's logical code chunk (the same in every 8-row group, whose row
+    // & 7 is lane / 8) and scale word.  Past the row's end (the last, partial
+    // stage) the loads re-read the row's last chunk / scale word; those code
+    // chunks are then zeroed in LDS (zero_tail_w), so they multiply as zeros.
+    const int w_ch = (lane & 7) ^ ((lane >> 3) & 7);
+    const int s_word = G::WDMA ? 4 * (lane % (G::SC_PER / 4)) : 0;
+    auto wcol_bytes = [&](int kt) { return min(kt * 128 + 16 * w_ch, K / 2 - 16); };
+    auto scol_bytes = [&](int kt) { return min(kt * G::SC_PER + s_word, K / G::SC_BLK - 4); };
     // W4A4: the lane's 16-byte chunk within a stage (the same for every load
     // group: a group covers 8 rows, so row & 7 == lr), clamped into the row
     // for the last, partial stage.
@@ -361,9 +411,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
 #pragma unroll
         for (int q = 0; q < A_W; ++q) {
             const int g = q * NW + wave;
-            if (g < na_valid)
-                dma16<false>(a_src[q] + col_of(kt), As[slot] + g * 512);
+            if (g < na_valid) {
+                if (G::WDMA)
+                    dma16<false>(a_src[q] + min(kt * BK + a_ch[q], K - 8), As[slot] + g * 512);
+                else
+                    dma16<false>(a_src[q] + col_of(kt), As[slot] + g * 512);
+            }
         }
+        const int bcol = WDMA ? wcol_bytes(kt) / 2 : col_of(kt);   // in 16-bit units
 #pragma unroll
         for (int q = 0; q < B_W; ++q) {
             const int g = q * NW + wave;
@@ -371,10 +426,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
                 // Weights of an expert with one row tile are read once: stream
                 // them past the caches.  Several row tiles re-read them: keep.
                 if (stream)
-                    dma16<true>(b_src[q] + col_of(kt), Bs[slot] + g * 512);
+                    dma16<true>(b_src[q] + bcol, Bs[slot] + g * 512);
                 else
-                    dma16<false>(b_src[q] + col_of(kt), Bs[slot] + g * 512);
+                    dma16<false>(b_src[q] + bcol, Bs[slot] + g * 512);
             }
+        }
+#pragma unroll
+        for (int q = 0; q < G::S_W; ++q) {
+            const int g = q * NW + wave;
+            if (G::NSC % NW == 0 || g < G::NSC) dma4(s_src[q] + scol_bytes(kt), Ss[slot] + g * 256);
         }
     };
 
@@ -398,12 +458,26 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
         }
     };
 
+    // 4-bit weights straight to LDS, last stage of a row whose length is not
+    // a multiple of 256: lanes whose code chunk lies past the row's end zero
+    // it (after their own loads of the stage have landed).
+    auto zero_tail_w = [&](int kt) {
+        if (kt * 256 + 32 * w_ch < K) return;
+        const int slot = kt % NS;
+#pragma unroll
+        for (int q = 0; q < B_W; ++q) {
+            const int g = q * NW + wave;
+            if (NB % NW == 0 || g < NB)
+                *reinterpret_cast<u32x4 *>(Bs[slot] + g * 512 + lane * 8) = u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+
     // ---- MXFP4 weights through registers (one set: committed, then reloaded).
     const char *mb_src[G::MB_PER];
     const uint8_t *ms_src[G::MS_PER];
     u32x4 mb[G::MB_PER];
     uint32_t ms[G::MS_PER][G::SCW];
-    if (MX) {
+    if (MX && !WDMA) {
 #pragma unroll
         for (int i = 0; i < G::MB_PER; ++i) {
             const int c = (tid + NT * i) % (G::MB_CHUNKS > 0 ? G::MB_CHUNKS : 1);
@@ -571,7 +645,25 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
 #pragma unroll
             for (int j = 0; j < NI; ++j) {
                 const int r = wn * WN + j * 16 + lrow;
-                if (MX && NV) {
+                if (WDMA) {
+                    // code row r of the stage: logical chunk kk (32 codes)
+                    // at physical chunk kk ^ (r & 7); the lane's 8 codes are
+                    // bytes 4 lk .. 4 lk + 3 of it; scales [row][SC_PER]
+                    const uint8_t *wrow = reinterpret_cast<const uint8_t *>(Bs[slot]) + r * 128;
+                    const uint32_t codes = *reinterpret_cast<const uint32_t *>(wrow + ((kk ^ (r & 7)) << 4) + 4 * lk);
+                    const uint8_t *srow = Ss[slot] + r * G::SC_PER;
+                    if (NV) {
+                        wf[j] = e2m1x8_times_scale(codes, e4m3_to_f32(srow[2 * kk + (lk >> 1)]));
+                    } else {
+                        const float sc = __uint_as_float((uint32_t)srow[kk] << 23);
+                        u32x4 v;
+                        v[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 0));
+                        v[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 1));
+                        v[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 2));
+                        v[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 3));
+                        wf[j] = v;
+                    }
+                } else if (MX && NV) {
                     // E2M1 -> bf16 at scale 1, then times the block's E4M3
                     // scale: the product has at most 6 significant bits, so
                     // it is exactly a bf16 value (the lane's 8 codes are K
@@ -625,11 +717,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
     for (int q = 0; q < A_W; ++q) dma_per_step += (q * NW + wave < na_valid) ? 1 : 0;
 #pragma unroll
     for (int q = 0; q < B_W; ++q) dma_per_step += (NB % NW == 0 || q * NW + wave < NB) ? 1 : 0;
+#pragma unroll
+    for (int q = 0; q < G::S_W; ++q) dma_per_step += (G::NSC % NW == 0 || q * NW + wave < G::NSC) ? 1 : 0;
     auto wait_for = [&](int kt) {
         const int later = min(NS - 2, KT - 1 - kt);   // steps issued after kt
         wait_vm_lgkm0_rt(later * dma_per_step);
     };
-    if (MX) issue_mx(0);
+    if (MX && !WDMA) issue_mx(0);
     if (A4) {
         load_scales(0);
         store_scales(0);   // published by the first step's barrier
@@ -647,12 +741,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
                 zero_tail(kt);
                 wait_vm_lgkm0<63>();      // the zeroes are in LDS
             }
-            if (MX) {
+            if (WDMA && kt == KT - 1 && (K & 255)) {
+                zero_tail_w(kt);
+                wait_vm_lgkm0<63>();
+            }
+            if (MX && !WDMA) {
                 commit_mx(kt);
                 wait_vm_lgkm0<63>();      // this wave's LDS writes are done
             }
             __builtin_amdgcn_s_barrier();
-            if (MX && kt + 1 < KT) issue_mx(kt + 1);
+            if (MX && !WDMA && kt + 1 < KT) issue_mx(kt + 1);
             // scales of step kt + 1: loaded before the DMA (so in-order
             // counts cover them), stored after this step's MFMAs are issued
             const bool next_sc = A4 && kt + 1 < KT;
@@ -758,8 +856,10 @@ static hipError_t launch_cfg(GemmArgs a, int A, hipStream_t st) {
     long long blocks = (long long)a.n_tiles * ((slots + 7) / 8 * 8);
     a.routed_blocks = (int)blocks;
     // every group's K must be whole steps (the kernel loops K / BK times)
-    if (A4 ? (a.K % 64 != 0 || a.sh_rows > 0)
-           : (a.K % BK != 0 || (MODE != kRouter && a.sh_rows > 0 && (a.sh_K % BK != 0 || a.sh_ksplit % BK != 0))))
+    // (W4A4 and 4-bit weights in 256-wide steps end with a partial stage)
+    constexpr bool PARTIAL = A4 || (MX && BK == 256);
+    if (PARTIAL ? (a.K % 64 != 0 || a.sh_rows > 0)
+                : (a.K % BK != 0 || (MODE != kRouter && a.sh_rows > 0 && (a.sh_K % BK != 0 || a.sh_ksplit % BK != 0))))
         return hipErrorInvalidValue;
     if (MODE != kRouter && a.sh_rows > 0) {
         a.sh_n_tiles = GEGLU ? (a.sh_I + BN / 2 - 1) / (BN / 2) : (a.sh_n_out + BN - 1) / BN;
@@ -787,13 +887,23 @@ static hipError_t launch_sized(const GemmArgs &a, int A, hipStream_t st) {
         // 1408).  Not with a shared group: its K need not be a multiple of
         // 128, and the smaller stages keep four workgroups per CU, so routed
         // and shared tiles run in one round.  4-bit weights take 256 K values
-        // per step where K allows it (128-byte pieces of code rows, four
-        // times the bytes in flight of 64-wide steps).
+        // per step where K allows it: code rows in 128-byte pieces and their
+        // scales go straight to LDS in three stages (two steps in flight;
+        // the register route of 64-wide steps has one step of 32 bytes per
+        // row in flight).
         if constexpr (!MX) {
             if (a.K % 128 == 0 && a.sh_rows == 0) return launch_cfg<16, 128, 1, 4, MODE, MX, 2, 128>(a, A, st);
         } else {
-            if (a.K % 256 == 0 && a.sh_rows == 0)
-                return launch_cfg<16, 128, 1, 4, MODE, MX, 2, 256, false, NV>(a, A, st);
+            // codes 16-byte and scale rows 4-byte aligned for the direct
+            // loads (any K % 64 == 0: a partial last stage is handled).
+            // Rows shorter than 1024 keep the register route: three or fewer
+            // steps never fill the three stages, and the 80 KB of LDS halves
+            // the workgroups per CU (measured, NVFP4 down at K = 704: 30.1
+            // against 24.6 us).
+            const bool aligned = (reinterpret_cast<uintptr_t>(a.w) & 15u) == 0 &&
+                                 (reinterpret_cast<uintptr_t>(a.scales) & 3u) == 0 && (a.K / (NV ? 16 : 32)) % 4 == 0;
+            if (a.sh_rows == 0 && aligned && a.K >= 1024)
+                return launch_cfg<16, 128, 1, 4, MODE, MX, 3, 256, false, NV>(a, A, st);
         }
         return launch_cfg<16, 128, 1, 4, MODE, MX, 2, 64, false, NV>(a, A, st);
     }

@@ -26,6 +26,9 @@ SMALL = {
     "decode-like-mxfp4": mi.Shape(T=8, H=768, E=64, k=8, I=704, mxfp4=True),
     # 16-row tiles with H % 256 != 0: 64-wide steps for both GEMMs
     "k576-mxfp4": mi.Shape(T=12, H=576, E=16, k=4, I=128, mxfp4=True),
+    # 16-row gate/up tiles with 256-wide steps and a partial last step
+    # (1152 = 4 x 256 + 128; E8M0 scale rows of 36 bytes)
+    "k1152-mxfp4": mi.Shape(T=12, H=1152, E=16, k=4, I=128, mxfp4=True),
     "one-token": mi.Shape(T=1, H=256, E=8, k=2, I=128),
     "k-equals-E": mi.Shape(T=40, H=256, E=8, k=8, I=128),
     "many-experts": mi.Shape(T=130, H=256, E=300, k=6, I=64),

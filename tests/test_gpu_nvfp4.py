@@ -20,6 +20,9 @@ NV = {
     "decode-like-nv": mi.Shape(T=8, H=768, E=64, k=8, I=704, nvfp4=True),     # 16-row tiles, the model's I
     "skew-nv": mi.Shape(T=200, H=256, E=16, k=4, I=64, nvfp4=True, skew=True),
     "k576-nv": mi.Shape(T=12, H=576, E=16, k=4, I=128, nvfp4=True),            # H % 256 != 0
+    # 16-row gate/up tiles with 256-wide steps straight to LDS and a partial
+    # last step (1088 = 4 x 256 + 64)
+    "k1088-nv": mi.Shape(T=12, H=1088, E=16, k=4, I=128, nvfp4=True),
 }
 
 
