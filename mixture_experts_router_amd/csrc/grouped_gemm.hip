@@ -230,6 +230,23 @@ __device__ __forceinline__ void dma16(const void *g, const void *lds) {
         asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(l) : "memory", "m0");
 }
 
+// Epilogue exchange between lanes l and l ^ 16 (k groups lk and lk ^ 1, which
+// hold columns 4 lk .. 4 lk + 3 of the same output row): a lane of an even
+// group keeps fragment 0's four values and receives its partner's, a lane of
+// an odd group receives the partner's fragment-1 values and keeps its own,
+// so each lane ends with 8 consecutive columns of one fragment.
+__device__ __forceinline__ uint4 pair_swap16(uint2 f0, uint2 f1, int odd) {
+    const uint2 keep = odd ? f1 : f0, send = odd ? f0 : f1;
+    // v_permlane16_swap exchanges the odd 16-lane rows of its first operand
+    // with the even rows of its second: with both operands the same value,
+    // an even row finds its partner's value in the second result, an odd
+    // row in the first
+    const auto rx = __builtin_amdgcn_permlane16_swap(send.x, send.x, false, false);
+    const auto ry = __builtin_amdgcn_permlane16_swap(send.y, send.y, false, false);
+    const uint2 recv = odd ? make_uint2(rx[0], ry[0]) : make_uint2(rx[1], ry[1]);
+    return odd ? make_uint4(recv.x, recv.y, keep.x, keep.y) : make_uint4(keep.x, keep.y, recv.x, recv.y);
+}
+
 // 4-byte direct global->LDS load of one wave: lane l's 4 bytes from `g`
 // land at lds + 4 l (same rules as dma16).
 __device__ __forceinline__ void dma4(const void *g, const void *lds) {
@@ -792,6 +809,31 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
                         lrow_out[n] = (float)(acc64[j][i][q] + b);
                     }
                 }
+        } else if (GEGLU && (NI / 2) % 2 == 0) {
+            // pairs of adjacent 16-column fragments: lanes l and l ^ 16 (k
+            // groups lk and lk ^ 1) swap half their values so that each lane
+            // stores 8 consecutive bf16 (16 bytes) and a row gets 64
+            // contiguous bytes per store instruction
+            constexpr int HALF_T = NI / 2;
+#pragma unroll
+            for (int j = 0; j < HALF_T; j += 2) {
+                const int n0 = nt * (BN / 2) + wn * (WN / 2) + j * 16;
+                uint2 p[2];
+#pragma unroll
+                for (int d = 0; d < 2; ++d) {
+                    f32x4 g = acc[j + d][i], u = acc[j + d + HALF_T][i];
+                    if (NV) {
+                        g *= gsc;
+                        u *= gsc;
+                    }
+                    p[d].x = pack_bf16x2(gelu_tanh(g[0]) * u[0], gelu_tanh(g[1]) * u[1]);
+                    p[d].y = pack_bf16x2(gelu_tanh(g[2]) * u[2], gelu_tanh(g[3]) * u[3]);
+                }
+                const int odd = lk & 1;
+                const uint4 o = pair_swap16(p[0], p[1], odd);
+                const int n = n0 + odd * 16 + 4 * (lk & ~1);
+                if (n < g_I) *reinterpret_cast<uint4 *>(orow + n) = o;
+            }
         } else if (GEGLU) {
             constexpr int HALF_T = NI / 2;
 #pragma unroll
@@ -815,6 +857,22 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
                 const int n = nt * BN + wn * WN + j * 16 + 4 * lk;
                 if (n >= g_n_out) continue;
                 *reinterpret_cast<f32x4 *>(prow + n) = acc[j][i];
+            }
+        } else if (NI % 2 == 0) {
+#pragma unroll
+            for (int j = 0; j < NI; j += 2) {   // fragment pairs, 16 bytes per lane (as above)
+                uint2 pr[2];
+#pragma unroll
+                for (int d = 0; d < 2; ++d) {
+                    f32x4 v = acc[j + d][i];
+                    if (NV) v *= gsc;
+                    pr[d].x = pack_bf16x2(v[0], v[1]);
+                    pr[d].y = pack_bf16x2(v[2], v[3]);
+                }
+                const int odd = lk & 1;
+                const uint4 o = pair_swap16(pr[0], pr[1], odd);
+                const int n = nt * BN + wn * WN + (j + odd) * 16 + 4 * (lk & ~1);
+                if (n < g_n_out) *reinterpret_cast<uint4 *>(orow + n) = o;
             }
         } else {
 #pragma unroll
