@@ -221,6 +221,12 @@ __device__ __forceinline__ void wait_vm_lgkm0_rt(int n) {
 // bandwidth (measured: 6.8 vs 6.1 TB/s for a 2 GiB read).  Data that other
 // workgroups re-read, or lines consumed in pieces over several K steps (the
 // 32-byte MXFP4 row slices), lose more from the early eviction than they gain.
+// The compiler reserves M0 and ignores it in a clobber list (it warns so);
+// nothing it generates in these kernels keeps a value in M0 (no LDS-DMA,
+// GWS, message or relative-move builtins are used), so setting it inside
+// the asm is safe, and the warning is silenced for these two helpers.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 template <bool STREAM>
 __device__ __forceinline__ void dma16(const void *g, const void *lds) {
     const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
@@ -253,6 +259,7 @@ __device__ __forceinline__ void dma4(const void *g, const void *lds) {
     const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(l) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int MODE, bool MX, int NS_, int BK_, bool A4 = false,
           bool NV = false>
@@ -398,7 +405,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
     const uint8_t *s_src[G::S_W > 0 ? G::S_W : 1];
 #pragma unroll
     for (int q = 0; q < G::S_W; ++q) {
-        constexpr int LPR = G::SC_PER / 4;   // lanes per row
+        constexpr int LPR = G::SC_PER >= 4 ? G::SC_PER / 4 : 1;   // lanes per row (used with SC_PER >= 4)
         const int g = q * NW + wave;
         const int row = (256 / G::SC_PER) * (g < G::NSC ? g : 0) + lane / LPR;
         const size_t rid = (size_t)e * g_w_rows + weight_row(row);
@@ -409,7 +416,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
     // stage) the loads re-read the row's last chunk / scale word; those code
     // chunks are then zeroed in LDS (zero_tail_w), so they multiply as zeros.
     const int w_ch = (lane & 7) ^ ((lane >> 3) & 7);
-    const int s_word = G::WDMA ? 4 * (lane % (G::SC_PER / 4)) : 0;
+    const int s_word = G::WDMA ? 4 * (lane % (G::SC_PER >= 4 ? G::SC_PER / 4 : 1)) : 0;
     auto wcol_bytes = [&](int kt) { return min(kt * 128 + 16 * w_ch, K / 2 - 16); };
     auto scol_bytes = [&](int kt) { return min(kt * G::SC_PER + s_word, K / G::SC_BLK - 4); };
     // W4A4: the lane's 16-byte chunk within a stage (the same for every load
