@@ -325,6 +325,10 @@ def main():
         "hbm_frac": alg["layer_bytes"] / t_layer / (HBM_PEAK_GBS * 1e9),
         "mfma_frac": alg["layer_flops"] / t_layer / (mfma_peak * 1e12),
     }
+    # t_roof / t with t_roof = max(F / peak, B / bandwidth): the layer against
+    # whichever roofline binds it
+    layer["binding_frac"] = max(layer["hbm_frac"], layer["mfma_frac"])
+    layer["binding"] = "hbm" if layer["hbm_frac"] >= layer["mfma_frac"] else "mfma"
     res = {
         "metric": METRIC,
         "value": tokens_per_s,
