@@ -99,7 +99,20 @@ def _sample_tokens(ids, T, n, seed):
 def test_forward_full_size(gpu, name):
     s = mi.CONFIGS[name]
     say(f"forward full size {name}: {s}")
-    inp = mi.make(name, seed=0)
+    _full_size_check(mi.make(name, seed=0), name)
+
+
+def test_forward_32k_tokens(gpu):
+    """The model's layer on 32 768 tokens with the skewed router bias:
+    262 144 assignments (16 permutation blocks of 1024 at the hot expert
+    alone), hot experts spanning dozens of 256-row tiles."""
+    s = mi.Shape(T=32768, H=2816, E=128, k=8, I=704, skew=True)
+    say(f"forward 32k tokens: {s}")
+    _full_size_check(mi.make(s, seed=3), "32k-skew")
+
+
+def _full_size_check(inp, name):
+    s = inp.shape
     out, ids, w = run_forward(inp)
     ids_np, w_np = ids.cpu().numpy(), w.cpu().numpy()
     # whole routing table against fp64 routing
