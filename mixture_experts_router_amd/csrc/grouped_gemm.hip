@@ -169,8 +169,8 @@ struct GemmTile {
     // W4A4: both operands are MXFP4 codes loaded like bf16 tiles (128-byte
     // rows = 256 K values per stage, two 16x16x128 scaled MFMA steps).
     static_assert(!A4_ || (!MX && BK == 64), "W4A4 tiles: code rows of 128 bytes");
-    // NVFP4 weights take the MXFP4 route with four E4M3 scales per row and
-    // step (blocks of 16), kept in LDS as fp32
+    // NVFP4 weights take the MXFP4 route with an E4M3 scale per 16 K values
+    // (kept in LDS as bytes, decoded where a fragment uses it)
     static_assert(!NV_ || (MX && !A4_), "NVFP4 is a variant of the MXFP4 weight path");
     static constexpr int SCW = SC_PER >= 4 ? SC_PER / 4 : 1;     // scale bytes per row and step in 32-bit words
     static constexpr int SS_BYTES = MX ? SC_PER * BN : 1;
@@ -271,8 +271,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
     constexpr int NA = G::NA, NB = G::NB, A_W = G::A_W, B_W = G::B_W, NW = G::NW, NT = G::NT;
 
     // bf16 tiles: [row][8 chunks of 16 B], chunk index XOR-swizzled by row.
-    // MXFP4 codes: [chunk (8 words of 4 B)][row]; scales: [2 blocks][row]
-    // (NVFP4: fp32 [4 blocks][row]).
+    // 4-bit weights through registers: codes [word of 8 codes][row], scale
+    // bytes [block][row]; straight to LDS: codes [row][8 chunks of 16 B]
+    // (XOR-swizzled by row & 7), scale bytes [row][block].
     __shared__ __attribute__((aligned(1024))) uint16_t As[NS][G::A_LDS];
     __shared__ __attribute__((aligned(1024))) uint16_t Bs[NS][G::B_LDS];
     __shared__ __attribute__((aligned(16))) uint8_t Ss[NS][G::SS_BYTES];
