@@ -11,26 +11,29 @@
 // grouped matmul of the pages (SwiftGMM, Pangu Pro MoE summary article,
 // group 4) is prior art only.
 //
-// Workgroup = 4 waves = WAVES_M (token direction) x WAVES_N (weight-row
-// direction); tile BM tokens x BN weight rows, K in steps of 64.  Two K steps
-// are in flight per workgroup: while the waves multiply step kt out of LDS,
-// the registers hold step kt+1 (landing) and the loads of step kt+2 are
-// issued.  The MFMA takes the weight tile as its A operand and the tokens as
-// B, so each lane ends with four consecutive output columns of one token and
-// stores them as one 8-byte word.
+// Workgroup = 4 or 8 waves = WAVES_M (token direction) x WAVES_N (weight-row
+// direction); tile BM tokens x BN weight rows, K in steps of BK.  Operand
+// tiles go straight from global memory into LDS (global_load_lds_dwordx4,
+// issued from inline asm so that the compiler adds no waits of its own) in
+// an NS-stage ring; each wave waits only for its own loads (explicit vmcnt)
+// and a barrier publishes a stage.  The MFMA takes the weight tile as its A
+// operand and the tokens as B, so each lane ends with four consecutive output
+// columns of one token; the epilogue pairs fragments across lanes (a lane
+// swap) so that a lane stores eight consecutive columns.
 //
 // For gate/up the BN weight rows of a tile are BN/2 gate rows and the BN/2
 // matching up rows, interleaved per wave so that gate column n and up column
 // I + n land in the same lane and register; the GEGLU runs on the fp32
-// accumulators.  MXFP4 weights stay packed in LDS (4 bits per value plus one
-// scale byte per 32) and are expanded to bf16 by the hardware scaled FP4
-// conversion when each fragment is read.
+// accumulators.  4-bit weights (MXFP4, NVFP4) stay packed in LDS and are
+// expanded to exact bf16 when each fragment is read; W4A4 multiplies packed
+// MXFP4 operands on the block-scaled FP4 MFMA.  The few-token router (and the
+// dense router for many tokens) use the same engine.
 //
 // The launch grid is static (one dimension, N tiles x M-tile slots, dealt
-// to the XCDs in groups).  Each workgroup finds its (expert, row block) from the offsets; slots past
-// the last tile exit at once, an empty expert owns no tile (its weights are
-// never read), and waves whose rows all lie past the expert's last row skip
-// their MFMAs.
+// to the XCDs in groups).  Each workgroup finds its (expert, row block) from
+// the offsets; slots past the last tile exit at once, an empty expert owns no
+// tile (its weights are never read), and waves whose rows all lie past the
+// expert's last row skip their MFMAs.
 #include <type_traits>
 
 #include "moe_common.h"
