@@ -26,8 +26,8 @@
 // I + n land in the same lane and register; the GEGLU runs on the fp32
 // accumulators.  4-bit weights (MXFP4, NVFP4) stay packed in LDS and are
 // expanded to exact bf16 when each fragment is read; W4A4 multiplies packed
-// MXFP4 operands on the block-scaled FP4 MFMA.  The few-token router (and the
-// dense router for many tokens) use the same engine.
+// MXFP4 operands on the block-scaled FP4 MFMA.  The router for many tokens
+// runs on the same engine (one dense group, fp32 chunk sums added in fp64).
 //
 // The launch grid is static (one dimension, N tiles x M-tile slots, dealt
 // to the XCDs in groups).  Each workgroup finds its (expert, row block) from
