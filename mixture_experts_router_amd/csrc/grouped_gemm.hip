@@ -120,7 +120,7 @@ __device__ __forceinline__ void find_tile(const int32_t *__restrict__ offsets, i
 enum GemmMode { kDown = 0, kGateUp = 1, kRouter = 2 };
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int MODE, bool MX, int NS_, int BK_, bool A4_ = false,
-          bool NV_ = false>
+          bool NV_ = false, bool WD_ = false>
 struct GemmTile {
     static constexpr bool GEGLU = MODE == kGateUp;
     static constexpr int BK = BK_;                // K per step (32, 64, 128; 4-bit weights 64 or 256)
@@ -140,12 +140,20 @@ struct GemmTile {
     static constexpr int SC_PER = BK / SC_BLK;                   // scale bytes per row and step
     // 4-bit weights in 256-wide steps go straight to LDS like the tokens:
     // code rows of 128 bytes (8 rows per 1 KB load) and their scale bytes
-    // (4 bytes per lane, [row][SC_PER] in LDS).  In 64-wide steps they are
-    // staged through registers.
-    static constexpr bool WDMA = MX && BK == 256;
+    // (4 bytes per lane, [row][SC_PER] in LDS).  With WD_ (MXFP4, 64-wide
+    // steps) the code rows of 32 bytes go straight to LDS too (32 rows per
+    // load) and the tile's block scales, whole rows of K/32 bytes, are read
+    // into LDS once when the tile starts.  Otherwise, in 64-wide steps, they
+    // are staged through registers.
+    static constexpr bool WDMA = MX && (BK == 256 || WD_);
+    static constexpr bool SC_TILE = WDMA && BK == 64;      // scales of the whole K range, per tile
+    static constexpr int SC_ROW = 100;                     // LDS bytes per scale row (K <= 3200)
+    static constexpr int CRB = BK / 2;                     // bytes per code row and step
+    static constexpr int CCH = CRB / 16;                   // 16-byte chunks per code row
+    static constexpr int CROWS = 1024 / CRB;               // code rows per 1 KB load
     static constexpr int NA = BM / RPD;           // token-tile instructions per stage
-    static constexpr int NB = MX ? (WDMA ? BN / 8 : 0) : BN / RPD;   // weight-tile instructions per stage
-    static constexpr int NSC = WDMA ? BN * SC_PER / 256 : 0;        // scale instructions per stage
+    static constexpr int NB = MX ? (WDMA ? BN / CROWS : 0) : BN / RPD;   // weight-tile instructions per stage
+    static constexpr int NSC = WDMA && !SC_TILE ? BN * SC_PER / 256 : 0;   // scale instructions per stage
     static constexpr int A_W = (NA + NW - 1) / NW;   // per wave (upper bound)
     static constexpr int B_W = (NB + NW - 1) / NW;
     static constexpr int S_W = (NSC + NW - 1) / NW;
@@ -168,7 +176,8 @@ struct GemmTile {
     // MXFP4 codes go through registers one step ahead; the wait counts
     // assume at most one DMA step is issued after them.
     static_assert(!MX || WDMA || NS <= 3, "MXFP4 pipeline depth");
-    static_assert(!WDMA || (BN % 8 == 0 && (BN * SC_PER) % 256 == 0), "whole 4-bit load groups");
+    static_assert(!WDMA || (BN % CROWS == 0 && (SC_TILE || (BN * SC_PER) % 256 == 0)), "whole 4-bit load groups");
+    static_assert(!WD_ || (MX && !NV_ && BK == 64), "per-tile scales: MXFP4 in 64-wide steps");
     // W4A4: both operands are MXFP4 codes loaded like bf16 tiles (128-byte
     // rows = 256 K values per stage, two 16x16x128 scaled MFMA steps).
     static_assert(!A4_ || (!MX && BK == 64), "W4A4 tiles: code rows of 128 bytes");
@@ -176,7 +185,8 @@ struct GemmTile {
     // (kept in LDS as bytes, decoded where a fragment uses it)
     static_assert(!NV_ || (MX && !A4_), "NVFP4 is a variant of the MXFP4 weight path");
     static constexpr int SCW = SC_PER >= 4 ? SC_PER / 4 : 1;     // scale bytes per row and step in 32-bit words
-    static constexpr int SS_BYTES = MX ? SC_PER * BN : 1;
+    static constexpr int SS_BYTES = SC_TILE ? SC_ROW * BN : MX ? SC_PER * BN : 1;
+    static constexpr int SS_SLOTS = SC_TILE ? 1 : NS;   // per-tile scales: one buffer
     // W4A4 block scales of a stage: 8 bytes (blocks 8 kt .. 8 kt + 7) per
     // weight row and per token row, one row per thread.
     static constexpr bool SC_PAIR_M = MI >= 2;   // token rows paired like weight rows
@@ -265,9 +275,9 @@ __device__ __forceinline__ void dma4(const void *g, const void *lds) {
 #pragma clang diagnostic pop
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int MODE, bool MX, int NS_, int BK_, bool A4 = false,
-          bool NV = false>
+          bool NV = false, bool WD = false>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(GemmArgs p) {
-    using G = GemmTile<BM, BN, WAVES_M, WAVES_N, MODE, MX, NS_, BK_, A4, NV>;
+    using G = GemmTile<BM, BN, WAVES_M, WAVES_N, MODE, MX, NS_, BK_, A4, NV, WD>;
     constexpr bool GEGLU = MODE == kGateUp, ROUTER = MODE == kRouter;
     constexpr int BK = G::BK, NS = G::NS, WTM = G::WTM, WN = G::WN, MI = G::MI, NI = G::NI;
     constexpr int CH = G::CH, RPD = G::RPD, KK = G::KK;
@@ -275,11 +285,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
 
     // bf16 tiles: [row][8 chunks of 16 B], chunk index XOR-swizzled by row.
     // 4-bit weights through registers: codes [word of 8 codes][row], scale
-    // bytes [block][row]; straight to LDS: codes [row][8 chunks of 16 B]
-    // (XOR-swizzled by row & 7), scale bytes [row][block].
+    // bytes [block][row]; straight to LDS in 256-wide steps: codes [row][8
+    // chunks of 16 B] (XOR-swizzled by row & 7), scale bytes [row][block];
+    // in 64-wide steps: codes [row][2 chunks] (XOR-swizzled by (row >> 3) &
+    // 1), scale bytes of the whole K range [row][SC_ROW].
     __shared__ __attribute__((aligned(1024))) uint16_t As[NS][G::A_LDS];
     __shared__ __attribute__((aligned(1024))) uint16_t Bs[NS][G::B_LDS];
-    __shared__ __attribute__((aligned(16))) uint8_t Ss[NS][G::SS_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t Ss[G::SS_SLOTS][G::SS_BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t Sc[NS][A4 ? G::SC_BYTES : 1];
     __shared__ int s_info[4];
 
@@ -353,8 +365,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
     const int rowu = A4 ? K / 4 : K;                     // row length in 16-bit units
     // 4-bit weights straight to LDS (256-wide steps) also end with a partial
     // stage when K is not a multiple of 256.
-    const int KT = A4 || G::WDMA ? (K + 255) / 256
-                                 : (shared && p.sh_splits > 1 ? min(p.sh_ksplit, K - kb) : K) / BK;
+    const int KT = A4 || (G::WDMA && BK == 256) ? (K + 255) / 256
+                                                : (shared && p.sh_splits > 1 ? min(p.sh_ksplit, K - kb) : K) / BK;
 
     // Weight row of tile row v (0 <= v < BN), clamped to a valid row.
     auto weight_row = [&](int v) -> int {
@@ -394,8 +406,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
 #pragma unroll
     for (int q = 0; q < B_W; ++q) {
         const int g = q * NW + wave;
-        if (WDMA) {   // 8 code rows of 128 bytes: lane l -> row 8 g + l / 8, chunk l % 8 (swizzled by row & 7)
-            const int row = 8 * (g < NB ? g : 0) + (lane >> 3);
+        if (WDMA) {   // CROWS code rows of CRB bytes: lane l -> row CROWS g + l / CCH, chunk l % CCH (swizzled)
+            const int row = G::CROWS * (g < NB ? g : 0) + lane / G::CCH;
             const size_t rid = (size_t)e * g_w_rows + weight_row(row);
             b_src[q] = reinterpret_cast<const uint16_t *>(reinterpret_cast<const char *>(g_w) + rid * (K / 2) + kb / 2);
         } else {
@@ -415,13 +427,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
         const size_t rid = (size_t)e * g_w_rows + weight_row(row);
         s_src[q] = g_scales + rid * (K / G::SC_BLK) + kb / G::SC_BLK;
     }
-    // The lane's logical code chunk (the same in every 8-row group, whose row
-    // & 7 is lane / 8) and scale word.  Past the row's end (the last, partial
-    // stage) the loads re-read the row's last chunk / scale word; those code
-    // chunks are then zeroed in LDS (zero_tail_w), so they multiply as zeros.
-    const int w_ch = (lane & 7) ^ ((lane >> 3) & 7);
+    // The lane's logical code chunk (the same in every load group: 128-byte
+    // rows, 8 to a group, XOR row & 7, which is lane / 8; 32-byte rows, 32
+    // to a group, XOR (row >> 3) & 1, which is (lane >> 4) & 1) and scale
+    // word.  Past the row's end (the last, partial stage of 256-wide steps)
+    // the loads re-read the row's last chunk / scale word; those code chunks
+    // are then zeroed in LDS (zero_tail_w), so they multiply as zeros.
+    const int w_ch = G::CCH == 8 ? (lane & 7) ^ ((lane >> 3) & 7) : (lane & 1) ^ ((lane >> 4) & 1);
     const int s_word = G::WDMA ? 4 * (lane % (G::SC_PER >= 4 ? G::SC_PER / 4 : 1)) : 0;
-    auto wcol_bytes = [&](int kt) { return min(kt * 128 + 16 * w_ch, K / 2 - 16); };
+    auto wcol_bytes = [&](int kt) { return min(kt * G::CRB + 16 * w_ch, K / 2 - 16); };
     auto scol_bytes = [&](int kt) { return min(kt * G::SC_PER + s_word, K / G::SC_BLK - 4); };
     // W4A4: the lane's 16-byte chunk within a stage (the same for every load
     // group: a group covers 8 rows, so row & 7 == lr), clamped into the row
@@ -675,11 +689,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
                 const int r = wn * WN + j * 16 + lrow;
                 if (WDMA) {
                     // code row r of the stage: logical chunk kk (32 codes)
-                    // at physical chunk kk ^ (r & 7); the lane's 8 codes are
-                    // bytes 4 lk .. 4 lk + 3 of it; scales [row][SC_PER]
-                    const uint8_t *wrow = reinterpret_cast<const uint8_t *>(Bs[slot]) + r * 128;
-                    const uint32_t codes = *reinterpret_cast<const uint32_t *>(wrow + ((kk ^ (r & 7)) << 4) + 4 * lk);
-                    const uint8_t *srow = Ss[slot] + r * G::SC_PER;
+                    // at physical chunk kk ^ (r & 7) (128-byte rows) or kk ^
+                    // ((r >> 3) & 1) (32-byte rows); the lane's 8 codes are
+                    // bytes 4 lk .. 4 lk + 3 of it; scales [row][SC_PER] of
+                    // the stage, or the tile's [row][SC_ROW] from block 2 kt
+                    const uint8_t *wrow = reinterpret_cast<const uint8_t *>(Bs[slot]) + r * G::CRB;
+                    const int pch = G::CCH == 8 ? kk ^ (r & 7) : kk ^ ((r >> 3) & 1);
+                    const uint32_t codes = *reinterpret_cast<const uint32_t *>(wrow + (pch << 4) + 4 * lk);
+                    const uint8_t *srow = G::SC_TILE ? Ss[0] + r * G::SC_ROW + 2 * kt : Ss[slot] + r * G::SC_PER;
                     if (NV) {
                         wf[j] = e2m1x8_times_scale(codes, e4m3_to_f32(srow[2 * kk + (lk >> 1)]));
                     } else {
@@ -759,6 +776,27 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
 #pragma unroll
     for (int s0 = 0; s0 < NS - 1; ++s0)
         if (s0 < KT) issue_dma(s0);
+    // Per-tile block scales (4-bit codes straight to LDS in 64-wide steps):
+    // the tile's whole scale rows, K/32 bytes each, read into LDS once,
+    // NT/BN threads per row, in 16-bit words.  They are issued after the
+    // first stages' loads so that the latencies overlap; the compiler's own
+    // wait before the LDS stores then also covers those stages, which the
+    // first step waits for anyway, so the pipeline's counts stay exact.
+    if constexpr (G::SC_TILE) {
+        constexpr int TPR = NT / BN, MAXW = (G::SC_ROW / 2 + TPR - 1) / TPR;
+        static_assert(NT % BN == 0, "whole threads per scale row");
+        const int v = tid % BN, w0 = tid / BN, nh = K / 64;
+        const uint16_t *srow = reinterpret_cast<const uint16_t *>(
+            g_scales + ((size_t)e * g_w_rows + weight_row(v)) * (size_t)(K / 32));
+        uint16_t sv[MAXW];
+#pragma unroll
+        for (int i = 0; i < MAXW; ++i)
+            if (TPR * i < nh) sv[i] = srow[min(w0 + TPR * i, nh - 1)];
+        uint16_t *dst = reinterpret_cast<uint16_t *>(Ss[0] + v * G::SC_ROW);
+#pragma unroll
+        for (int i = 0; i < MAXW; ++i)
+            if (w0 + TPR * i < nh) dst[w0 + TPR * i] = sv[i];
+    }
     // The loop is instantiated twice so that the accumulators are never live
     // across a branch: waves with rows multiply, the others only load.
     auto run = [&](auto mul_c) {
@@ -769,7 +807,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
                 zero_tail(kt);
                 wait_vm_lgkm0<63>();      // the zeroes are in LDS
             }
-            if (WDMA && kt == KT - 1 && (K & 255)) {
+            if (WDMA && BK == 256 && kt == KT - 1 && (K & 255)) {
                 zero_tail_w(kt);
                 wait_vm_lgkm0<63>();
             }
@@ -908,7 +946,8 @@ static int mtile_slots(int A, int E, int BM) {
     return (int)(((long long)A + (long long)(BM - 1) * ne) / BM);
 }
 
-template <int BM, int BN, int WM, int WN, int MODE, bool MX, int NS, int BK, bool A4 = false, bool NV = false>
+template <int BM, int BN, int WM, int WN, int MODE, bool MX, int NS, int BK, bool A4 = false, bool NV = false,
+          bool WD = false>
 static hipError_t launch_cfg(GemmArgs a, int A, hipStream_t st) {
     constexpr bool GEGLU = MODE == kGateUp;
     const int ncols = GEGLU ? a.I : a.n_out;
@@ -935,7 +974,8 @@ static hipError_t launch_cfg(GemmArgs a, int A, hipStream_t st) {
         blocks += (long long)a.sh_n_tiles * ((a.sh_rows + BM - 1) / BM) * max(1, a.sh_splits);
     }
     if (blocks == 0) return hipSuccess;
-    grouped_gemm_kernel<BM, BN, WM, WN, MODE, MX, NS, BK, A4, NV><<<dim3((unsigned)blocks), 64 * WM * WN, 0, st>>>(a);
+    grouped_gemm_kernel<BM, BN, WM, WN, MODE, MX, NS, BK, A4, NV, WD>
+        <<<dim3((unsigned)blocks), 64 * WM * WN, 0, st>>>(a);
     return hipGetLastError();
 }
 
@@ -978,6 +1018,15 @@ static hipError_t launch_sized(const GemmArgs &a, int A, hipStream_t st) {
     }
     if (mean_rows <= 40) return launch_cfg<32, 128, 2, 2, MODE, MX, 2, 64, false, NV>(a, A, st);
     if (mean_rows <= 80) return launch_cfg<64, 128, 2, 2, MODE, MX, 2, 64, false, NV>(a, A, st);
+    if constexpr (MX && !NV) {
+        // MXFP4 codes straight to LDS (16-byte aligned rows of K/2 bytes)
+        // with the tile's scale rows (K/32 bytes, 2-byte aligned, at most
+        // SC_ROW) read into LDS once: no register staging in the K loop.
+        const bool direct = (reinterpret_cast<uintptr_t>(a.w) & 15u) == 0 &&
+                            (reinterpret_cast<uintptr_t>(a.scales) & 1u) == 0 && a.K >= 128 &&
+                            a.K / 32 <= GemmTile<256, 256, 4, 2, MODE, MX, 3, 64, false, false, true>::SC_ROW;
+        if (direct && a.sh_rows == 0) return launch_cfg<256, 256, 4, 2, MODE, MX, 3, 64, false, false, true>(a, A, st);
+    }
     return launch_cfg<256, 256, 4, 2, MODE, MX, MX ? 3 : 2, 64, false, NV>(a, A, st);
 }
 

@@ -136,13 +136,16 @@ def test_down(gpu, T, H, E, k, I, mx):
     assert rel <= REL_L2 and ratio <= 1.0
 
 
-@pytest.mark.parametrize("T", [300, 24])
-def test_mxfp4_equals_bf16_on_dequantised_weights(gpu, T):
+@pytest.mark.parametrize("T,H,I", [(300, 512, 192), (24, 512, 192), (1200, 512, 192), (1200, 2816, 704)])
+def test_mxfp4_equals_bf16_on_dequantised_weights(gpu, T, H, I):
     """MXFP4 decodes exactly to bf16, so the MXFP4 kernels must reproduce the
     bf16 kernels fed the decoded weights, bitwise (T=300: 64-row tiles with
     64-wide K steps; T=24: 16-row tiles, 4-bit gate/up in 256-wide steps
-    against bf16 in 128-wide steps -- the MFMAs still run in K order)."""
-    H, E, k, I = 512, 16, 4, 192
+    against bf16 in 128-wide steps; T=1200: 256-row tiles, 4-bit codes and
+    the tile's scale rows straight to LDS, at K = 512 / 192 and at the
+    Gemma-4 expert shape, K = 2816 / 704 -- the MFMAs still run in K order)."""
+    E, k = 16, 4
+    say(f"mxfp4 vs bf16 T={T} H={H} E={E} k={k} I={I}")
     inp, ids, counts, offsets, sorted_ids, inv = _setup(T, H, E, k, I, True, seed=5)
     A = T * k
     dq_gu = np.stack([oracle.expert_weights(inp, e)[0] for e in range(E)]).astype(np.float32)
