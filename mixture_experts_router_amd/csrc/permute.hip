@@ -6,8 +6,8 @@
 // Deterministic and free of global atomics: each block of kChunk assignments
 // builds its histogram in LDS, one block scans the block histograms, and each
 // block then ranks its assignments in order (wave ballots give the rank
-// among equal experts inside 64 lanes; a running LDS counter per expert
-// carries it across the block's chunks).
+// among equal experts inside 64 lanes; per-wave counts, scanned per expert
+// over the block's waves, carry it across the block).
 #include "moe_common.h"
 #include "moe_launch.h"
 #include "permute_block.h"
@@ -69,16 +69,34 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t *__restrict__ block_
     if (e == 0) offsets[E] = A;
 }
 
-// One wave per block: positions for the block's chunk.
-__global__ __launch_bounds__(64) void scatter_kernel(const int32_t *__restrict__ ids,
-                                                     const int32_t *__restrict__ block_base,
-                                                     int32_t *__restrict__ sorted_ids,
-                                                     int32_t *__restrict__ inv, int A, int E, int nbits) {
-    extern __shared__ int cnt[];
-    for (int e = threadIdx.x; e < E; e += 64) cnt[e] = block_base[(size_t)blockIdx.x * E + e];
+// Positions for one chunk of kChunk assignments, one per thread (16 waves):
+// each wave ranks its 64 assignments among equal experts (ballots) and
+// records its count of each expert (at most 64: one byte); a lane's position
+// is then the block's base for its expert, plus the counts of that expert in
+// the earlier waves, plus its rank.
+constexpr int kScatterWaves = kChunk / 64;
+__global__ __launch_bounds__(kChunk) void scatter_kernel(const int32_t *__restrict__ ids,
+                                                         const int32_t *__restrict__ block_base,
+                                                         int32_t *__restrict__ sorted_ids,
+                                                         int32_t *__restrict__ inv, int A, int E, int nbits) {
+    extern __shared__ uint8_t wc[];   // [kScatterWaves][E] per-wave counts
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    for (int i = tid; i < kScatterWaves * E; i += kChunk) wc[i] = 0;
+    const int a = blockIdx.x * kChunk + tid;
+    const bool valid = a < A;
+    const int e = valid ? ids[a] : 0;
+    const int base = valid ? block_base[(size_t)blockIdx.x * E + e] : 0;
     __syncthreads();
-    const int a0 = blockIdx.x * kChunk;
-    rank_chunk(ids, a0, min(A, a0 + kChunk), cnt, nbits, sorted_ids, inv);
+    const uint64_t m = match_lanes(e, valid, nbits);
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    if (valid && (m >> lane) == 1ull) wc[wave * E + e] = (uint8_t)__popcll(m);   // highest lane of its group
+    __syncthreads();
+    if (valid) {
+        int pos = base + __popcll(m & below);
+        for (int w = 0; w < wave; ++w) pos += wc[w * E + e];
+        sorted_ids[pos] = a;
+        inv[a] = pos;
+    }
 }
 
 // Everything in one block of 1024 threads when A <= kChunk: histogram,
@@ -124,7 +142,7 @@ hipError_t launch_permute(const int32_t *ids, int32_t *counts, int32_t *offsets,
     const int NB = (A + kChunk - 1) / kChunk;
     hist_kernel<<<NB, 256, E * sizeof(int32_t), st>>>(ids, block_hist, A, E);
     scan_kernel<<<1, 1024, 0, st>>>(block_hist, counts, offsets, NB, E, A);
-    scatter_kernel<<<NB, 64, E * sizeof(int32_t), st>>>(ids, block_hist, sorted_ids, inv, A, E, nbits);
+    scatter_kernel<<<NB, kChunk, kScatterWaves * E, st>>>(ids, block_hist, sorted_ids, inv, A, E, nbits);
     return hipGetLastError();
 }
 
