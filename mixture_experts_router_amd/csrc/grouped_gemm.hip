@@ -1108,10 +1108,14 @@ hipError_t launch_down(const uint16_t *h, const int32_t *offsets, const void *w,
 // Router for many tokens: x [T][H] times W_r [E][H]^T as one dense group, 16
 // tokens x 64 experts per workgroup; K steps of 128 where H allows (half
 // the steps of a latency-bound loop: measured 23 -> 18.5 us at 2048 tokens),
-// four stages.
+// four stages.  From 8192 tokens (256 tiles of 32 tokens) the tile is 32
+// tokens x 128 experts in three stages: half the operand bytes per FLOP
+// through the per-CU load path (8192 tokens: 43.6 -> 35.6 us for the
+// routing; at 2048 tokens, 64 such tiles leave most CUs idle: 18 -> 29 us).
 hipError_t launch_router_dense(const uint16_t *x, const uint16_t *wr, const float *bias, float *logits,
                                int T, int H, int E, hipStream_t st) {
     GemmArgs a{x, nullptr, 1, nullptr, wr, nullptr, nullptr, 1, H, E, 0, E, 0, 0, T, logits, bias};
+    if (H % 128 == 0 && T >= 8192) return launch_cfg<32, 128, 2, 2, kRouter, false, 3, 128>(a, T, st);
     if (H % 128 == 0) return launch_cfg<16, 64, 1, 4, kRouter, false, 4, 128>(a, T, st);
     return launch_cfg<16, 64, 1, 4, kRouter, false, 6, 64>(a, T, st);
 }

@@ -73,30 +73,84 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t *__restrict__ block_
 // each wave ranks its 64 assignments among equal experts (ballots) and
 // records its count of each expert (at most 64: one byte); a lane's position
 // is then the block's base for its expert, plus the counts of that expert in
-// the earlier waves, plus its rank.
+// the earlier waves, plus its rank.  base: LDS, [E]; wc: LDS, [16][E].
 constexpr int kScatterWaves = kChunk / 64;
-__global__ __launch_bounds__(kChunk) void scatter_kernel(const int32_t *__restrict__ ids,
-                                                         const int32_t *__restrict__ block_base,
-                                                         int32_t *__restrict__ sorted_ids,
-                                                         int32_t *__restrict__ inv, int A, int E, int nbits) {
-    extern __shared__ uint8_t wc[];   // [kScatterWaves][E] per-wave counts
+__device__ __forceinline__ void scatter_chunk(const int32_t *__restrict__ ids, const int *base, uint8_t *wc,
+                                              int32_t *__restrict__ sorted_ids, int32_t *__restrict__ inv, int A,
+                                              int E, int nbits) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    for (int i = tid; i < kScatterWaves * E; i += kChunk) wc[i] = 0;
     const int a = blockIdx.x * kChunk + tid;
     const bool valid = a < A;
     const int e = valid ? ids[a] : 0;
-    const int base = valid ? block_base[(size_t)blockIdx.x * E + e] : 0;
-    __syncthreads();
     const uint64_t m = match_lanes(e, valid, nbits);
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     if (valid && (m >> lane) == 1ull) wc[wave * E + e] = (uint8_t)__popcll(m);   // highest lane of its group
     __syncthreads();
     if (valid) {
-        int pos = base + __popcll(m & below);
+        int pos = base[e] + __popcll(m & below);
         for (int w = 0; w < wave; ++w) pos += wc[w * E + e];
         sorted_ids[pos] = a;
         inv[a] = pos;
     }
+}
+
+// The scatter after scan_kernel: block_base[b][e] is chunk b's start of
+// expert e.
+__global__ __launch_bounds__(kChunk) void scatter_kernel(const int32_t *__restrict__ ids,
+                                                         const int32_t *__restrict__ block_base,
+                                                         int32_t *__restrict__ sorted_ids,
+                                                         int32_t *__restrict__ inv, int A, int E, int nbits) {
+    extern __shared__ int dyn[];
+    int *base = dyn;                                          // [E]
+    uint8_t *wc = reinterpret_cast<uint8_t *>(dyn + E);       // [16][E]
+    for (int i = threadIdx.x; i < kScatterWaves * E; i += kChunk) wc[i] = 0;
+    for (int x = threadIdx.x; x < E; x += kChunk) base[x] = block_base[(size_t)blockIdx.x * E + x];
+    __syncthreads();
+    scatter_chunk(ids, base, wc, sorted_ids, inv, A, E, nbits);
+}
+
+// Scan and scatter in one launch for at most kScanFuseMaxBlocks chunks: every
+// block sums the chunk histograms per expert itself (chunks before its own
+// give its bases, all chunks the expert totals), scans the totals over the
+// experts, and block 0 writes counts and offsets.  E <= kChunk: one thread
+// per expert.
+constexpr int kScanFuseMaxBlocks = 64;
+__global__ __launch_bounds__(kChunk) void scan_scatter_kernel(const int32_t *__restrict__ ids,
+                                                              const int32_t *__restrict__ block_hist,
+                                                              int32_t *__restrict__ counts,
+                                                              int32_t *__restrict__ offsets,
+                                                              int32_t *__restrict__ sorted_ids,
+                                                              int32_t *__restrict__ inv, int A, int E, int nbits,
+                                                              int NB) {
+    extern __shared__ int dyn[];
+    __shared__ int sh[kChunk];
+    int *base = dyn;                                          // [E]
+    uint8_t *wc = reinterpret_cast<uint8_t *>(dyn + E);       // [16][E]
+    const int x = threadIdx.x;
+    for (int i = x; i < kScatterWaves * E; i += kChunk) wc[i] = 0;
+    int tot = 0, pre = 0;
+    if (x < E) {
+        // all chunk counts of the expert in flight at once (NB <= 64)
+        int c[kScanFuseMaxBlocks];
+#pragma unroll
+        for (int b = 0; b < kScanFuseMaxBlocks; ++b) c[b] = b < NB ? block_hist[(size_t)b * E + x] : 0;
+#pragma unroll
+        for (int b = 0; b < kScanFuseMaxBlocks; ++b) {
+            pre += b < (int)blockIdx.x ? c[b] : 0;
+            tot += c[b];
+        }
+    }
+    const int start = block_exclusive_scan(tot, sh);
+    if (x < E) {
+        base[x] = start + pre;
+        if (blockIdx.x == 0) {
+            counts[x] = tot;
+            offsets[x] = start;
+        }
+    }
+    if (blockIdx.x == 0 && x == 0) offsets[E] = A;
+    __syncthreads();
+    scatter_chunk(ids, base, wc, sorted_ids, inv, A, E, nbits);
 }
 
 // Everything in one block of 1024 threads when A <= kChunk: histogram,
@@ -140,9 +194,15 @@ hipError_t launch_permute(const int32_t *ids, int32_t *counts, int32_t *offsets,
         return hipGetLastError();
     }
     const int NB = (A + kChunk - 1) / kChunk;
+    const size_t lds = E * sizeof(int32_t) + kScatterWaves * E;
     hist_kernel<<<NB, 256, E * sizeof(int32_t), st>>>(ids, block_hist, A, E);
+    if (NB <= kScanFuseMaxBlocks) {
+        scan_scatter_kernel<<<NB, kChunk, lds, st>>>(ids, block_hist, counts, offsets, sorted_ids, inv, A, E, nbits,
+                                                     NB);
+        return hipGetLastError();
+    }
     scan_kernel<<<1, 1024, 0, st>>>(block_hist, counts, offsets, NB, E, A);
-    scatter_kernel<<<NB, kChunk, kScatterWaves * E, st>>>(ids, block_hist, sorted_ids, inv, A, E, nbits);
+    scatter_kernel<<<NB, kChunk, lds, st>>>(ids, block_hist, sorted_ids, inv, A, E, nbits);
     return hipGetLastError();
 }
 

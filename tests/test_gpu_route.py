@@ -107,16 +107,19 @@ def test_router_gemm_and_routing(gpu, T, H, E, skew):
     assert (margin[diff] < 1e-6).all()
 
 
-def test_router_paths_agree_bitwise(gpu):
+@pytest.mark.parametrize("T", [200, 8192])
+def test_router_paths_agree_bitwise(gpu, T):
     """Few tokens go through the split-K router, many through the GEMM
-    engine; both follow one definition of the logit, so the logits of the
+    engine (16-token tiles; from 8192 tokens, 32-token tiles of 128
+    experts); all follow one definition of the logit, so the logits of the
     same token agree bit for bit."""
-    T, H, E = 200, 2816, 128
+    H, E = 2816, 128
+    say(f"router paths T={T}")
     inp = mi.make(mi.Shape(T=T, H=H, E=E, k=8, I=64, skew=True), seed=4)
     x = dev.to_device(inp.x)
     wr = dev.to_device(inp.w_router)
     b = dev.to_device(inp.router_bias)
     L_many, _, _ = _route_x(gpu, moe.shape(T, H, E, 8, 64), x, wr, b)
-    for t0 in (0, 64, 136):
+    for t0 in (0, 64, 136, T - 64):
         L_few, _, _ = _route_x(gpu, moe.shape(64, H, E, 8, 64), x[t0:t0 + 64].contiguous(), wr, b)
         assert (L_few.view(np.uint32) == L_many[t0:t0 + 64].view(np.uint32)).all()
