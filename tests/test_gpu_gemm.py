@@ -53,6 +53,7 @@ CASES = [
     (300, 512, 16, 4, 192),    # mean 75
     (1000, 256, 8, 2, 128),    # mean 250
     (257, 2816, 128, 8, 704),  # Gemma-4 expert shape, mean 16
+    (4096, 512, 128, 8, 256),  # mean 256: 512 down tiles of 256 rows, two rounds per CU
 ]
 
 
