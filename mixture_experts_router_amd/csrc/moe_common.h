@@ -85,14 +85,12 @@ __device__ __forceinline__ f32x4 mfma_fp4x128(const u32x4 &a, const u32x4 &b, f3
 #undef MOE_FP4_CASE
 }
 
-// FP8 E4M3 code -> fp32 (OCP 8-bit floating point: exponent bias 7, three
-// mantissa bits, exponent field 0 subnormal m * 2^-9, no infinities).  The
-// NaN codes S.1111.111 are not valid scales; they decode to +-480.
-__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
-    const uint32_t ef = (b >> 3) & 15u, m = b & 7u;
-    const float v = ef ? __uint_as_float(((ef + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
-    return (b & 0x80u) ? -v : v;
-}
+// FP8 E4M3 code (the low byte of b) -> fp32 (OCP 8-bit floating point:
+// exponent bias 7, three mantissa bits, exponent field 0 subnormal m * 2^-9,
+// no infinities) in one v_cvt_f32_fp8, which on gfx950 decodes the OCP
+// encoding (all 254 finite codes checked bitwise against a host decode).  The
+// NaN codes S.1111.111 are not valid scales; they give NaN.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) { return __builtin_amdgcn_cvt_f32_fp8(b, 0); }
 
 // Eight E2M1 codes (a 32-bit word, the lower K index in the low nibble)
 // times an fp32 factor, as eight bf16 values in K order.  Each code goes to
