@@ -52,9 +52,11 @@ def _check(gpu, ids, E, label, H=0):
         assert (back == x[:, None, :]).all()
 
 
+# (8192, 128, 8): 64 chunks of 1024 assignments, the most the scan runs
+# inside the scatter blocks; (8193, 128, 8): 65 chunks, a scan launch of its own
 @pytest.mark.parametrize("T,E,k", [(1, 8, 2), (8, 128, 8), (16, 8, 2), (128, 128, 8),
                                    (129, 128, 8), (300, 16, 4), (2048, 128, 8), (777, 1000, 3),
-                                   (5000, 1024, 32)])
+                                   (8192, 128, 8), (8193, 128, 8), (5000, 1024, 32)])
 def test_uniform_routing(gpu, T, E, k):
     _check(gpu, mi.random_ids(T, E, k, seed=T + E), E, "uniform")
 
