@@ -100,6 +100,40 @@ def traffic_from_profiles(config):
     return d.get("hbm_bytes_per_launch")
 
 
+def host_info():
+    """Where the numbers were taken: CPU model, BLAS threads, torch and HIP
+    versions, the GPU and its compute units."""
+    import torch
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:                                            # pragma: no cover
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:                                          # pragma: no cover
+        blas = None
+    props = torch.cuda.get_device_properties(0)
+    return {"cpu_model": cpu, "host_cpus": len(os.sched_getaffinity(0)), "blas_threads": blas,
+            "torch": torch.__version__, "hip": torch.version.hip, "gpu": props.name,
+            "arch": getattr(props, "gcnArchName", None), "compute_units": props.multi_processor_count}
+
+
+# The pages' own figures, for context only: whole-model latencies and rates on
+# other hardware, none of them for this layer alone (so vs_baseline is null).
+PAGES_CONTEXT = {
+    "note": "whole-model figures from the pages on other hardware; none measures this layer",
+    "ascend_910b_x8_bs8_seq256_prefill_ms": 312.51,
+    "ascend_910b_x8_bs8_decode_ms": {"eager": 98.47, "after_operator_fusion": 92.0},
+    "llama_cpp_rtx4070_iq3s_generation_tokens_per_s": 48,
+}
+
+
 def cpu_baseline(inp, budget_s):
     """The oracle as it stands, on this host, on a bounded sample."""
     import oracle
@@ -364,6 +398,8 @@ def main():
         "layer": layer,
         "step_us": {"mean_back_to_back": ms * 1e3, "per_step_events": spread, "graph_replay": graph_us},
         "stages_us": stage_avg_us,
+        "host": host_info(),
+        "context": PAGES_CONTEXT,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
