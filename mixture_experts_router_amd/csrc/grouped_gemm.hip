@@ -79,15 +79,19 @@ struct GemmArgs {
     const float *w_global;
 };
 
-// Locate this workgroup's M tile: tile index -> (expert, first row).  Run by
-// one wave; results go to LDS.
+// Locate this workgroup's M tile: tile index -> (expert e, first row m0
+// within the expert, the expert's rows n and its first grouped row off), or
+// e = -1 past the last tile.  Every wave computes it (a wave prefix scan of
+// ceil(n_e / BM) over the experts, 64 at a time); the results are
+// wave-uniform.
+struct TileInfo {
+    int e, m0, n, off;
+};
 template <int BM>
-__device__ __forceinline__ void find_tile(const int32_t *__restrict__ offsets, int E, int tile,
-                                          int *s_info) {
+__device__ __forceinline__ TileInfo find_tile(const int32_t *__restrict__ offsets, int E, int tile) {
     const int lane = threadIdx.x & 63;
     int running = 0;
-    bool found = false;
-    for (int base = 0; base < E && !found; base += 64) {
+    for (int base = 0; base < E; base += 64) {
         const int e = base + lane;
         int n = 0, off = 0;
         if (e < E) {
@@ -104,30 +108,36 @@ __device__ __forceinline__ void find_tile(const int32_t *__restrict__ offsets, i
         const int total = __shfl(incl, 63, 64);
         if (tile < running + total) {
             const int excl = incl - t;
-            if (running + excl <= tile && tile < running + incl) {
-                s_info[0] = e;
-                s_info[1] = (tile - running - excl) * BM;   // first row within the expert
-                s_info[2] = n;
-                s_info[3] = off;
-            }
-            found = true;
+            const uint64_t hit = __ballot(running + excl <= tile && tile < running + incl);
+            const int src = (int)__builtin_ctzll(hit);   // the expert holding the tile
+            TileInfo r;
+            r.e = base + src;
+            r.n = __builtin_amdgcn_readlane(n, src);
+            r.off = __builtin_amdgcn_readlane(off, src);
+            r.m0 = (tile - running - __builtin_amdgcn_readlane(excl, src)) * BM;
+            return r;
         }
         running += total;
     }
-    if (!found && lane == 0) s_info[0] = -1;
+    return TileInfo{-1, 0, 0, 0};
 }
 
 enum GemmMode { kDown = 0, kGateUp = 1, kRouter = 2 };
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int MODE, bool MX, int NS_, int BK_, bool A4_ = false,
-          bool NV_ = false, bool WD_ = false>
+          bool NV_ = false, bool WD_ = false, int NSB_ = 0>
 struct GemmTile {
     static constexpr bool GEGLU = MODE == kGateUp;
     static constexpr int BK = BK_;                // K per step (32, 64, 128; 4-bit weights 64 or 256)
     static constexpr int CH = BK / 8;             // 16-byte chunks per tile row
     static constexpr int RPD = 64 / CH;           // tile rows per 1 KB direct-to-LDS load
     static constexpr int KK = BK / 32;            // MFMA K steps per step
-    static constexpr int NS = NS_;                // LDS stages (NS - 1 loads ahead)
+    static constexpr int NS = NS_;                // LDS stages (NS - 1 loads ahead) of the token tile
+    // Stages of the weight tile: NS, or one more in the bf16 256 x 256 tile
+    // (two token stages and three weight stages fill the 160 KB of LDS): the
+    // weights come from HBM, the token rows mostly from L2, so the weights
+    // are requested one step earlier.
+    static constexpr int NSB = NSB_ ? NSB_ : NS_;
     static constexpr int NW = WAVES_M * WAVES_N;   // waves per workgroup
     static constexpr int NT = 64 * NW;             // threads per workgroup
     static constexpr int WTM = BM / WAVES_M;      // tokens per wave
@@ -185,7 +195,7 @@ struct GemmTile {
     // (kept in LDS as bytes, decoded where a fragment uses it)
     static_assert(!NV_ || (MX && !A4_), "NVFP4 is a variant of the MXFP4 weight path");
     static constexpr int SCW = SC_PER >= 4 ? SC_PER / 4 : 1;     // scale bytes per row and step in 32-bit words
-    static constexpr int SS_BYTES = SC_TILE ? SC_ROW * BN : MX ? SC_PER * BN : 1;
+    static constexpr int SS_BYTES = SC_TILE ? SC_ROW * BN : MX ? SC_PER * BN : 0;
     static constexpr int SS_SLOTS = SC_TILE ? 1 : NS;   // per-tile scales: one buffer
     // W4A4 block scales of a stage: 8 bytes (blocks 8 kt .. 8 kt + 7) per
     // weight row and per token row, one row per thread.
@@ -197,6 +207,15 @@ struct GemmTile {
     // count the direct-to-LDS ones), which only a two-stage pipeline affords
     static_assert(!A4_ || NS == 2, "W4A4: two stages");
     static_assert(!A4_ || (NI % 2 == 0 && (!SC_PAIR_M || MI % 2 == 0)), "W4A4: scale rows in pairs");
+    static_assert(NSB == NS || (NS == 2 && NSB == 3 && !MX && !A4_), "a deeper weight ring: bf16, 2 + 3 stages");
+    // LDS: token stages, weight stages, block scales (4-bit weights), W4A4
+    // scale pairs, carved from one buffer (byte offsets, 16-byte aligned)
+    static constexpr int A_OFF = 0;
+    static constexpr int B_OFF = A_OFF + NS * A_LDS * 2;
+    static constexpr int S_OFF = B_OFF + NSB * B_LDS * 2;
+    static constexpr int C_OFF = S_OFF + ((SS_SLOTS * SS_BYTES + 15) / 16) * 16;
+    static constexpr int LDS_BYTES = C_OFF + (A4_ ? NS * SC_BYTES : 0);
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS of one workgroup");
 };
 
 // s_waitcnt with vmcnt = VM and lgkmcnt = 0 (expcnt left at its maximum).
@@ -275,11 +294,11 @@ __device__ __forceinline__ void dma4(const void *g, const void *lds) {
 #pragma clang diagnostic pop
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int MODE, bool MX, int NS_, int BK_, bool A4 = false,
-          bool NV = false, bool WD = false>
+          bool NV = false, bool WD = false, int NSB_ = 0>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(GemmArgs p) {
-    using G = GemmTile<BM, BN, WAVES_M, WAVES_N, MODE, MX, NS_, BK_, A4, NV, WD>;
+    using G = GemmTile<BM, BN, WAVES_M, WAVES_N, MODE, MX, NS_, BK_, A4, NV, WD, NSB_>;
     constexpr bool GEGLU = MODE == kGateUp, ROUTER = MODE == kRouter;
-    constexpr int BK = G::BK, NS = G::NS, WTM = G::WTM, WN = G::WN, MI = G::MI, NI = G::NI;
+    constexpr int BK = G::BK, NS = G::NS, NSB = G::NSB, WTM = G::WTM, WN = G::WN, MI = G::MI, NI = G::NI;
     constexpr int CH = G::CH, RPD = G::RPD, KK = G::KK;
     constexpr int NA = G::NA, NB = G::NB, A_W = G::A_W, B_W = G::B_W, NW = G::NW, NT = G::NT;
 
@@ -289,11 +308,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
     // chunks of 16 B] (XOR-swizzled by row & 7), scale bytes [row][block];
     // in 64-wide steps: codes [row][2 chunks] (XOR-swizzled by (row >> 3) &
     // 1), scale bytes of the whole K range [row][SC_ROW].
-    __shared__ __attribute__((aligned(1024))) uint16_t As[NS][G::A_LDS];
-    __shared__ __attribute__((aligned(1024))) uint16_t Bs[NS][G::B_LDS];
-    __shared__ __attribute__((aligned(16))) uint8_t Ss[G::SS_SLOTS][G::SS_BYTES];
-    __shared__ __attribute__((aligned(16))) uint8_t Sc[NS][A4 ? G::SC_BYTES : 1];
-    __shared__ int s_info[4];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[G::LDS_BYTES];
+    uint16_t(*As)[G::A_LDS] = reinterpret_cast<uint16_t(*)[G::A_LDS]>(smem + G::A_OFF);   // [NS]
+    uint16_t(*Bs)[G::B_LDS] = reinterpret_cast<uint16_t(*)[G::B_LDS]>(smem + G::B_OFF);   // [NSB]
+    constexpr int SSB = G::SS_BYTES > 0 ? G::SS_BYTES : 1, SCB = A4 ? G::SC_BYTES : 1;
+    uint8_t(*Ss)[SSB] = reinterpret_cast<uint8_t(*)[SSB]>(smem + G::S_OFF);               // [SS_SLOTS]
+    uint8_t(*Sc)[SCB] = reinterpret_cast<uint8_t(*)[SCB]>(smem + G::C_OFF);               // [NS], W4A4
 
     // XCD-aware tile order.  Workgroups go to the 8 XCDs round-robin (block
     // b -> XCD b % 8).  The N tiles of one M tile form a group that shares
@@ -348,14 +368,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
         seg = m0;
         stream = p.sh_rows <= p.stream_max_rows;
     } else {
-        if (wave == 0) find_tile<BM>(p.offsets, p.E, mslot, s_info);
-        __syncthreads();
-        e = __builtin_amdgcn_readfirstlane(s_info[0]);
+        const TileInfo ti = find_tile<BM>(p.offsets, p.E, mslot);
+        e = __builtin_amdgcn_readfirstlane(ti.e);
         if (e < 0) return;
-        m0 = __builtin_amdgcn_readfirstlane(s_info[1]);
-        const int n_e = __builtin_amdgcn_readfirstlane(s_info[2]);
+        m0 = __builtin_amdgcn_readfirstlane(ti.m0);
+        const int n_e = __builtin_amdgcn_readfirstlane(ti.n);
         rows = min(BM, n_e - m0);                                         // valid tokens of this tile
-        seg = __builtin_amdgcn_readfirstlane(s_info[3]) + m0;             // global row of tile token 0
+        seg = __builtin_amdgcn_readfirstlane(ti.off) + m0;                // global row of tile token 0
         stream = n_e <= p.stream_max_rows;
     }
     const int K = shared ? p.sh_K : p.K;                 // row length of both operands
@@ -448,7 +467,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
     // Token-row groups past the tile's last valid row are not loaded (their
     // LDS rows keep stale data that only reaches outputs never stored).
     const int na_valid = (rows + RPD - 1) / RPD;
-    auto issue_dma = [&](int kt) {
+    // Token tile of step kt into stage kt % NS.
+    auto issue_a = [&](int kt) {
         const int slot = kt % NS;
 #pragma unroll
         for (int q = 0; q < A_W; ++q) {
@@ -460,19 +480,26 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
                     dma16<false>(a_src[q] + col_of(kt), As[slot] + g * 512);
             }
         }
+    };
+    // Weight load q of this wave for step kt, into stage kt % NSB.
+    auto issue_bq = [&](int kt, int q) {
+        const int slot = kt % NSB;
         const int bcol = WDMA ? wcol_bytes(kt) / 2 : col_of(kt);   // in 16-bit units
-#pragma unroll
-        for (int q = 0; q < B_W; ++q) {
-            const int g = q * NW + wave;
-            if (NB % NW == 0 || g < NB) {
-                // Weights of an expert with one row tile are read once: stream
-                // them past the caches.  Several row tiles re-read them: keep.
-                if (stream)
-                    dma16<true>(b_src[q] + bcol, Bs[slot] + g * 512);
-                else
-                    dma16<false>(b_src[q] + bcol, Bs[slot] + g * 512);
-            }
+        const int g = q * NW + wave;
+        if (NB % NW == 0 || g < NB) {
+            // Weights of an expert with one row tile are read once: stream
+            // them past the caches.  Several row tiles re-read them: keep.
+            if (stream)
+                dma16<true>(b_src[q] + bcol, Bs[slot] + g * 512);
+            else
+                dma16<false>(b_src[q] + bcol, Bs[slot] + g * 512);
         }
+    };
+    // Weight tile (and block scales) of step kt.
+    auto issue_b = [&](int kt) {
+#pragma unroll
+        for (int q = 0; q < B_W; ++q) issue_bq(kt, q);
+        const int slot = kt % NSB;
 #pragma unroll
         for (int q = 0; q < G::S_W; ++q) {
             const int g = q * NW + wave;
@@ -486,7 +513,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
     // after the wave's own loads of the stage have landed.
     auto zero_tail = [&](int kt) {
         if (kt * 256 + 4 * lane_col < K) return;
-        const int slot = kt % NS;
+        const int slot = kt % NS;   // NSB == NS here
 #pragma unroll
         for (int q = 0; q < A_W; ++q) {
             const int g = q * NW + wave;
@@ -505,7 +532,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
     // it (after their own loads of the stage have landed).
     auto zero_tail_w = [&](int kt) {
         if (kt * 256 + 32 * w_ch < K) return;
-        const int slot = kt % NS;
+        const int slot = kt % NSB;
 #pragma unroll
         for (int q = 0; q < B_W; ++q) {
             const int g = q * NW + wave;
@@ -552,7 +579,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
             }
     };
     auto commit_mx = [&](int kt) {
-        const int slot = kt % NS;
+        const int slot = kt % NSB;   // NSB == NS here
         uint32_t *words = reinterpret_cast<uint32_t *>(Bs[slot]);
 #pragma unroll
         for (int i = 0; i < G::MB_PER; ++i) {
@@ -669,8 +696,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
     // (its partial tile rows are multiplied anyway: their outputs are simply
     // not stored).
     const bool wave_has_rows = wm * WTM < rows;   // scalar condition
-    auto compute = [&](int kt) {
-        const int slot = kt % NS;
+    // Spread weight loads (deeper weight ring, waves with rows): this wave's
+    // B_W weight loads of step kt_b go out one per GAP MFMAs of step kt, so
+    // that the loads never stall a wave for long before its MFMAs; they are
+    // needed two steps later.
+    constexpr bool SPREAD = NSB > NS;
+    constexpr int GAP = (KK * MI * NI) / (B_W > 0 ? B_W : 1) > 0 ? (KK * MI * NI) / (B_W > 0 ? B_W : 1) : 1;
+    auto compute = [&](int kt, int kt_b) {
+        const int slot = kt % NS, wslot = kt % NSB;
         constexpr int NSW = A4 ? NI / 2 : 1, NSX = A4 ? (G::SC_PAIR_M ? MI / 2 : MI) : 1;
         uint32_t sw[NSW], sx[NSX];
         if (A4) {
@@ -693,10 +726,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
                     // ((r >> 3) & 1) (32-byte rows); the lane's 8 codes are
                     // bytes 4 lk .. 4 lk + 3 of it; scales [row][SC_PER] of
                     // the stage, or the tile's [row][SC_ROW] from block 2 kt
-                    const uint8_t *wrow = reinterpret_cast<const uint8_t *>(Bs[slot]) + r * G::CRB;
+                    const uint8_t *wrow = reinterpret_cast<const uint8_t *>(Bs[wslot]) + r * G::CRB;
                     const int pch = G::CCH == 8 ? kk ^ (r & 7) : kk ^ ((r >> 3) & 1);
                     const uint32_t codes = *reinterpret_cast<const uint32_t *>(wrow + (pch << 4) + 4 * lk);
-                    const uint8_t *srow = G::SC_TILE ? Ss[0] + r * G::SC_ROW + 2 * kt : Ss[slot] + r * G::SC_PER;
+                    const uint8_t *srow = G::SC_TILE ? Ss[0] + r * G::SC_ROW + 2 * kt : Ss[wslot] + r * G::SC_PER;
                     if (NV) {
                         wf[j] = e2m1x8_times_scale(codes, e4m3_to_f32(srow[2 * kk + (lk >> 1)]));
                     } else {
@@ -713,12 +746,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
                     // scale: the product has at most 6 significant bits, so
                     // it is exactly a bf16 value (the lane's 8 codes are K
                     // 8 ch .. 8 ch + 7, block 2 kk + lk / 2 of the step)
-                    const uint32_t codes = reinterpret_cast<const uint32_t *>(Bs[slot])[ch * BN + r];
-                    const float sc = e4m3_to_f32(Ss[slot][(2 * kk + (lk >> 1)) * BN + r]);
+                    const uint32_t codes = reinterpret_cast<const uint32_t *>(Bs[wslot])[ch * BN + r];
+                    const float sc = e4m3_to_f32(Ss[wslot][(2 * kk + (lk >> 1)) * BN + r]);
                     wf[j] = e2m1x8_times_scale(codes, sc);
                 } else if (MX) {
-                    const uint32_t codes = reinterpret_cast<const uint32_t *>(Bs[slot])[ch * BN + r];
-                    const float sc = __uint_as_float((uint32_t)Ss[slot][kk * BN + r] << 23);
+                    const uint32_t codes = reinterpret_cast<const uint32_t *>(Bs[wslot])[ch * BN + r];
+                    const float sc = __uint_as_float((uint32_t)Ss[wslot][kk * BN + r] << 23);
                     u32x4 v;
                     v[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 0));
                     v[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 1));
@@ -726,7 +759,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
                     v[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 3));
                     wf[j] = v;
                 } else {
-                    wf[j] = *reinterpret_cast<const u32x4 *>(&Bs[slot][r * BK + tswz<BK>(r, ch) * 8]);
+                    wf[j] = *reinterpret_cast<const u32x4 *>(&Bs[wslot][r * BK + tswz<BK>(r, ch) * 8]);
                 }
             }
 #pragma unroll
@@ -745,7 +778,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
 #pragma unroll
                 for (int i = 0; i < MI; ++i)
 #pragma unroll
-                    for (int j = 0; j < NI; ++j) acc[j][i] = mfma16x16x32(wf[j], xf[i], acc[j][i]);
+                    for (int j = 0; j < NI; ++j) {
+                        acc[j][i] = mfma16x16x32(wf[j], xf[i], acc[j][i]);
+                        if constexpr (SPREAD) {
+                            const int idx = (kk * MI + i) * NI + j;
+                            if (kt_b >= 0 && idx % GAP == GAP - 1 && idx / GAP < B_W) {
+                                __builtin_amdgcn_sched_barrier(0);
+                                issue_bq(kt_b, idx / GAP);
+                                __builtin_amdgcn_sched_barrier(0);
+                            }
+                        }
+                    }
             }
         }
     };
@@ -764,9 +807,26 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
     for (int q = 0; q < B_W; ++q) dma_per_step += (NB % NW == 0 || q * NW + wave < NB) ? 1 : 0;
 #pragma unroll
     for (int q = 0; q < G::S_W; ++q) dma_per_step += (G::NSC % NW == 0 || q * NW + wave < G::NSC) ? 1 : 0;
+    // This wave's weight (and scale) loads per step.
+    int dmab_per_step = 0;
+#pragma unroll
+    for (int q = 0; q < B_W; ++q) dmab_per_step += (NB % NW == 0 || q * NW + wave < NB) ? 1 : 0;
+#pragma unroll
+    for (int q = 0; q < G::S_W; ++q) dmab_per_step += (G::NSC % NW == 0 || q * NW + wave < G::NSC) ? 1 : 0;
+    // Issue order: the prologue issues, for s = 0, 1, ..., the token tile of
+    // step s (s < NS - 1) and then the weight tile of step s (s < NSB - 1);
+    // step kt issues the token tile of kt + NS - 1, then the weight tile of
+    // kt + NSB - 1.  At the top of step kt the loads issued after the last
+    // one it needs are: NSB == NS: the NS - 2 later steps' loads; NS = 2,
+    // NSB = 3: the weight tile of kt + 1, issued right after the token tile
+    // of kt.
     auto wait_for = [&](int kt) {
-        const int later = min(NS - 2, KT - 1 - kt);   // steps issued after kt
-        wait_vm_lgkm0_rt(later * dma_per_step);
+        if constexpr (NSB == NS) {
+            const int later = min(NS - 2, KT - 1 - kt);   // steps issued after kt
+            wait_vm_lgkm0_rt(later * dma_per_step);
+        } else {
+            wait_vm_lgkm0_rt(kt + 1 < KT ? dmab_per_step : 0);
+        }
     };
     if (MX && !WDMA) issue_mx(0);
     if (A4) {
@@ -774,8 +834,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
         store_scales(0);   // published by the first step's barrier
     }
 #pragma unroll
-    for (int s0 = 0; s0 < NS - 1; ++s0)
-        if (s0 < KT) issue_dma(s0);
+    for (int s0 = 0; s0 < NSB - 1; ++s0) {
+        if (s0 < NS - 1 && s0 < KT) issue_a(s0);
+        if (s0 < KT) issue_b(s0);
+    }
     // Per-tile block scales (4-bit codes straight to LDS in 64-wide steps):
     // the tile's whole scale rows, K/32 bytes each, read into LDS once,
     // NT/BN threads per row, in 16-bit words.  They are issued after the
@@ -821,9 +883,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
             // counts cover them), stored after this step's MFMAs are issued
             const bool next_sc = A4 && kt + 1 < KT;
             if (next_sc) load_scales(kt + 1);
-            if (kt + NS - 1 < KT) issue_dma(kt + NS - 1);
+            if (kt + NS - 1 < KT) issue_a(kt + NS - 1);
+            const bool spread = SPREAD && MUL && kt + NSB - 1 < KT;
+            if (kt + NSB - 1 < KT && !spread) issue_b(kt + NSB - 1);
             if (MUL) {
-                compute(kt);
+                compute(kt, spread ? kt + NSB - 1 : -1);
                 if (ROUTER && ((kt % (256 / BK)) == 256 / BK - 1 || kt == KT - 1)) flush();
             }
             if (next_sc) {
@@ -947,7 +1011,7 @@ static int mtile_slots(int A, int E, int BM) {
 }
 
 template <int BM, int BN, int WM, int WN, int MODE, bool MX, int NS, int BK, bool A4 = false, bool NV = false,
-          bool WD = false>
+          bool WD = false, int NSB = 0>
 static hipError_t launch_cfg(GemmArgs a, int A, hipStream_t st) {
     constexpr bool GEGLU = MODE == kGateUp;
     const int ncols = GEGLU ? a.I : a.n_out;
@@ -974,7 +1038,7 @@ static hipError_t launch_cfg(GemmArgs a, int A, hipStream_t st) {
         blocks += (long long)a.sh_n_tiles * ((a.sh_rows + BM - 1) / BM) * max(1, a.sh_splits);
     }
     if (blocks == 0) return hipSuccess;
-    grouped_gemm_kernel<BM, BN, WM, WN, MODE, MX, NS, BK, A4, NV, WD>
+    grouped_gemm_kernel<BM, BN, WM, WN, MODE, MX, NS, BK, A4, NV, WD, NSB>
         <<<dim3((unsigned)blocks), 64 * WM * WN, 0, st>>>(a);
     return hipGetLastError();
 }
@@ -1027,7 +1091,10 @@ static hipError_t launch_sized(const GemmArgs &a, int A, hipStream_t st) {
                             a.K / 32 <= GemmTile<256, 256, 4, 2, MODE, MX, 3, 64, false, false, true>::SC_ROW;
         if (direct && a.sh_rows == 0) return launch_cfg<256, 256, 4, 2, MODE, MX, 3, 64, false, false, true>(a, A, st);
     }
-    return launch_cfg<256, 256, 4, 2, MODE, MX, MX ? 3 : 2, 64, false, NV>(a, A, st);
+    if constexpr (!MX)
+        return launch_cfg<256, 256, 4, 2, MODE, MX, 2, 64, false, NV, false, 3>(a, A, st);
+    else
+        return launch_cfg<256, 256, 4, 2, MODE, MX, 3, 64, false, NV>(a, A, st);
 }
 
 // W4A4: the same tile choice as bf16 activations, K steps of 256 codes.
