@@ -15,8 +15,10 @@
 // direction); tile BM tokens x BN weight rows, K in steps of BK.  Operand
 // tiles go straight from global memory into LDS (global_load_lds_dwordx4,
 // issued from inline asm so that the compiler adds no waits of its own) in
-// an NS-stage ring; each wave waits only for its own loads (explicit vmcnt)
-// and a barrier publishes a stage.  The MFMA takes the weight tile as its A
+// rings of NS token stages and NS or NS + 1 weight stages; each wave waits
+// only for its own loads (explicit vmcnt) and a barrier publishes a stage.
+// With the deeper weight ring a wave's weight loads are spread among its
+// MFMAs.  The MFMA takes the weight tile as its A
 // operand and the tokens as B, so each lane ends with four consecutive output
 // columns of one token; the epilogue pairs fragments across lanes (a lane
 // swap) so that a lane stores eight consecutive columns.
@@ -1052,8 +1054,9 @@ static hipError_t launch_sized(const GemmArgs &a, int A, hipStream_t st) {
     // four workgroups per CU.  The 256 x 256 block runs one workgroup of eight
     // waves (two per SIMD, so one wave's LDS reads overlap the other's MFMAs)
     // per CU: the large tile moves the fewest bytes per FLOP through the
-    // per-CU load path; bf16 in two stages of 64 KB, MXFP4 (small weight
-    // tiles) in three.  (Measured: K steps of 32 in four stages are slower.)
+    // per-CU load path; bf16 with two token and three weight stages (the
+    // 160 KB of LDS), MXFP4 (small weight tiles) in three stages of both.
+    // (Measured: K steps of 32 in four stages are slower.)
     if (mean_rows <= 16) {
         // bf16 weight rows are read in 256-byte pieces per step where K
         // allows it (measured: 2% faster than 128-byte pieces at 2816 x
