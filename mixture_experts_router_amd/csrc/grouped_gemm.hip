@@ -83,9 +83,8 @@ struct GemmArgs {
 
 // Locate this workgroup's M tile: tile index -> (expert e, first row m0
 // within the expert, the expert's rows n and its first grouped row off), or
-// e = -1 past the last tile.  Every wave computes it (a wave prefix scan of
-// ceil(n_e / BM) over the experts, 64 at a time); the results are
-// wave-uniform.
+// e = -1 past the last tile: a wave prefix scan of ceil(n_e / BM) over the
+// experts, 64 at a time; the results are wave-uniform.
 struct TileInfo {
     int e, m0, n, off;
 };
@@ -216,7 +215,12 @@ struct GemmTile {
     static constexpr int B_OFF = A_OFF + NS * A_LDS * 2;
     static constexpr int S_OFF = B_OFF + NSB * B_LDS * 2;
     static constexpr int C_OFF = S_OFF + ((SS_SLOTS * SS_BYTES + 15) / 16) * 16;
-    static constexpr int LDS_BYTES = C_OFF + (A4_ ? NS * SC_BYTES : 0);
+    static constexpr int I_OFF = C_OFF + ((A4_ ? NS * SC_BYTES : 0) + 15) / 16 * 16;
+    // The tile lookup runs in wave 0 and reaches the others through 16 bytes
+    // of LDS where they fit; a tile that fills the 160 KB runs it in every
+    // wave instead.
+    static constexpr bool INFO_LDS = I_OFF + 16 <= 160 * 1024;
+    static constexpr int LDS_BYTES = I_OFF + (INFO_LDS ? 16 : 0);
     static_assert(LDS_BYTES <= 160 * 1024, "LDS of one workgroup");
 };
 
@@ -370,7 +374,23 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
         seg = m0;
         stream = p.sh_rows <= p.stream_max_rows;
     } else {
-        const TileInfo ti = find_tile<BM>(p.offsets, p.E, mslot);
+        TileInfo ti;
+        if constexpr (G::INFO_LDS) {
+            int *s_info = reinterpret_cast<int *>(smem + G::I_OFF);
+            if (wave == 0) {
+                ti = find_tile<BM>(p.offsets, p.E, mslot);
+                if (lane == 0) {
+                    s_info[0] = ti.e;
+                    s_info[1] = ti.m0;
+                    s_info[2] = ti.n;
+                    s_info[3] = ti.off;
+                }
+            }
+            __syncthreads();
+            ti = TileInfo{s_info[0], s_info[1], s_info[2], s_info[3]};
+        } else {
+            ti = find_tile<BM>(p.offsets, p.E, mslot);
+        }
         e = __builtin_amdgcn_readfirstlane(ti.e);
         if (e < 0) return;
         m0 = __builtin_amdgcn_readfirstlane(ti.m0);
