@@ -82,9 +82,15 @@ def algorithmic(inp, ids):
 
 
 def kernel_source_hash():
+    """Hash of the gate/up kernel's code (comments and whitespace removed,
+    so a comment edit does not invalidate counters taken on the same code)."""
+    import re
     h = hashlib.sha256()
     for f in ("grouped_gemm.hip", "moe_common.h"):
-        h.update(open(os.path.join(ROOT, "mixture_experts_router_amd", "csrc", f), "rb").read())
+        src = open(os.path.join(ROOT, "mixture_experts_router_amd", "csrc", f)).read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

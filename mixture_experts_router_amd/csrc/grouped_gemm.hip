@@ -308,7 +308,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
     constexpr int CH = G::CH, RPD = G::RPD, KK = G::KK;
     constexpr int NA = G::NA, NB = G::NB, A_W = G::A_W, B_W = G::B_W, NW = G::NW, NT = G::NT;
 
-    // bf16 tiles: [row][8 chunks of 16 B], chunk index XOR-swizzled by row.
+    // bf16 tiles: [row][BK/8 chunks of 16 B], chunk index XOR-swizzled by row.
     // 4-bit weights through registers: codes [word of 8 codes][row], scale
     // bytes [block][row]; straight to LDS in 256-wide steps: codes [row][8
     // chunks of 16 B] (XOR-swizzled by row & 7), scale bytes [row][block];
@@ -815,11 +815,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
         }
     };
 
-    // ---- pipeline.  Step kt: wait until its loads have landed (the loads of
-    // the later steps already issued may stay in flight), publish, issue the
-    // loads of step kt + NS - 1 into the buffer freed by step kt - 1, then
-    // multiply.  Issue order keeps the counts exact: every wave issues its
-    // loads of one step before those of the next.
+    // ---- pipeline.  Step kt: wait until its loads have landed (loads of
+    // later steps already issued may stay in flight), publish, issue the
+    // token tile of step kt + NS - 1 and the weight tile of step kt + NSB - 1
+    // into the stages freed by step kt - 1, then multiply.  The issue order
+    // (below, at wait_for) keeps the counts exact.
     // Loads this wave issues per step: its valid token-row groups and its
     // weight-row groups (exact, so each wave waits for no more than it must).
     int dma_per_step = 0;
