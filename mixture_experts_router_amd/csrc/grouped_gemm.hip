@@ -180,7 +180,7 @@ struct GemmTile {
     static_assert(NW == 4 || NW == 8, "four or eight waves");
     static_assert(MI >= 1 && NI >= 1, "tile too small");
     static_assert(!GEGLU || (NI % 2 == 0), "GEGLU pairs gate and up tiles");
-    static_assert(BK == 32 || BK == 64 || BK == 128 || (MX && BK == 256), "K step");
+    static_assert(BK == 32 || BK == 64 || BK == 128 || ((MX || MODE == kRouter) && BK == 256), "K step");
     static_assert(BM % RPD == 0 && BN % RPD == 0, "whole 1 KB load groups");
     static_assert(!MX || BK == 64 || BK == 256, "4-bit weight tiles use K steps of 64 or 256");
     static_assert(NS >= 2 && NS <= 8, "stages");
@@ -1196,9 +1196,11 @@ hipError_t launch_down(const uint16_t *h, const int32_t *offsets, const void *w,
 }
 
 // Router for many tokens: x [T][H] times W_r [E][H]^T as one dense group, 16
-// tokens x 64 experts per workgroup; K steps of 128 where H allows (half
-// the steps of a latency-bound loop: measured 23 -> 18.5 us at 2048 tokens),
-// four stages.  From 8192 tokens (256 tiles of 32 tokens) the tile is 32
+// tokens x 64 experts per workgroup; K steps as long as H allows (fewer
+// steps of a latency-bound loop: 64 -> 128 measured 23 -> 18.5 us for the
+// routing at 2048 tokens, 128 in four stages -> 256 in three 18.5 -> 17.5
+// us; a step of 256 is one chunk of the logit definition).  From 8192
+// tokens (256 tiles of 32 tokens) the tile is 32
 // tokens x 128 experts in three stages: half the operand bytes per FLOP
 // through the per-CU load path (8192 tokens: 43.6 -> 35.6 us for the
 // routing; at 2048 tokens, 64 such tiles leave most CUs idle: 18 -> 29 us).
@@ -1206,6 +1208,7 @@ hipError_t launch_router_dense(const uint16_t *x, const uint16_t *wr, const floa
                                int T, int H, int E, hipStream_t st) {
     GemmArgs a{x, nullptr, 1, nullptr, wr, nullptr, nullptr, 1, H, E, 0, E, 0, 0, T, logits, bias};
     if (H % 128 == 0 && T >= 8192) return launch_cfg<32, 128, 2, 2, kRouter, false, 3, 128>(a, T, st);
+    if (H % 256 == 0) return launch_cfg<16, 64, 1, 4, kRouter, false, 3, 256>(a, T, st);
     if (H % 128 == 0) return launch_cfg<16, 64, 1, 4, kRouter, false, 4, 128>(a, T, st);
     return launch_cfg<16, 64, 1, 4, kRouter, false, 6, 64>(a, T, st);
 }
