@@ -1109,10 +1109,13 @@ static hipError_t launch_sized(const GemmArgs &a, int A, hipStream_t st) {
         // MXFP4 codes straight to LDS (16-byte aligned rows of K/2 bytes)
         // with the tile's scale rows (K/32 bytes, 2-byte aligned, at most
         // SC_ROW) read into LDS once: no register staging in the K loop.
+        // Waves 2 x 4 (128 tokens x 64 weight rows each): every weight
+        // fragment is expanded by two waves instead of four (by one at <=
+        // 128 rows); measured at 2048 tokens: gate/up 237.8 -> 229.4 us.
         const bool direct = (reinterpret_cast<uintptr_t>(a.w) & 15u) == 0 &&
                             (reinterpret_cast<uintptr_t>(a.scales) & 1u) == 0 && a.K >= 128 &&
-                            a.K / 32 <= GemmTile<256, 256, 4, 2, MODE, MX, 3, 64, false, false, true>::SC_ROW;
-        if (direct && a.sh_rows == 0) return launch_cfg<256, 256, 4, 2, MODE, MX, 3, 64, false, false, true>(a, A, st);
+                            a.K / 32 <= GemmTile<256, 256, 2, 4, MODE, MX, 3, 64, false, false, true>::SC_ROW;
+        if (direct && a.sh_rows == 0) return launch_cfg<256, 256, 2, 4, MODE, MX, 3, 64, false, false, true>(a, A, st);
     }
     if constexpr (!MX)
         return launch_cfg<256, 256, 4, 2, MODE, MX, 2, 64, false, NV, false, 3>(a, A, st);
