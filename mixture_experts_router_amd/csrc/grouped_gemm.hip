@@ -11,7 +11,7 @@
 // grouped matmul of the pages (SwiftGMM, Pangu Pro MoE summary article,
 // group 4) is prior art only.
 //
-// Workgroup = 4 or 8 waves = WAVES_M (token direction) x WAVES_N (weight-row
+// Workgroup = 4, 8 or 16 waves = WAVES_M (token direction) x WAVES_N (weight-row
 // direction); tile BM tokens x BN weight rows, K in steps of BK.  Operand
 // tiles go straight from global memory into LDS (global_load_lds_dwordx4,
 // issued from inline asm so that the compiler adds no waits of its own) in
@@ -177,7 +177,7 @@ struct GemmTile {
     static constexpr int MS_PER = MX && !WDMA ? (BN + NT - 1) / NT : 1;
     static constexpr int A_LDS = BM * BK;                      // uint16 per stage
     static constexpr int B_LDS = MX ? BN * BK / 4 : BN * BK;   // uint16 per stage
-    static_assert(NW == 4 || NW == 8, "four or eight waves");
+    static_assert(NW == 4 || NW == 8 || NW == 16, "four, eight or sixteen waves");
     static_assert(MI >= 1 && NI >= 1, "tile too small");
     static_assert(!GEGLU || (NI % 2 == 0), "GEGLU pairs gate and up tiles");
     static_assert(BK == 32 || BK == 64 || BK == 128 || ((MX || MODE == kRouter) && BK == 256), "K step");
@@ -1071,12 +1071,16 @@ template <int MODE, bool MX, bool NV = false>
 static hipError_t launch_sized(const GemmArgs &a, int A, hipStream_t st) {
     const int mean_rows = A / a.E;
     // Small row blocks stream weights: two stages keep LDS small enough for
-    // four workgroups per CU.  The 256 x 256 block runs one workgroup of eight
-    // waves (two per SIMD, so one wave's LDS reads overlap the other's MFMAs)
-    // per CU: the large tile moves the fewest bytes per FLOP through the
-    // per-CU load path; bf16 with two token and three weight stages (the
-    // 160 KB of LDS), MXFP4 (small weight tiles) in three stages of both.
-    // (Measured: K steps of 32 in four stages are slower.)
+    // four workgroups per CU.  The 256 x 256 block runs one workgroup of
+    // sixteen waves (4 x 4, 64 tokens x 64 weight rows each) per CU: the
+    // large tile moves the fewest bytes per FLOP through the per-CU load
+    // path, and at <= 128 rows per expert (the first two token groups busy)
+    // each SIMD still has two multiplying waves, so one wave's LDS reads and
+    // waits overlap another's MFMAs (eight waves, 4 x 2, left one per SIMD:
+    // measured at 2048 tokens, gate/up 239 -> 220 us bf16 and 228 -> 194 us
+    // MXFP4).  bf16 with two token and three weight stages (the 160 KB of
+    // LDS), MXFP4 (small weight tiles) in three stages of both.  (Measured:
+    // K steps of 32 in four stages are slower.)
     if (mean_rows <= 16) {
         // bf16 weight rows are read in 256-byte pieces per step where K
         // allows it (measured: 2% faster than 128-byte pieces at 2816 x
@@ -1109,16 +1113,17 @@ static hipError_t launch_sized(const GemmArgs &a, int A, hipStream_t st) {
         // MXFP4 codes straight to LDS (16-byte aligned rows of K/2 bytes)
         // with the tile's scale rows (K/32 bytes, 2-byte aligned, at most
         // SC_ROW) read into LDS once: no register staging in the K loop.
-        // Waves 2 x 4 (128 tokens x 64 weight rows each): every weight
-        // fragment is expanded by two waves instead of four (by one at <=
-        // 128 rows); measured at 2048 tokens: gate/up 237.8 -> 229.4 us.
+        // Waves 4 x 4: each weight fragment is expanded by four waves, but
+        // two waves per SIMD multiply at <= 128 rows (2 x 8 waves, two
+        // expansions per fragment: 217 us; 4 x 4: 194 us for the gate/up at
+        // 2048 tokens).
         const bool direct = (reinterpret_cast<uintptr_t>(a.w) & 15u) == 0 &&
                             (reinterpret_cast<uintptr_t>(a.scales) & 1u) == 0 && a.K >= 128 &&
-                            a.K / 32 <= GemmTile<256, 256, 2, 4, MODE, MX, 3, 64, false, false, true>::SC_ROW;
-        if (direct && a.sh_rows == 0) return launch_cfg<256, 256, 2, 4, MODE, MX, 3, 64, false, false, true>(a, A, st);
+                            a.K / 32 <= GemmTile<256, 256, 4, 4, MODE, MX, 3, 64, false, false, true>::SC_ROW;
+        if (direct && a.sh_rows == 0) return launch_cfg<256, 256, 4, 4, MODE, MX, 3, 64, false, false, true>(a, A, st);
     }
     if constexpr (!MX)
-        return launch_cfg<256, 256, 4, 2, MODE, MX, 2, 64, false, NV, false, 3>(a, A, st);
+        return launch_cfg<256, 256, 4, 4, MODE, MX, 2, 64, false, NV, false, 3>(a, A, st);
     else
         return launch_cfg<256, 256, 4, 2, MODE, MX, 3, 64, false, NV>(a, A, st);
 }
@@ -1130,7 +1135,7 @@ static hipError_t launch_sized_a4(const GemmArgs &a, int A, hipStream_t st) {
     if (mean_rows <= 16) return launch_cfg<16, 128, 1, 4, MODE, false, 2, 64, true>(a, A, st);
     if (mean_rows <= 40) return launch_cfg<32, 128, 2, 2, MODE, false, 2, 64, true>(a, A, st);
     if (mean_rows <= 80) return launch_cfg<64, 128, 2, 2, MODE, false, 2, 64, true>(a, A, st);
-    return launch_cfg<256, 256, 4, 2, MODE, false, 2, 64, true>(a, A, st);
+    return launch_cfg<256, 256, 4, 4, MODE, false, 2, 64, true>(a, A, st);
 }
 
 hipError_t launch_gateup_a4(const uint8_t *xq, const uint8_t *xs, const int32_t *sorted_ids, int k,
@@ -1206,11 +1211,13 @@ hipError_t launch_down(const uint16_t *h, const int32_t *offsets, const void *w,
 // tokens (256 tiles of 32 tokens) the tile is 32
 // tokens x 128 experts in three stages: half the operand bytes per FLOP
 // through the per-CU load path (8192 tokens: 43.6 -> 35.6 us for the
-// routing; at 2048 tokens, 64 such tiles leave most CUs idle: 18 -> 29 us).
+// routing; at 2048 tokens, 64 such tiles leave most CUs idle: 18 -> 29 us),
+// in eight waves of 16 tokens x 32 experts (four waves: 37.0 us for the
+// routing at 8192 tokens, eight: 31.1 us).
 hipError_t launch_router_dense(const uint16_t *x, const uint16_t *wr, const float *bias, float *logits,
                                int T, int H, int E, hipStream_t st) {
     GemmArgs a{x, nullptr, 1, nullptr, wr, nullptr, nullptr, 1, H, E, 0, E, 0, 0, T, logits, bias};
-    if (H % 128 == 0 && T >= 8192) return launch_cfg<32, 128, 2, 2, kRouter, false, 3, 128>(a, T, st);
+    if (H % 128 == 0 && T >= 8192) return launch_cfg<32, 128, 2, 4, kRouter, false, 3, 128>(a, T, st);
     if (H % 256 == 0) return launch_cfg<16, 64, 1, 4, kRouter, false, 3, 256>(a, T, st);
     if (H % 128 == 0) return launch_cfg<16, 64, 1, 4, kRouter, false, 4, 128>(a, T, st);
     return launch_cfg<16, 64, 1, 4, kRouter, false, 6, 64>(a, T, st);
