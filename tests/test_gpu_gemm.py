@@ -54,6 +54,7 @@ CASES = [
     (1000, 256, 8, 2, 128),    # mean 250
     (257, 2816, 128, 8, 704),  # Gemma-4 expert shape, mean 16
     (4096, 512, 128, 8, 256),  # mean 256: 512 down tiles of 256 rows, two rounds per CU
+    (1000, 320, 8, 2, 192),    # mean 250, 256-row tiles: last down column tile 64 of 256 wide, last gate/up one half
 ]
 
 
