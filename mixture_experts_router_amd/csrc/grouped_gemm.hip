@@ -1128,8 +1128,13 @@ static hipError_t launch_sized(const GemmArgs &a, int A, hipStream_t st) {
         }
         return launch_cfg<16, 128, 1, 4, MODE, MX, 2, 64, false, NV>(a, A, st);
     }
-    if (mean_rows <= 40) return launch_cfg<32, 128, 2, 2, MODE, MX, 2, 64, false, NV>(a, A, st);
-    if (mean_rows <= 80) return launch_cfg<64, 128, 2, 2, MODE, MX, 2, 64, false, NV>(a, A, st);
+    // Above 16: the row tile holds a typical expert's rows whole (mean plus
+    // a few standard deviations), so each weight slab is streamed once
+    // rather than once per row tile: 64-row tiles up to a mean of 40 rows,
+    // the 256 x 256 tile above (measured: 512 tokens, 64- instead of 32-row
+    // tiles, step 376 -> 295 us; 1024 tokens, 256- instead of 64-row tiles,
+    // 398 -> 336 us).
+    if (mean_rows <= 40) return launch_cfg<64, 128, 2, 2, MODE, MX, 2, 64, false, NV>(a, A, st);
     if constexpr (MX && !NV) {
         // MXFP4 codes straight to LDS (16-byte aligned rows of K/2 bytes)
         // with the tile's scale rows (K/32 bytes, 2-byte aligned, at most

@@ -45,12 +45,12 @@ def _acc_err(absdot, K):
     return (K / 32 + 32) * U32 * absdot
 
 
-# Cases span several row blocks and a ragged tail, and hit the four row-block
-# sizes (mean rows per expert <= 16, <= 48, <= 96, > 96).
+# Cases span several row blocks and a ragged tail, and hit the three row-block
+# sizes (16 rows up to a mean of 16 rows per expert, 64 up to 40, 256 above).
 CASES = [
     (64, 512, 16, 2, 192),     # mean 8 rows/expert
-    (300, 512, 16, 2, 192),    # mean 37
-    (300, 512, 16, 4, 192),    # mean 75
+    (300, 512, 16, 2, 192),    # mean 37: 64-row tiles
+    (300, 512, 16, 4, 192),    # mean 75: 256-row tiles
     (1000, 256, 8, 2, 128),    # mean 250
     (257, 2816, 128, 8, 704),  # Gemma-4 expert shape, mean 16
     (4096, 512, 128, 8, 256),  # mean 256: 512 down tiles of 256 rows, two rounds per CU
