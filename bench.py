@@ -11,6 +11,9 @@ cannot serve them from a previous step.
 Prints one JSON line:  value = tokens/s of the whole layer; roofline = the
 dominant kernel (grouped gate/up GEMM) against the HBM or MFMA peak, its
 duration from HIP events around back-to-back launches on the launch stream;
+layer = the whole step against both rooflines; extra = the same figures for
+the prefill-size workloads (bf16 prefill of 2048 tokens, the Zipf-skewed
+prefill of 8192 tokens, MXFP4 experts), timed in the same process;
 cpu_baseline = the fp64 numpy oracle timed on this host on a bounded sample.
 """
 from __future__ import annotations
@@ -44,6 +47,10 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle timing")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
+    p.add_argument("--extra", default="prefill,skew,mxfp4",
+                   help="other workloads timed in the same run and reported under 'extra' (comma list, or none)")
+    p.add_argument("--extra-steps", type=int, default=30)
+    p.add_argument("--extra-warmup", type=int, default=5)
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a device copy of MIB mebibytes (counter calibration) and exit")
     return p.parse_args()
@@ -175,31 +182,54 @@ def cpu_baseline(inp, budget_s):
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only: the layer holds all experts on one device and this "
-              f"build has no multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
-        sys.exit(2)
+def kernel_roofline(alg, launch_us, mfma_peak):
+    """The gate/up kernel against both rooflines; `bound` is the one its
+    arithmetic intensity (FLOP per algorithmic byte) puts it under."""
+    t = launch_us * 1e-6
+    ridge = mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)
+    gbs = alg["gateup_bytes"] / t / 1e9
+    tfs = alg["gateup_flops"] / t / 1e12
+    if alg["gateup_flops"] / alg["gateup_bytes"] > ridge:
+        bound, unit, peak, achieved = "mfma", "TFLOP/s", mfma_peak, tfs
+    else:
+        bound, unit, peak, achieved = "hbm", "GB/s", HBM_PEAK_GBS, gbs
+    return {"kernel": "grouped_gemm gate/up + GEGLU", "bound": bound, "achieved": achieved, "peak": peak,
+            "unit": unit, "frac": achieved / peak, "hbm_frac": gbs / HBM_PEAK_GBS,
+            "mfma_frac": tfs / mfma_peak, "alg_bytes_per_launch": alg["gateup_bytes"],
+            "alg_flops_per_launch": alg["gateup_flops"], "avg_launch_us": launch_us}
 
+
+def layer_roofline(alg, ms, mfma_peak):
+    """The whole layer (one step) against both rooflines: t_roof / t with
+    t_roof = max(F / peak, B / bandwidth) is the binding fraction."""
+    t = ms * 1e-3
+    layer = {"touched_experts": alg["U"], "alg_bytes": alg["layer_bytes"], "alg_flops": alg["layer_flops"],
+             "hbm_frac": alg["layer_bytes"] / t / (HBM_PEAK_GBS * 1e9),
+             "mfma_frac": alg["layer_flops"] / t / (mfma_peak * 1e12)}
+    layer["binding_frac"] = max(layer["hbm_frac"], layer["mfma_frac"])
+    layer["binding"] = "hbm" if layer["hbm_frac"] >= layer["mfma_frac"] else "mfma"
+    return layer
+
+
+def workload_name(config, s):
+    return (f"Gemma-4-26B-A4B MoE FFN layer, {config}: T={s.T} tokens, "
+            f"hidden {s.H}, {s.E} experts, top-{s.k}, intermediate {s.I}, "
+            f"GEGLU, {'MXFP4' if s.mxfp4 else ('NVFP4' if s.nvfp4 else 'bf16')} expert weights"
+            f"{' and MXFP4 activations (W4A4)' if s.a4 else ''}"
+            f"{', Zipf(1.2) router bias' if s.skew else ''}"
+            f"{f', plus the dense GEGLU MLP (intermediate {s.I_sh}) as a shared expert' if s.I_sh else ''}")
+
+
+def measure(config, K, warmup, rotate, full):
+    """Time moe_forward on one workload.  Returns (result dict, inputs).
+    `full` adds the per-step event spread and the HIP-graph replay."""
     import torch
     import moe_inputs as mi
     import mixture_experts_router_amd as moe
     from mixture_experts_router_amd import device as dev
 
-    if args.copy_calibration:
-        n = args.copy_calibration << 20
-        a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
-        b = torch.empty_like(a)
-        torch.cuda.synchronize()
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
-        return
-
     t_gen = time.perf_counter()
-    inp = mi.make(args.config, seed=0)
+    inp = mi.make(config, seed=0)
     s = inp.shape
     sh = moe.shape(s.T, s.H, s.E, s.k, s.I, mxfp4=s.mxfp4, a4=s.a4, nvfp4=s.nvfp4)
     x = dev.to_device(inp.x)
@@ -212,7 +242,7 @@ def main():
     if s.nvfp4:   # one buffer per matrix: the fp32 expert scales, then the E4M3 codes
         gus = dev.to_device(moe.nvfp4_scale_buffer(inp.gu_global, inp.gu_scales))
         ds = dev.to_device(moe.nvfp4_scale_buffer(inp.d_global, inp.d_scales))
-    copies = [(gu0, d0)] + [(gu0.clone(), d0.clone()) for _ in range(max(0, args.rotate - 1))]
+    copies = [(gu0, d0)] + [(gu0.clone(), d0.clone()) for _ in range(max(0, rotate - 1))]
     if s.I_sh:   # the dense MLP's weights rotate with the experts'
         sg0, sd0 = dev.to_device(inp.w_sh_gate_up), dev.to_device(inp.w_sh_down)
         sh_copies = [(sg0, sd0)] + [(sg0.clone(), sd0.clone()) for _ in range(len(copies) - 1)]
@@ -224,7 +254,7 @@ def main():
     ws = dev.workspace(sh, I_sh=s.I_sh)
     torch.cuda.synchronize()
     gen_s = time.perf_counter() - t_gen
-    print(f"# inputs ready in {gen_s:.1f}s: {args.config} {s}", file=sys.stderr, flush=True)
+    print(f"# inputs ready in {gen_s:.1f}s: {config} {s}", file=sys.stderr, flush=True)
 
     def step(i, events=None):
         gu, d = copies[i % len(copies)]
@@ -235,13 +265,12 @@ def main():
         else:
             moe.forward(sh, x, wr, bias, gu, gus, d, ds, out, ids, wts, ws, stage_events=events)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     ids_np = ids.cpu().numpy()
     alg = algorithmic(inp, ids_np)
 
-    K = args.steps
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
 
@@ -266,7 +295,7 @@ def main():
     stage_ms = np.array([ev.stage_ms(i) for i in range(K)])      # [K, 5]
     ev.close()
     stage_avg_us = {n: float(v) * 1e3 for n, v in zip(STAGES, stage_ms.mean(axis=0))}
-    print(f"# {K} steps: {ms * 1e3:.1f} us/step; stages (us) " +
+    print(f"# {config}: {K} steps: {ms * 1e3:.1f} us/step; stages (us) " +
           " ".join(f"{n}={v:.1f}" for n, v in stage_avg_us.items()), file=sys.stderr, flush=True)
 
     # Timed region 3: the dominant kernel alone, K back-to-back launches of
@@ -281,12 +310,11 @@ def main():
     offsets = torch.empty(s.E + 1, **i32)
     sorted_ids = torch.empty(A, **i32)
     inv = torch.empty(A, **i32)
-    x_perm = torch.empty((A, s.H), dtype=torch.bfloat16, device="cuda")
     h = torch.empty((A, s.I), dtype=torch.bfloat16, device="cuda")
     rws = torch.empty(max(1, moe.route_workspace_bytes(sh)), dtype=torch.uint8, device="cuda")
     pws = torch.empty(max(1, moe.permute_workspace_bytes(sh)), dtype=torch.uint8, device="cuda")
     moe.route(sh, x, wr, bias, r_logits, r_ids, r_w, ws=rws)
-    moe.permute(sh, r_ids, x, counts, offsets, sorted_ids, inv, x_perm, pws)
+    moe.permute(sh, r_ids, None, counts, offsets, sorted_ids, inv, None, pws)
     torch.cuda.synchronize()
     if not torch.equal(r_ids.cpu(), ids.cpu()):
         raise RuntimeError("moe_route and moe_forward disagree on the routing")
@@ -305,26 +333,26 @@ def main():
         end.record()
         torch.cuda.synchronize()
         gateup_launch_us = start.elapsed_time(end) / K * 1e3
-        print(f"# gate/up kernel alone: {gateup_launch_us:.1f} us per launch", file=sys.stderr, flush=True)
+        print(f"# {config}: gate/up kernel alone: {gateup_launch_us:.1f} us per launch", file=sys.stderr,
+              flush=True)
 
-    # Timed region 4: K steps, each bracketed by its own pair of events ->
-    # the spread of the step time (each pair adds its own record latency).
-    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    torch.cuda.synchronize()
-    for i in range(K):
-        ev_a[i].record()
-        step(i)
-        ev_b[i].record()
-    torch.cuda.synchronize()
-    per_step = np.array([a.elapsed_time(b) * 1e3 for a, b in zip(ev_a, ev_b)])
-    spread = {"p10": float(np.percentile(per_step, 10)), "p50": float(np.percentile(per_step, 50)),
-              "p90": float(np.percentile(per_step, 90))}
-
-    # Timed region 5: the same steps captured once as a HIP graph (one
-    # moe_forward per weight copy) and replayed back to back.
-    graph_us = None
-    if not args.no_graph:
+    spread, graph_us = None, None
+    if full:
+        # Timed region 4: K steps, each bracketed by its own pair of events ->
+        # the spread of the step time (each pair adds its own record latency).
+        ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+        ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+        torch.cuda.synchronize()
+        for i in range(K):
+            ev_a[i].record()
+            step(i)
+            ev_b[i].record()
+        torch.cuda.synchronize()
+        per_step = np.array([a.elapsed_time(b) * 1e3 for a, b in zip(ev_a, ev_b)])
+        spread = {"p10": float(np.percentile(per_step, 10)), "p50": float(np.percentile(per_step, 50)),
+                  "p90": float(np.percentile(per_step, 90))}
+        # Timed region 5: the same steps captured once as a HIP graph (one
+        # moe_forward per weight copy) and replayed back to back.
         g = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
@@ -344,66 +372,87 @@ def main():
         end.record()
         torch.cuda.synchronize()
         graph_us = start.elapsed_time(end) * 1e3 / (reps * len(copies))
-    print(f"# per-step events p10/p50/p90 {spread['p10']:.1f}/{spread['p50']:.1f}/{spread['p90']:.1f} us; "
-          f"graph replay {graph_us if graph_us is None else round(graph_us, 1)} us per step",
-          file=sys.stderr, flush=True)
+        del g
+        print(f"# per-step events p10/p50/p90 {spread['p10']:.1f}/{spread['p50']:.1f}/{spread['p90']:.1f} us; "
+              f"graph replay {round(graph_us, 1)} us per step", file=sys.stderr, flush=True)
 
-    tokens_per_s = s.T / (ms * 1e-3)
-    gu_s = gateup_launch_us * 1e-6
     mfma_peak = FP4_PEAK_TFLOPS if s.a4 else BF16_PEAK_TFLOPS   # the expert matmuls' own dtype
-    ridge = mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)
-    if alg["gateup_flops"] / alg["gateup_bytes"] > ridge:
-        bound, unit, peak = "mfma", "TFLOP/s", mfma_peak
-        achieved = alg["gateup_flops"] / gu_s / 1e12
-    else:
-        bound, unit, peak = "hbm", "GB/s", HBM_PEAK_GBS
-        achieved = alg["gateup_bytes"] / gu_s / 1e9
-    t_layer = ms * 1e-3
-    layer = {
-        "touched_experts": alg["U"],
-        "alg_bytes": alg["layer_bytes"], "alg_flops": alg["layer_flops"],
-        "hbm_frac": alg["layer_bytes"] / t_layer / (HBM_PEAK_GBS * 1e9),
-        "mfma_frac": alg["layer_flops"] / t_layer / (mfma_peak * 1e12),
-    }
-    # t_roof / t with t_roof = max(F / peak, B / bandwidth): the layer against
-    # whichever roofline binds it
-    layer["binding_frac"] = max(layer["hbm_frac"], layer["mfma_frac"])
-    layer["binding"] = "hbm" if layer["hbm_frac"] >= layer["mfma_frac"] else "mfma"
+    roof = kernel_roofline(alg, gateup_launch_us, mfma_peak)
+    roof["traffic"] = traffic_from_profiles(config)
     res = {
-        "metric": METRIC,
-        "value": tokens_per_s,
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
         "ms_per_step": ms,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
+        "tokens_per_s": s.T / (ms * 1e-3),
+        "steps": K,
+        "warmup": warmup,
         "dtype": "mxfp4" if s.a4 else "bf16",
-        "data": "synthetic",
-        "config": {"workload": f"Gemma-4-26B-A4B MoE FFN layer, {args.config}: T={s.T} tokens, "
-                               f"hidden {s.H}, {s.E} experts, top-{s.k}, intermediate {s.I}, "
-                               f"GEGLU, {'MXFP4' if s.mxfp4 else ('NVFP4' if s.nvfp4 else 'bf16')} expert weights"
-                               f"{' and MXFP4 activations (W4A4)' if s.a4 else ''}"
-                               f"{', Zipf(1.2) router bias' if s.skew else ''}"
-                               f"{f', plus the dense GEGLU MLP (intermediate {s.I_sh}) as a shared expert' if s.I_sh else ''}",
+        "config": {"workload": workload_name(config, s),
                    "T": s.T, "H": s.H, "E": s.E, "k": s.k, "I": s.I,
                    "weights": (("mxfp4 weights and activations (W4A4)" if s.a4 else "mxfp4") if s.mxfp4
                                else ("nvfp4" if s.nvfp4 else "bf16")),
                    "weight_copies": len(copies),
                    **({"I_shared": s.I_sh} if s.I_sh else {})},
-        "roofline": {
-            "kernel": "grouped_gemm gate/up + GEGLU",
-            "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
-            "frac": achieved / peak,
-            "traffic": traffic_from_profiles(args.config),
-            "alg_bytes_per_launch": alg["gateup_bytes"], "alg_flops_per_launch": alg["gateup_flops"],
-            "avg_launch_us": gateup_launch_us,
-        },
-        "layer": layer,
+        "roofline": roof,
+        "layer": layer_roofline(alg, ms, mfma_peak),
         "step_us": {"mean_back_to_back": ms * 1e3, "per_step_events": spread, "graph_replay": graph_us},
         "stages_us": stage_avg_us,
+    }
+    del copies, ws, out, h, x
+    if s.I_sh:
+        del sh_copies
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res, inp
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the layer holds all experts on one device and this "
+              f"build has no multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
+        return
+
+    main_res, inp = measure(args.config, args.steps, args.warmup, args.rotate, full=not args.no_graph)
+    # The other workloads of the metric, timed in the same process with the
+    # same protocol (fewer steps): the prefill half of the metric (bf16
+    # prefill, Zipf-skewed prefill, MXFP4 experts).
+    extra = {}
+    names = [] if args.extra in ("", "none") else [n for n in args.extra.split(",") if n != args.config]
+    for name in names:
+        r, _ = measure(name, args.extra_steps, args.extra_warmup, args.rotate, full=False)
+        extra[name] = {key: r[key] for key in ("ms_per_step", "tokens_per_s", "steps", "warmup", "dtype",
+                                               "config", "layer", "roofline", "stages_us")}
+    res = {
+        "metric": METRIC,
+        "value": main_res["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": main_res["dtype"],
+        "data": "synthetic",
+        "config": main_res["config"],
+        "roofline": main_res["roofline"],
+        "layer": main_res["layer"],
+        "step_us": main_res["step_us"],
+        "stages_us": main_res["stages_us"],
+        "extra": extra,
         "host": host_info(),
         "context": PAGES_CONTEXT,
     }

@@ -4,7 +4,8 @@
 // The pages fuse the routing as one gating top-k softmax op (Gemma-4-26B-A4B
 // optimisation report, section 5, MoE Router row, 30 calls per step); here
 // the router GEMM is a dense contraction on the matrix cores and the top-k is
-// a wave-wide radix select.
+// k rounds of a wave-wide argmax (one wave per token, the lower expert index
+// winning ties), whose softmax weights are taken over the k selected logits.
 //
 // Logit definition shared by both GEMM paths (split-K below for few tokens,
 // the pipelined grouped GEMM engine for many): the K (hidden) axis is cut

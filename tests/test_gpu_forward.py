@@ -1,9 +1,9 @@
 """End-to-end parity of moe_forward against the fp64 oracle.
 
-Small problems are compared in full; the four Gemma-4-26B-A4B workloads
-(decode T=8, prefill T=2048, Zipf-skewed T=8192, MXFP4 experts T=2048) run in
-the launch configuration the benchmark times and are compared on the whole
-routing table plus a sample of tokens the oracle evaluates one by one."""
+Every problem is compared in full, token by token: small ragged shapes, and
+the four Gemma-4-26B-A4B workloads (decode T=8, prefill T=2048, Zipf-skewed
+T=8192, MXFP4 experts T=2048) plus a Zipf-skewed batch of 32 768 tokens, run
+in the launch configuration the benchmark times."""
 import numpy as np
 import pytest
 import torch
@@ -12,7 +12,7 @@ import moe_inputs as mi
 import oracle
 import mixture_experts_router_amd as moe
 from mixture_experts_router_amd import device as dev
-from gpu_helpers import say, upload, run_forward, to64, check_layer, TIE_MARGIN
+from gpu_helpers import say, upload, run_forward, to64, check_layer
 
 pytestmark = pytest.mark.gpu
 
@@ -83,53 +83,36 @@ def test_forward_is_deterministic_and_reusable(gpu):
 
 
 # ---------------------------------------------------------------- full sizes
-def _sample_tokens(ids, T, n, seed):
-    """Random tokens plus the first/last token and tokens of the busiest expert."""
-    rng = np.random.default_rng(seed)
-    counts = np.bincount(ids.reshape(-1), minlength=ids.max() + 1)
-    hot = int(np.argmax(counts))
-    hot_tok = np.nonzero((ids == hot).any(axis=1))[0]
-    pick = set(rng.choice(T, size=min(n, T), replace=False).tolist())
-    pick |= {0, T - 1}
-    pick |= set(hot_tok[-4:].tolist())
-    return np.array(sorted(pick))
-
-
 @pytest.mark.parametrize("name", ["decode", "prefill", "skew", "mxfp4"])
 def test_forward_full_size(gpu, name):
     s = mi.CONFIGS[name]
     say(f"forward full size {name}: {s}")
-    _full_size_check(mi.make(name, seed=0), name)
+    full_size_check(mi.make(name, seed=0), name)
 
 
 def test_forward_32k_tokens(gpu):
     """The model's layer on 32 768 tokens with the skewed router bias:
     262 144 assignments (16 permutation blocks of 1024 at the hot expert
-    alone), hot experts spanning dozens of 256-row tiles."""
+    alone), hot experts spanning dozens of 256-row tiles, and a down GEMM
+    output (1.5 GB) far above the last-level cache, so its row-tile groups
+    run last to first."""
     s = mi.Shape(T=32768, H=2816, E=128, k=8, I=704, skew=True)
     say(f"forward 32k tokens: {s}")
-    _full_size_check(mi.make(s, seed=3), "32k-skew")
+    full_size_check(mi.make(s, seed=3), "32k-skew")
 
 
-def _full_size_check(inp, name):
+def full_size_check(inp, name):
+    """The whole output against the oracle's whole fp64 forward, plus the
+    routing-table invariants."""
     s = inp.shape
     out, ids, w = run_forward(inp)
     ids_np, w_np = ids.cpu().numpy(), w.cpu().numpy()
-    # whole routing table against fp64 routing
-    L = oracle.router_logits(oracle.bf16_to_f64(inp.x), oracle.bf16_to_f64(inp.w_router), inp.router_bias)
-    rid, rw = oracle.topk_softmax(L, s.k)
-    margin = oracle.routing_margin(L, s.k)
-    keep = margin >= TIE_MARGIN
-    flips = np.array([set(a) != set(b) for a, b in zip(ids_np, rid)])
+    got = to64(out)
+    del out
     counts = np.bincount(ids_np.reshape(-1), minlength=s.E)
-    say(f"  near ties {int((~keep).sum())}, flips outside ties {int((flips & keep).sum())}, "
-        f"counts min {counts.min()} max {counts.max()} empty {int((counts == 0).sum())}")
-    assert not (flips & keep).any()
+    say(f"  counts min {counts.min()} max {counts.max()} empty {int((counts == 0).sum())}")
     assert counts.sum() == s.T * s.k
     assert all(len(set(r)) == s.k for r in ids_np)
-    assert np.abs(w_np.sum(axis=1) - 1).max() <= 1e-6
-    # sampled outputs
-    tok = np.arange(s.T) if s.T <= 16 else _sample_tokens(ids_np, s.T, 40, seed=1)
-    ref = oracle.forward_tokens(inp, tok)
-    check_layer(to64(out)[tok], ids_np[tok], w_np[tok], ref["ids"], ref["w"], ref["out"],
-                ref["margin"], f"{name} ({len(tok)} sampled tokens)")
+    ref = oracle.forward(inp)
+    check_layer(got, ids_np, w_np, ref["ids"], ref["w"], ref["out"], ref["margin"],
+                f"{name} (all {s.T} tokens)")

@@ -55,6 +55,11 @@ CASES = [
     (257, 2816, 128, 8, 704),  # Gemma-4 expert shape, mean 16
     (4096, 512, 128, 8, 256),  # mean 256: 512 down tiles of 256 rows, two rounds per CU
     (1000, 320, 8, 2, 192),    # mean 250, 256-row tiles: last down column tile 64 of 256 wide, last gate/up one half
+    # the prefill tile (256 x 256, sixteen waves; bf16: two token and three
+    # weight stages with spread weight loads; MXFP4: codes and scale rows
+    # straight to LDS) at the Gemma-4 expert shape, K = 2816 / 704
+    (2048, 2816, 128, 8, 704), # the prefill batch: mean 128, single-tile experts stream, hot ones span many tiles
+    (1024, 2816, 16, 4, 704),  # mean 256
 ]
 
 
@@ -138,12 +143,14 @@ def test_down(gpu, T, H, E, k, I, mx):
     assert rel <= REL_L2 and ratio <= 1.0
 
 
-@pytest.mark.parametrize("T,H,I", [(300, 512, 192), (24, 512, 192), (1200, 512, 192), (1200, 2816, 704)])
+@pytest.mark.parametrize("T,H,I", [(150, 512, 192), (300, 512, 192), (24, 512, 192), (1200, 512, 192),
+                                   (1200, 2816, 704)])
 def test_mxfp4_equals_bf16_on_dequantised_weights(gpu, T, H, I):
     """MXFP4 decodes exactly to bf16, so the MXFP4 kernels must reproduce the
-    bf16 kernels fed the decoded weights, bitwise (T=300: 64-row tiles with
-    64-wide K steps; T=24: 16-row tiles, 4-bit gate/up in 256-wide steps
-    against bf16 in 128-wide steps; T=1200: 256-row tiles, 4-bit codes and
+    bf16 kernels fed the decoded weights, bitwise (E=16, k=4; T=150, mean 37
+    rows per expert: 64-row tiles with 64-wide K steps, codes through
+    registers; T=24: 16-row tiles, 4-bit gate/up in 256-wide steps against
+    bf16 in 128-wide steps; T=300 and T=1200: 256-row tiles, 4-bit codes and
     the tile's scale rows straight to LDS, at K = 512 / 192 and at the
     Gemma-4 expert shape, K = 2816 / 704 -- the MFMAs still run in K order)."""
     E, k = 16, 4
@@ -171,6 +178,71 @@ def test_mxfp4_equals_bf16_on_dequantised_weights(gpu, T, H, I):
     torch.cuda.synchronize()
     assert (dev.bf16_bits(h_mx) == dev.bf16_bits(h_bf)).all()
     assert (dev.bf16_bits(y_mx) == dev.bf16_bits(y_bf)).all()
+
+
+def _cache_groups(counts, H, max_bytes, min_mean):
+    """Consecutive expert ranges whose rows' down output (rows x H bf16) fits
+    in max_bytes, each with more than min_mean rows per expert."""
+    groups, e0, rows = [], 0, 0
+    for e, c in enumerate(counts):
+        if rows and (rows + c) * H * 2 > max_bytes:
+            groups.append((e0, e))
+            e0, rows = e, 0
+        rows += c
+    groups.append((e0, len(counts)))
+    for a, b in groups:
+        assert counts[a:b].sum() * H * 2 <= max_bytes and counts[a:b].sum() > min_mean * (b - a)
+    return groups
+
+
+def test_down_reversed_group_order(gpu):
+    """8192 Zipf-routed tokens at the Gemma-4 expert shape: the down GEMM's
+    output (A x H bf16 = 369 MB) exceeds the 256 MB last-level cache, so each
+    XCD runs its row-tile groups last to first.  The whole output is checked
+    against the oracle's elementwise bound, and -- tile arithmetic does not
+    depend on the order tiles run in -- bitwise against forward-order calls
+    on consecutive expert ranges (offsets rebased, outputs under the cache
+    size, still more than 40 rows per expert so the same 256-row tile runs)."""
+    T, H, E, k, I = 8192, 2816, 128, 8, 704
+    say(f"down reversed order T={T} H={H} E={E} k={k} I={I}")
+    inp, ids, counts, offsets, sorted_ids, inv = _setup(T, H, E, k, I, False, seed=11)
+    A = T * k
+    assert A * H * 2 > 256 << 20
+    hb = mi.random_bf16((A, I), sigma=0.5, seed=A + 1)
+    h = dev.to_device(hb)
+    w = dev.to_device(inp.w_down)
+    off = torch.from_numpy(offsets).cuda()
+    y = torch.empty((A, H), dtype=torch.bfloat16, device="cuda")
+    gpu.gemm_down(moe.shape(T, H, E, k, I), h, off, w, None, y)
+    groups = _cache_groups(counts, H, 240 << 20, 40)
+    say(f"  counts min {counts.min()} max {counts.max()}; {len(groups)} forward-order expert ranges")
+    y_parts = torch.empty_like(y)
+    for e0, e1 in groups:
+        lo, hi = int(offsets[e0]), int(offsets[e1])
+        sub_off = torch.from_numpy((offsets[e0:e1 + 1] - lo).astype(np.int32)).cuda()
+        gpu.gemm_down(moe.shape(hi - lo, H, e1 - e0, 1, I), h[lo:hi], sub_off, w[e0:e1], None, y_parts[lo:hi])
+    torch.cuda.synchronize()
+    assert (dev.bf16_bits(y) == dev.bf16_bits(y_parts)).all()
+    del y_parts
+    got = y.float().cpu().numpy().astype(np.float64)
+    del y
+    h64 = oracle.bf16_to_f64(hb)
+    worst, num, den = 0.0, 0.0, 0.0
+    for e in range(E):
+        lo, hi = offsets[e], offsets[e + 1]
+        if hi > lo:
+            _, wd = oracle.expert_weights(inp, e)
+            ref = oracle.down_proj(h64[lo:hi], wd)
+            dY = _acc_err(np.abs(h64[lo:hi]) @ np.abs(wd).T, I)
+            bound = U16 * (np.abs(ref) + dY) + dY + 1e-30
+            d = got[lo:hi] - ref
+            worst = max(worst, float((np.abs(d) / bound).max()))
+            num += float((d * d).sum())
+            den += float((ref * ref).sum())
+    rel = (num / den) ** 0.5
+    say(f"  rel_l2 {rel:.3e} max err/bound {worst:.3f}")
+    assert np.isfinite(got).all()
+    assert rel <= REL_L2 and worst <= 1.0
 
 
 @pytest.mark.parametrize("T,H,k", [(1, 64, 1), (16, 256, 2), (300, 2816, 8), (2048, 2816, 8)])
@@ -202,7 +274,7 @@ def test_combine(gpu, T, H, k):
     assert (dev.bf16_bits(out) == dev.bf16_bits(out2)).all()
 
 
-@pytest.mark.parametrize("T", [300, 24])
+@pytest.mark.parametrize("T", [150, 300, 24])
 def test_nvfp4_equals_bf16_on_dequantised_weights(gpu, T):
     """With every expert's fp32 scale 1, NVFP4 weights decode exactly to bf16
     (E2M1 x E4M3), so the NVFP4 kernels must reproduce the bf16 kernels fed

@@ -15,7 +15,8 @@ pytestmark = pytest.mark.gpu
 
 NV = {
     "tiny-nv": mi.Shape(T=16, H=256, E=8, k=2, I=128, nvfp4=True),
-    "ragged-nv": mi.Shape(T=300, H=512, E=16, k=4, I=192, nvfp4=True),        # 64-row tiles, ragged tails
+    "mid-tiles-nv": mi.Shape(T=150, H=512, E=16, k=4, I=192, nvfp4=True),     # mean 37: 64-row tiles
+    "ragged-nv": mi.Shape(T=300, H=512, E=16, k=4, I=192, nvfp4=True),        # mean 75: 256-row tiles, ragged tails
     "big-tiles-nv": mi.Shape(T=600, H=512, E=16, k=4, I=320, nvfp4=True),     # 256-row tiles
     "decode-like-nv": mi.Shape(T=8, H=768, E=64, k=8, I=704, nvfp4=True),     # 16-row tiles, the model's I
     "skew-nv": mi.Shape(T=200, H=256, E=16, k=4, I=64, nvfp4=True, skew=True),

@@ -13,13 +13,17 @@ from gpu_helpers import say, upload, run_forward, run_forward_shared, to64, chec
 
 pytestmark = pytest.mark.gpu
 
+# Row-block size from the mean rows per expert (T k / E): 16-row tiles up to
+# 16, 64-row tiles up to 40, 256-row tiles above.
 SMALL = {
-    "tiny+mlp": mi.Shape(T=16, H=256, E=8, k=2, I=128, I_sh=192),
+    "tiny+mlp": mi.Shape(T=16, H=256, E=8, k=2, I=128, I_sh=192),             # mean 4: 16-row tiles
     "one-token+mlp": mi.Shape(T=1, H=256, E=8, k=2, I=128, I_sh=128),
-    "ragged+mlp": mi.Shape(T=300, H=512, E=16, k=4, I=192, I_sh=320),          # 2 partial M tiles of the MLP
+    "mid-tiles+mlp": mi.Shape(T=150, H=512, E=16, k=4, I=192, I_sh=256),      # mean 37: 64-row tiles
+    "mid-tiles-mxfp4+mlp": mi.Shape(T=150, H=512, E=16, k=4, I=192, I_sh=256, mxfp4=True),
+    "ragged+mlp": mi.Shape(T=300, H=512, E=16, k=4, I=192, I_sh=320),         # mean 75: 256-row tiles
     "ragged-mxfp4+mlp": mi.Shape(T=300, H=512, E=16, k=4, I=192, I_sh=256, mxfp4=True),
-    "big-tiles+mlp": mi.Shape(T=600, H=512, E=16, k=4, I=128, I_sh=512),      # 256-row tiles
-    "skew+mlp": mi.Shape(T=200, H=256, E=16, k=4, I=64, I_sh=128, skew=True),
+    "big-tiles+mlp": mi.Shape(T=600, H=512, E=16, k=4, I=128, I_sh=512),      # mean 150: 256-row tiles
+    "skew+mlp": mi.Shape(T=200, H=256, E=16, k=4, I=64, I_sh=128, skew=True),  # mean 50: 256-row tiles
 }
 
 
@@ -34,7 +38,7 @@ def test_forward_shared_small_full_compare(gpu, name):
                 ref["margin"], name)
 
 
-@pytest.mark.parametrize("name", ["tiny+mlp", "big-tiles+mlp", "ragged-mxfp4+mlp"])
+@pytest.mark.parametrize("name", ["tiny+mlp", "mid-tiles+mlp", "big-tiles+mlp", "ragged-mxfp4+mlp"])
 def test_zero_mlp_is_bitwise_moe_forward(gpu, name):
     """A zero dense MLP adds exact zeros before the routed sum, so the result
     must be moe_forward's, bit for bit."""
