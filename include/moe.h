@@ -50,11 +50,13 @@
  *     block sums in fp64 before the single rounding of each logit to fp32.
  *   - Ownership: the caller allocates and frees every buffer, including the
  *     workspace.  The library allocates nothing and keeps no pointer after a
- *     call returns.  Inputs are never written.
+ *     call returns.  Inputs are never written.  (moe_forward_noalloc takes
+ *     its workspace from a scratch buffer of the library instead: below.)
  *   - Execution: every call only enqueues kernels on `stream` (a hipStream_t;
  *     NULL is the null stream).  None synchronises or copies data to the
- *     host.  The entry points hold no global mutable state; calls on
- *     different streams with disjoint outputs may overlap.
+ *     host.  The entry points other than moe_forward_noalloc hold no global
+ *     mutable state; their calls on different streams with disjoint outputs
+ *     and workspaces may overlap.
  *   - Errors: the return value is a status.  Shape, pointer, alignment and
  *     workspace checks run on the host before any HIP call; a failing check
  *     launches nothing.  MOE_ERR_HIP reports a launch failure; faults during
@@ -108,7 +110,8 @@ enum {
     MOE_ERR_INVALID_ARGUMENT = -1, /* NULL pointer, T/H/E/I < 1, k < 1, k > E, misalignment */
     MOE_ERR_UNSUPPORTED = -2,      /* a size outside the supported set above */
     MOE_ERR_WORKSPACE = -3,        /* workspace NULL or smaller than required */
-    MOE_ERR_HIP = -4               /* a HIP launch or event call failed */
+    MOE_ERR_HIP = -4,              /* a HIP launch or event call failed */
+    MOE_ERR_SCRATCH_TOO_SMALL = -5 /* moe_forward_noalloc: the shape needs more than its scratch */
 };
 
 typedef void *moe_stream_t; /* hipStream_t */
@@ -259,6 +262,33 @@ int moe_forward_shared(const moe_shape *s, const uint16_t *x,
  */
 int moe_quantize_mx(const uint16_t *src, int64_t rows, int32_t K, uint8_t *codes,
                     uint8_t *scales, moe_stream_t stream);
+
+/*
+ * moe_forward_noalloc -- moe_forward for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same kernels, with the workspace taken from a
+ * scratch buffer inside the library instead of an argument.  It calls no
+ * allocating routine.
+ *   arguments, layout and errors as for moe_forward (no workspace, no stage
+ *   events); MOE_ERR_SCRATCH_TOO_SMALL, before any launch, when
+ *   moe_workspace_bytes(s) > MOE_NOALLOC_SCRATCH_BYTES (64 MiB: the
+ *   Gemma-4 layer shape up to about 1 100 tokens)
+ * Scratch: one static device buffer of MOE_NOALLOC_SCRATCH_BYTES per GPU,
+ * held by every GPU the library runs on until the process ends.  Its
+ * address on the current device is looked up on the first call on that
+ * device, which also enqueues a fill kernel on `stream` that clears its
+ * completion counters; every call leaves them zero again.  All calls on one
+ * GPU share its buffer, and it keeps the last call's contents: calls that
+ * overlap in time on one GPU (other streams, other threads) race and give
+ * undefined results, so order them on one stream or synchronise between
+ * them.  Make the first call on each device outside graph capture.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_forward_noalloc(const moe_shape *s, const uint16_t *x, const uint16_t *w_router,
+                        const float *router_bias, const void *w_gate_up,
+                        const uint8_t *gu_scales, const void *w_down,
+                        const uint8_t *d_scales, uint16_t *out, int32_t *topk_ids_out,
+                        float *topk_w_out, moe_stream_t stream);
 
 /* Workspace bytes moe_forward needs for this shape; 0 for an invalid or
  * unsupported shape.  Monotone in T. */

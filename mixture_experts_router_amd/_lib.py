@@ -12,13 +12,15 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 MOE_W_BF16, MOE_W_MXFP4, MOE_W_MXFP4_A4, MOE_W_NVFP4 = 0, 1, 2, 3
 MOE_FORWARD_STAGES = 5
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARGUMENT", -2: "MOE_ERR_UNSUPPORTED",
-          -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP"}
+          -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP", -5: "MOE_ERR_SCRATCH_TOO_SMALL"}
+# MOE_NOALLOC_SCRATCH_BYTES: the scratch moe_forward_noalloc holds per GPU.
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # Entry points declared in include/moe.h.
 EXPORTS = ("moe_route", "moe_permute", "moe_grouped_gemm_gateup", "moe_grouped_gemm_down",
            "moe_combine", "moe_forward", "moe_forward_shared", "moe_workspace_bytes",
            "moe_workspace_shared_bytes", "moe_route_workspace_bytes", "moe_permute_workspace_bytes",
-           "moe_quantize_mx", "moe_status_string")
+           "moe_quantize_mx", "moe_forward_noalloc", "moe_status_string")
 
 
 class MoeShape(ctypes.Structure):
@@ -59,6 +61,7 @@ def load(path: str = LIB_PATH):
         "moe_grouped_gemm_down": [_S, _P, _P, _P, _P, _P, _P],
         "moe_combine": [_S, _P, _P, _P, _P, _P],
         "moe_forward": [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, c_size, _P, _P],
+        "moe_forward_noalloc": [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
         "moe_forward_shared": [_S, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P,
                                c_size, _P, _P],
     }
@@ -192,6 +195,17 @@ def forward(s, x, w_router, router_bias, w_gate_up, gu_scales, w_down, d_scales,
            lib.moe_forward(ctypes.byref(s), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w_gate_up),
                            _ptr(gu_scales), _ptr(w_down), _ptr(d_scales), _ptr(out), _ptr(topk_ids_out),
                            _ptr(topk_w_out), _ptr(ws), nbytes, _stream(stream), ev))
+
+
+def forward_noalloc(s, x, w_router, router_bias, w_gate_up, gu_scales, w_down, d_scales, out,
+                    topk_ids_out=None, topk_w_out=None, stream=None):
+    """moe_forward_noalloc: moe_forward on the library's own per-GPU scratch
+    (no workspace argument; calls on one GPU must not overlap)."""
+    lib = load()
+    _check("moe_forward_noalloc",
+           lib.moe_forward_noalloc(ctypes.byref(s), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w_gate_up),
+                                   _ptr(gu_scales), _ptr(w_down), _ptr(d_scales), _ptr(out), _ptr(topk_ids_out),
+                                   _ptr(topk_w_out), _stream(stream)))
 
 
 def forward_shared(s, x, w_router, router_bias, w_gate_up, gu_scales, w_down, d_scales, I_sh, w_sh_gate_up,

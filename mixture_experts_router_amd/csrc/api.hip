@@ -3,8 +3,16 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/moe.h"
 #include "moe_launch.h"
+
+// Scratch of moe_forward_noalloc: the library's own device memory, one copy
+// on every GPU the library runs on, held until the process ends.  In host
+// code this name is only a stand-in for the symbol; the device address of
+// each GPU's copy comes from hipGetSymbolAddress (noalloc_scratch below).
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -137,13 +145,48 @@ Workspace carve(const moe_shape *s, void *base, int I_sh = 0) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// Device address of `scratch` on each device, looked up once per device
+// with that device current.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices];
+
+__global__ void zero_words_kernel(uint32_t *p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+// The current device's scratch.  The first call on a device also clears its
+// completion counters (the first MOE_WS_ZERO_BYTES) with a fill kernel on
+// `hs`, ahead of the caller's kernels on that stream; every later call
+// leaves them zero.
+int noalloc_scratch(hipStream_t hs, void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+        constexpr int words = MOE_WS_ZERO_BYTES / 4;
+        zero_words_kernel<<<1, words, 0, hs>>>(static_cast<uint32_t *>(p), words);
+        if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return MOE_OK;
+}
+
 }  // namespace
 
-static int forward_impl(const moe_shape *s, const uint16_t *x, const uint16_t *w_router, const float *router_bias,
-                        const void *w_gate_up, const uint8_t *gu_scales, const void *w_down, const uint8_t *d_scales,
-                        int32_t I_sh, const void *w_sh_gate_up, const uint8_t *sh_gu_scales, const void *w_sh_down,
-                        const uint8_t *sh_d_scales, uint16_t *out, int32_t *topk_ids_out, float *topk_w_out, void *ws,
-                        size_t ws_bytes, moe_stream_t stream, const moe_event_t *stage_events) {
+// Every argument check of moe_forward / moe_forward_shared except the
+// workspace's (host only, launches nothing).
+static int forward_checks(const moe_shape *s, const uint16_t *x, const uint16_t *w_router, const float *router_bias,
+                          const void *w_gate_up, const uint8_t *gu_scales, const void *w_down,
+                          const uint8_t *d_scales, int32_t I_sh, const void *w_sh_gate_up,
+                          const uint8_t *sh_gu_scales, const void *w_sh_down, const uint8_t *sh_d_scales,
+                          const uint16_t *out, const int32_t *topk_ids_out, const float *topk_w_out,
+                          const moe_event_t *stage_events) {
     int st = check_shape(s);
     if (st != MOE_OK) return st;
     if (I_sh < 0) return MOE_ERR_INVALID_ARGUMENT;
@@ -163,9 +206,19 @@ static int forward_impl(const moe_shape *s, const uint16_t *x, const uint16_t *w
     if (stage_events)
         for (int i = 0; i <= MOE_FORWARD_STAGES; ++i)
             if (!stage_events[i]) return MOE_ERR_INVALID_ARGUMENT;
-    const size_t need = carve(s, nullptr, I_sh).bytes;
-    if (!ws || ws_bytes < need || !al16(ws)) return MOE_ERR_WORKSPACE;
+    return MOE_OK;
+}
 
+// The kernel sequence of the layer on checked arguments and a workspace of
+// at least carve(s, nullptr, I_sh).bytes.
+static int forward_launch(const moe_shape *s, const uint16_t *x, const uint16_t *w_router, const float *router_bias,
+                          const void *w_gate_up, const uint8_t *gu_scales, const void *w_down,
+                          const uint8_t *d_scales, int32_t I_sh, const void *w_sh_gate_up,
+                          const uint8_t *sh_gu_scales, const void *w_sh_down, const uint8_t *sh_d_scales,
+                          uint16_t *out, int32_t *topk_ids_out, float *topk_w_out, void *ws, moe_stream_t stream,
+                          const moe_event_t *stage_events) {
+    int st = MOE_OK;
+    const bool a4 = s->w_format == MOE_W_MXFP4_A4;
     Workspace w = carve(s, ws, I_sh);
     int32_t *ids = topk_ids_out ? topk_ids_out : w.ids;
     float *wts = topk_w_out ? topk_w_out : w.w;
@@ -224,6 +277,21 @@ static int forward_impl(const moe_shape *s, const uint16_t *x, const uint16_t *w
     return mark();
 }
 
+static int forward_impl(const moe_shape *s, const uint16_t *x, const uint16_t *w_router, const float *router_bias,
+                        const void *w_gate_up, const uint8_t *gu_scales, const void *w_down, const uint8_t *d_scales,
+                        int32_t I_sh, const void *w_sh_gate_up, const uint8_t *sh_gu_scales, const void *w_sh_down,
+                        const uint8_t *sh_d_scales, uint16_t *out, int32_t *topk_ids_out, float *topk_w_out, void *ws,
+                        size_t ws_bytes, moe_stream_t stream, const moe_event_t *stage_events) {
+    int st = forward_checks(s, x, w_router, router_bias, w_gate_up, gu_scales, w_down, d_scales, I_sh, w_sh_gate_up,
+                            sh_gu_scales, w_sh_down, sh_d_scales, out, topk_ids_out, topk_w_out, stage_events);
+    if (st != MOE_OK) return st;
+    const size_t need = carve(s, nullptr, I_sh).bytes;
+    if (!ws || ws_bytes < need || !al16(ws)) return MOE_ERR_WORKSPACE;
+    return forward_launch(s, x, w_router, router_bias, w_gate_up, gu_scales, w_down, d_scales, I_sh, w_sh_gate_up,
+                          sh_gu_scales, w_sh_down, sh_d_scales, out, topk_ids_out, topk_w_out, ws, stream,
+                          stage_events);
+}
+
 extern "C" {
 
 const char *moe_status_string(int status) {
@@ -233,6 +301,8 @@ const char *moe_status_string(int status) {
         case MOE_ERR_UNSUPPORTED: return "unsupported size or format";
         case MOE_ERR_WORKSPACE: return "workspace missing or too small";
         case MOE_ERR_HIP: return "HIP launch or event call failed";
+        case MOE_ERR_SCRATCH_TOO_SMALL:
+            return "shape needs more scratch than moe_forward_noalloc holds (MOE_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }
@@ -354,6 +424,19 @@ int moe_quantize_mx(const uint16_t *src, int64_t rows, int32_t K, uint8_t *codes
     if (rows == 0) return MOE_OK;
     if (!src || !codes || !scales || !al16(src) || !al16(codes)) return MOE_ERR_INVALID_ARGUMENT;
     return hip_status(moe::launch_quantize_mx(src, rows, K, codes, scales, static_cast<hipStream_t>(stream)));
+}
+
+int moe_forward_noalloc(const moe_shape *s, const uint16_t *x, const uint16_t *w_router, const float *router_bias,
+                        const void *w_gate_up, const uint8_t *gu_scales, const void *w_down, const uint8_t *d_scales,
+                        uint16_t *out, int32_t *topk_ids_out, float *topk_w_out, moe_stream_t stream) {
+    int st = forward_checks(s, x, w_router, router_bias, w_gate_up, gu_scales, w_down, d_scales, 0, nullptr,
+                            nullptr, nullptr, nullptr, out, topk_ids_out, topk_w_out, nullptr);
+    if (st != MOE_OK) return st;
+    if (carve(s, nullptr).bytes > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_SCRATCH_TOO_SMALL;
+    void *ws = nullptr;
+    if ((st = noalloc_scratch(static_cast<hipStream_t>(stream), &ws)) != MOE_OK) return st;
+    return forward_launch(s, x, w_router, router_bias, w_gate_up, gu_scales, w_down, d_scales, 0, nullptr, nullptr,
+                          nullptr, nullptr, out, topk_ids_out, topk_w_out, ws, stream, nullptr);
 }
 
 size_t moe_workspace_shared_bytes(const moe_shape *s, int32_t I_sh) {

@@ -211,3 +211,27 @@ def test_nvfp4_header_size():
     assert buf.size == 256 + 6
     assert buf[:8].view(np.float32).tolist() == [1.5, -2.0]
     assert (buf[8:256] == 0).all() and buf[256:].tolist() == list(range(6))
+
+
+def test_forward_noalloc_argument_checks(lib):
+    """moe_forward_noalloc checks its arguments like moe_forward, and rejects
+    shapes whose workspace exceeds its built-in scratch, before any launch."""
+    F = FAKE
+    call = lambda s, x=F, wr=F, gu=F, gus=None, d=F, ds=None, out=F: lib.moe_forward_noalloc(
+        ctypes.byref(s), x, wr, None, gu, gus, d, ds, out, None, None, None)
+    assert call(S(T=0)) == -1
+    assert call(S(H=96)) == -2
+    assert call(S(), x=None) == -1
+    assert call(S(), out=MIS) == -1
+    assert call(S(), gus=F) == -1                         # bf16 weights come without scales
+    assert call(S(f=1)) == -1                             # MXFP4 weights need scales
+    text = open(HEADER).read()
+    assert "#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in text
+    assert _lib.NOALLOC_SCRATCH_BYTES == 64 << 20
+    fits = _lib.MoeShape(1000, 2816, 128, 8, 704, 0)
+    too_big = _lib.MoeShape(2048, 2816, 128, 8, 704, 0)
+    assert lib.moe_workspace_bytes(ctypes.byref(fits)) <= _lib.NOALLOC_SCRATCH_BYTES
+    assert lib.moe_workspace_bytes(ctypes.byref(too_big)) > _lib.NOALLOC_SCRATCH_BYTES
+    assert call(too_big) == -5
+    assert call(_lib.MoeShape(2048, 2816, 128, 8, 704, 1), gus=F, ds=F) == -5
+    assert "scratch" in lib.moe_status_string(-5).decode()
