@@ -16,10 +16,32 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into mixture_experts_router_amd/libmoe.so."""
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
+# The same library with its host code (argument checks, workspace carve,
+# launch sequence) under AddressSanitizer and UndefinedBehaviorSanitizer, for
+# the CPU tests of the C ABI; the device code is compiled as for LIB.
+HOSTSAN_LIB = os.path.join(HERE, "libmoe_hostsan.so")
+HOSTSAN_FLAGS = [
+    "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-omit-frame-pointer", "-shared-libsan", "-g",
+]
+
+
+def asan_runtime() -> str:
+    """Path of the clang AddressSanitizer runtime that HOSTSAN_LIB links."""
+    import glob
+    hits = sorted(glob.glob(os.path.join(os.path.dirname(os.path.dirname(HIPCC)), "llvm", "lib", "clang", "*",
+                                         "lib", "linux", "libclang_rt.asan-x86_64.so")))
+    if not hits:
+        raise RuntimeError("clang AddressSanitizer runtime not found under the ROCm LLVM")
+    return hits[-1]
+
+
+def build(verbose: bool = False, hostsan: bool = False) -> str:
+    """Compile every HIP source into mixture_experts_router_amd/libmoe.so
+    (hostsan: into libmoe_hostsan.so with sanitised host code)."""
+    out = HOSTSAN_LIB if hostsan else LIB
+    tmp = out + ".tmp"
+    cmd = [HIPCC, *FLAGS, *(HOSTSAN_FLAGS if hostsan else []), "-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -28,8 +50,8 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{msgs}")
     if verbose and msgs.strip():
         print(msgs, flush=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -18,7 +18,9 @@ MIS = FAKE + 2            # misaligned
 
 @pytest.fixture(scope="module")
 def lib():
-    return moe.load()
+    # MOE_TEST_LIB: run these checks against another build of the library
+    # (the host-sanitised one, from test_sanitizers.py)
+    return moe.load(os.environ.get("MOE_TEST_LIB", _lib.LIB_PATH))
 
 
 def declared():
