@@ -199,7 +199,7 @@ struct GemmTile {
     static_assert(!NV_ || (MX && !A4_), "NVFP4 is a variant of the MXFP4 weight path");
     static constexpr int SCW = SC_PER >= 4 ? SC_PER / 4 : 1;     // scale bytes per row and step in 32-bit words
     static constexpr int SS_BYTES = SC_TILE ? SC_ROW * BN : MX ? SC_PER * BN : 0;
-    static constexpr int SS_SLOTS = SC_TILE ? 1 : NS;   // per-tile scales: one buffer
+    static constexpr int SS_SLOTS = SC_TILE ? 1 : NSB;   // per-tile scales: one buffer
     // W4A4 block scales of a stage: 8 bytes (blocks 8 kt .. 8 kt + 7) per
     // weight row and per token row, one row per thread.
     static constexpr bool SC_PAIR_M = MI >= 2;   // token rows paired like weight rows
@@ -210,7 +210,9 @@ struct GemmTile {
     // count the direct-to-LDS ones), which only a two-stage pipeline affords
     static_assert(!A4_ || NS == 2, "W4A4: two stages");
     static_assert(!A4_ || (NI % 2 == 0 && (!SC_PAIR_M || MI % 2 == 0)), "W4A4: scale rows in pairs");
-    static_assert(NSB == NS || (NS == 2 && NSB == 3 && !MX && !A4_), "a deeper weight ring: bf16, 2 + 3 stages");
+    // a deeper weight ring: two token stages and three or more weight stages
+    // (bf16 tiles, or 4-bit codes straight to LDS)
+    static_assert(NSB == NS || (NS == 2 && NSB >= 3 && !A4_ && (!MX || WDMA)), "weight ring deeper than the token ring");
     // LDS: token stages, weight stages, block scales (4-bit weights), W4A4
     // scale pairs, carved from one buffer (byte offsets, 16-byte aligned)
     static constexpr int A_OFF = 0;
@@ -861,14 +863,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
     // step kt issues the token tile of kt + NS - 1, then the weight tile of
     // kt + NSB - 1.  At the top of step kt the loads issued after the last
     // one it needs are: NSB == NS: the NS - 2 later steps' loads; NS = 2,
-    // NSB = 3: the weight tile of kt + 1, issued right after the token tile
-    // of kt.
+    // NSB > 2: the weight tile of kt + NSB - 2, issued (in step kt - 1)
+    // right after the token tile of kt.  (In step 0 this waits for more than
+    // it needs: the prologue's later weight tiles.)
     auto wait_for = [&](int kt) {
         if constexpr (NSB == NS) {
             const int later = min(NS - 2, KT - 1 - kt);   // steps issued after kt
             wait_vm_lgkm0_rt(later * dma_per_step);
         } else {
-            wait_vm_lgkm0_rt(kt + 1 < KT ? dmab_per_step : 0);
+            wait_vm_lgkm0_rt(kt + NSB - 2 < KT ? dmab_per_step : 0);
         }
     };
     if (MX && !WDMA) issue_mx(0);
@@ -1142,11 +1145,19 @@ static hipError_t launch_sized(const GemmArgs &a, int A, hipStream_t st) {
         // Waves 4 x 4: each weight fragment is expanded by four waves, but
         // two waves per SIMD multiply at <= 128 rows (2 x 8 waves, two
         // expansions per fragment: 217 us; 4 x 4: 194 us for the gate/up at
-        // 2048 tokens).
+        // 2048 tokens).  Two token stages and a deeper ring of code stages
+        // (8 KB each): six for gate/up (K = 2816: 44 steps), four for down
+        // (K = 704: 11 steps, where a long prologue costs more than it
+        // hides).  Measured at 2048 tokens against three + three stages:
+        // gate/up 201 -> 187 us (six) and 192 us (four), down 122.5 ->
+        // 120.4 us (four) and 125.5 us (six).
+        constexpr int NSB = MODE == kGateUp ? 6 : 4;
+        using Tile = GemmTile<256, 256, 4, 4, MODE, MX, 2, 64, false, false, true, NSB>;
         const bool direct = (reinterpret_cast<uintptr_t>(a.w) & 15u) == 0 &&
                             (reinterpret_cast<uintptr_t>(a.scales) & 1u) == 0 && a.K >= 128 &&
-                            a.K / 32 <= GemmTile<256, 256, 4, 4, MODE, MX, 3, 64, false, false, true>::SC_ROW;
-        if (direct && a.sh_rows == 0) return launch_cfg<256, 256, 4, 4, MODE, MX, 3, 64, false, false, true>(a, A, st);
+                            a.K / 32 <= Tile::SC_ROW;
+        if (direct && a.sh_rows == 0)
+            return launch_cfg<256, 256, 4, 4, MODE, MX, 2, 64, false, false, true, NSB>(a, A, st);
     }
     if constexpr (!MX)
         return launch_cfg<256, 256, 4, 4, MODE, MX, 2, 64, false, NV, false, 3>(a, A, st);
@@ -1154,13 +1165,16 @@ static hipError_t launch_sized(const GemmArgs &a, int A, hipStream_t st) {
         return launch_cfg<256, 256, 4, 2, MODE, MX, 3, 64, false, NV>(a, A, st);
 }
 
-// W4A4: the same tile choice as bf16 activations, K steps of 256 codes.
+// W4A4: K steps of 256 codes, and the row-block rule of the bf16 tiles (a
+// typical expert's rows in one row tile, so its weights stream once): 16
+// rows up to a mean of 16 rows per expert, 64 up to 40, 256 above
+// (measured, layer step: 512 tokens 180.0 -> 155.4 us against 32-row tiles,
+// 1024 tokens 208.5 -> 193.2 us against 64-row tiles).
 template <int MODE>
 static hipError_t launch_sized_a4(const GemmArgs &a, int A, hipStream_t st) {
     const int mean_rows = A / a.E;
     if (mean_rows <= 16) return launch_cfg<16, 128, 1, 4, MODE, false, 2, 64, true>(a, A, st);
-    if (mean_rows <= 40) return launch_cfg<32, 128, 2, 2, MODE, false, 2, 64, true>(a, A, st);
-    if (mean_rows <= 80) return launch_cfg<64, 128, 2, 2, MODE, false, 2, 64, true>(a, A, st);
+    if (mean_rows <= 40) return launch_cfg<64, 128, 2, 2, MODE, false, 2, 64, true>(a, A, st);
     return launch_cfg<256, 256, 4, 4, MODE, false, 2, 64, true>(a, A, st);
 }
 

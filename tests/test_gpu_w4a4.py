@@ -60,9 +60,13 @@ def test_quantizer_special_values(gpu):
 
 A4 = {
     "tiny-a4": mi.Shape(T=16, H=256, E=8, k=2, I=128, mxfp4=True, a4=True),          # down K: half a step
-    "ragged-a4": mi.Shape(T=300, H=512, E=16, k=4, I=192, mxfp4=True, a4=True),
+    "mid-tiles-a4": mi.Shape(T=120, H=512, E=16, k=4, I=192, mxfp4=True, a4=True),    # mean 30: 64-row tiles
+    "ragged-a4": mi.Shape(T=300, H=512, E=16, k=4, I=192, mxfp4=True, a4=True),      # mean 75: 256-row tiles
     "big-tiles-a4": mi.Shape(T=600, H=512, E=16, k=4, I=320, mxfp4=True, a4=True),   # 256-row tiles
     "decode-like-a4": mi.Shape(T=8, H=768, E=64, k=8, I=704, mxfp4=True, a4=True),   # the model's I
+    # the Gemma-4 layer at 300 tokens (mean 19): 64-row tiles with the model's
+    # K (gate/up 2816 = 11 steps of 256, down 704 = 2.75 steps)
+    "model-mid-tiles-a4": mi.Shape(T=300, H=2816, E=128, k=8, I=704, mxfp4=True, a4=True),
     "skew-a4": mi.Shape(T=200, H=256, E=16, k=4, I=64, mxfp4=True, a4=True, skew=True),
 }
 
