@@ -72,6 +72,7 @@ class Shape:
     I_sh: int = 0           # intermediate size of the always-on dense MLP (0: none)
     a4: bool = False        # with mxfp4: activations quantised to MXFP4 too (W4A4)
     nvfp4: bool = False     # expert weights stored as NVFP4 (E2M1, E4M3 per 16, fp32 per expert)
+    nv_a4: bool = False     # with nvfp4: activations quantised to NVFP4 too (NVFP4 W4A4)
 
     @property
     def A(self) -> int:
@@ -96,7 +97,18 @@ CONFIGS = {
     # the decode layer with MXFP4 / NVFP4 expert weights (bf16 activations)
     "mxfp4_decode": Shape(T=8, H=2816, E=128, k=8, I=704, mxfp4=True),
     "nvfp4_decode": Shape(T=8, H=2816, E=128, k=8, I=704, nvfp4=True),
+    # NVFP4 weights and activations (the Gemma-4-26B-A4B-NVFP4 checkpoint's
+    # scheme) at decode and prefill sizes
+    "nvfp4_a4_decode": Shape(T=8, H=2816, E=128, k=8, I=704, nvfp4=True, nv_a4=True),
+    "nvfp4_a4": Shape(T=2048, H=2816, E=128, k=8, I=704, nvfp4=True, nv_a4=True),
 }
+
+# Input (activation) scale of the NVFP4 W4A4 matmuls, for x and for h: a
+# checkpoint calibrates it as the activation's amax over 6 x 448; here a
+# fixed 2^-8 stands in (E4M3 block scales of amax * 2^8 / 6 stay below 448
+# for |values| < 10.5, above the x ~ N(0, 1) and h magnitudes of these
+# synthetic layers, and in E4M3's normal range for amax > 0.09).
+NV_INPUT_SCALE = np.float32(2.0 ** -8)
 
 
 def make_shape(name_or_shape) -> Shape:
@@ -234,6 +246,10 @@ class Inputs:
     d_scales: Optional[np.ndarray] = None    # uint8 [E, H, I/32] for MXFP4, E4M3 [E, H, I/16] for NVFP4
     gu_global: Optional[np.ndarray] = None   # float32 [E]: NVFP4 per-expert scale of gate/up
     d_global: Optional[np.ndarray] = None    # float32 [E]: NVFP4 per-expert scale of down
+    # NVFP4 W4A4: the fp32 input scales of the gate/up and down matmuls'
+    # activations (calibration constants of the checkpoint; here fixed)
+    gu_input_scale: Optional[np.float32] = None
+    d_input_scale: Optional[np.float32] = None
     # dense MLP (shape.I_sh > 0): uint16 [2 I_sh, H] and [H, I_sh], or MXFP4
     # codes [2 I_sh, H/2], [H, I_sh/2] with scales [2 I_sh, H/32], [H, I_sh/32]
     w_sh_gate_up: Optional[np.ndarray] = None
@@ -313,6 +329,8 @@ def make(config, seed: int = 0) -> Inputs:
         raise ValueError("W4A4 (a4) needs MXFP4 weights (mxfp4)")
     if s.nvfp4 and (s.mxfp4 or s.I_sh > 0):
         raise ValueError("NVFP4 experts exclude MXFP4 and the dense MLP")
+    if s.nv_a4 and not s.nvfp4:
+        raise ValueError("NVFP4 activations (nv_a4) need NVFP4 weights (nvfp4)")
     T, H, E, k, I = s.T, s.H, s.E, s.k, s.I
     w_router, w_gu, w_d, state = _weights(s, seed)
     rng = np.random.default_rng(seed)
@@ -351,6 +369,8 @@ def make(config, seed: int = 0) -> Inputs:
             nv = (gu_q, gu_s, gu_g, d_q, d_s, d_g)
             _MX_CACHE[key] = nv
         inp.w_gate_up, inp.gu_scales, inp.gu_global, inp.w_down, inp.d_scales, inp.d_global = nv
+        if s.nv_a4:
+            inp.gu_input_scale = inp.d_input_scale = NV_INPUT_SCALE
     if s.I_sh > 0:
         d = _Drawer(np.random.default_rng([seed, 2112]))
         sh_gu = d.into(np.empty((2 * s.I_sh, H), dtype=np.uint16), s.w_sigma)

@@ -33,6 +33,15 @@ gelu_pytorch_tanh):
       checkpoint of the verification report) decoded to fp64 before O7:
       E2M1 element x FP8 E4M3 scale of its 16-element block x the matrix's
       fp32 scale
+  O13 NVFP4 weights and activations (nv_a4): x, and the bf16 h of every
+      GEGLU, are quantised per 16 consecutive K values to NVFP4 before their
+      matmuls (the verification report's quantisation table, section 2.3,
+      gives 4-bit float with group size 16 for weights and activations):
+      relative to the tensor's fp32 input scale g, a block's E4M3 scale is
+      the nearest E4M3 value to amax / (6 g) (ties to the even code,
+      saturating at 448), and each value v / (scale g) goes to the nearest
+      E2M1 value (ties to the even code, saturating at 6); these decisions
+      are taken in fp32, as a kernel takes them
   O10 shapes with a dense MLP (I_sh > 0): out[t] += MLP(x[t]) with
       MLP(x) = (gelu_tanh(x Wg^T) * (x Wu^T)) Wd^T, the same GEGLU form as an
       expert, weight 1 (the block runs its dense MLP of intermediate 2112 next
@@ -47,7 +56,10 @@ design notes of the repository.
 Parity status: O2-O8 are pinned by the dense brute force (`dense_forward`) and
 by closed-form special cases in the CPU test suite; O9 is pinned by the E2M1
 table of the OCP Microscaling Formats v1.0 specification; O12's E4M3 table by
-torch's float8_e4m3fn decoding of all finite codes.  Against the real
+torch's float8_e4m3fn decoding of all finite codes; O13's E4M3 rounding by
+torch's float8_e4m3fn cast at every midpoint and by the generator's own
+encoder, its block rule by a per-value scalar rule, and a one-expert layer by
+a textbook torch GEGLU FFN on the quantised operands.  Against the real
 Gemma-4 layer parity is unpinned: the pages print no activations or weights.
 """
 from __future__ import annotations
@@ -62,7 +74,7 @@ __all__ = [
     "down_proj", "combine", "expert_weights", "forward", "forward_tokens",
     "dense_forward", "routing_margin", "shared_weights", "shared_mlp",
     "mx_quantize", "mx_dequantize", "mx_round", "round_to_bf16",
-    "e4m3_to_f64", "nvfp4_to_f64",
+    "e4m3_to_f64", "nvfp4_to_f64", "e4m3_nearest", "nv_quantize", "nv_dequantize", "nv_round",
 ]
 
 
@@ -145,6 +157,69 @@ def nvfp4_to_f64(packed, scales, glob) -> np.ndarray:
         raise ValueError("E4M3 NaN code used as a scale")
     vals = _E2M1[codes].reshape(*codes.shape[:-1], K // 16, 16) * sc[..., None]
     return vals.reshape(*codes.shape[:-1], K) * float(np.float32(glob))
+
+
+# ---------------------------------------------------------------- O13
+def e4m3_nearest(v) -> np.ndarray:
+    """Code of the E4M3 value nearest to each non-negative v (O13): the
+    least distance over the 127 finite non-negative codes, the even code on
+    a tie (round half to even), 448 (code 0x7E) for everything from 448 up."""
+    v = np.asarray(v, dtype=np.float64)
+    if np.any(v < 0) or np.any(np.isnan(v)):
+        raise ValueError("E4M3 scales are taken of non-negative amax values")
+    grid = _E4M3[:127]                                   # codes 0x00 .. 0x7E, ascending values
+    dist = np.abs(v[..., None] - grid)                   # [..., 127]
+    best = dist.min(axis=-1, keepdims=True)
+    score = np.where(dist == best, np.arange(127) % 2, 2)   # even codes first on a tie
+    code = np.argmin(score, axis=-1)
+    return np.where(v >= 448.0, 0x7E, code).astype(np.uint8)
+
+
+def nv_quantize(v, g):
+    """NVFP4 codes of rows of values, per 16 along the last axis, relative to
+    the tensor's fp32 scale g (O13).  Returns (codes uint8 [..., K], one
+    E2M1 code per value, and E4M3 block-scale codes uint8 [..., K/16]).
+
+    In fp32, as a kernel computes them: amax of the block, s = amax / (6 g)
+    (6 g rounded to fp32 first), its E4M3 code; then step = scale * g and
+    each value's quotient v / step, both rounded to fp32, whose nearest E2M1
+    code (ties to the even code, saturating at 6, the sign kept) is the
+    value's code.  A block whose scale code is 0 gets all-zero codes."""
+    v = np.asarray(v, dtype=np.float64)
+    K = v.shape[-1]
+    if K % 16:
+        raise ValueError("NVFP4 blocks need K % 16 == 0")
+    v32 = v.astype(np.float32)
+    if not np.array_equal(v32.astype(np.float64), v):
+        raise ValueError("NVFP4 activations must be fp32 values (here: bf16)")
+    g32 = np.float32(g)
+    blk = v32.reshape(*v.shape[:-1], K // 16, 16)
+    amax = np.max(np.abs(blk), axis=-1)
+    with np.errstate(over="ignore"):
+        s = amax / (np.float32(6.0) * g32)                 # float32 arithmetic
+    sc = e4m3_nearest(s.astype(np.float64))
+    step = (e4m3_to_f64(sc).astype(np.float32) * g32)    # float32
+    safe = np.where(step > 0, step, np.float32(1.0))
+    q = (blk / safe[..., None]).astype(np.float64)       # float32 quotient, widened exactly
+    dist = np.abs(np.abs(q)[..., None] - np.asarray(_E2M1_MAG))
+    best = dist.min(axis=-1, keepdims=True)
+    score = np.where(dist == best, np.where(np.arange(8) % 2 == 0, 0, 1), 2)
+    code = np.argmin(score, axis=-1).astype(np.uint8) | np.where(np.signbit(q), 8, 0).astype(np.uint8)
+    code = np.where((step > 0)[..., None], code, 0).astype(np.uint8)
+    return code.reshape(v.shape), sc
+
+
+def nv_dequantize(codes, scales, g) -> np.ndarray:
+    """Values of one-code-per-value NVFP4 data: E2M1 x E4M3 block scale x g."""
+    codes = np.asarray(codes, dtype=np.int64)
+    K = codes.shape[-1]
+    vals = _E2M1[codes].reshape(*codes.shape[:-1], K // 16, 16) * e4m3_to_f64(scales)[..., None]
+    return vals.reshape(codes.shape) * float(np.float32(g))
+
+
+def nv_round(v, g) -> np.ndarray:
+    """v quantised to NVFP4 relative to the scale g and decoded again."""
+    return nv_dequantize(*nv_quantize(v, g), g)
 
 
 def expert_weights(inp, e: int):
@@ -371,6 +446,22 @@ def combine(Y: np.ndarray, inv: np.ndarray, w: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------- whole layer
+def _expert_input(inp, x64):
+    """The expert matmuls' view of x: itself, or quantised (O11 MXFP4, O13
+    NVFP4 relative to the gate/up input scale)."""
+    if getattr(inp.shape, "nv_a4", False):
+        return nv_round(x64, inp.gu_input_scale)
+    return mx_round(x64) if getattr(inp.shape, "a4", False) else x64
+
+
+def _down_input(inp, h):
+    """The down matmul's view of an expert's h: h, or its bf16 rounding
+    quantised (O11 MXFP4, O13 NVFP4 relative to the down input scale)."""
+    if getattr(inp.shape, "nv_a4", False):
+        return nv_round(round_to_bf16(h), inp.d_input_scale)
+    return mx_round(round_to_bf16(h)) if getattr(inp.shape, "a4", False) else h
+
+
 def forward(inp, logits_fp32: np.ndarray | None = None) -> dict:
     """The routed layer, step by step (O1-O9).
 
@@ -386,7 +477,7 @@ def forward(inp, logits_fp32: np.ndarray | None = None) -> dict:
     counts, offsets = counts_offsets(ids, E)
     sorted_ids, inv = permutation(ids)
     a4 = getattr(s, "a4", False)
-    xe = mx_round(x64) if a4 else x64     # what the expert matmuls read (O11)
+    xe = _expert_input(inp, x64)          # what the expert matmuls read (O11, O13)
     Y = np.zeros((T * k, H), dtype=np.float64)
     Hh = np.zeros((T * k, I), dtype=np.float64)
     for e in range(E):
@@ -396,9 +487,7 @@ def forward(inp, logits_fp32: np.ndarray | None = None) -> dict:
         rows = sorted_ids[lo:hi]
         X = xe[rows // k]
         wgu, wd = expert_weights(inp, e)
-        h = gateup_geglu(X, wgu)
-        if a4:
-            h = mx_round(round_to_bf16(h))
+        h = _down_input(inp, gateup_geglu(X, wgu))
         Hh[lo:hi] = h
         Y[lo:hi] = down_proj(h, wd)
     out = combine(Y, inv, w) + shared_mlp(xe, shared_weights(inp), a4)
@@ -418,7 +507,7 @@ def forward_tokens(inp, tokens) -> dict:
     L = router_logits(x64, bf16_to_f64(inp.w_router), inp.router_bias)
     ids, w = topk_softmax(L, k)
     a4 = getattr(s, "a4", False)
-    xe = mx_round(x64) if a4 else x64
+    xe = _expert_input(inp, x64)
     out = np.zeros((len(tokens), s.H), dtype=np.float64)
     cache = {}
     for i in range(len(tokens)):
@@ -427,9 +516,7 @@ def forward_tokens(inp, tokens) -> dict:
             if e not in cache:
                 cache[e] = expert_weights(inp, e)
             wgu, wd = cache[e]
-            h = gateup_geglu(xe[i:i + 1], wgu)
-            if a4:
-                h = mx_round(round_to_bf16(h))
+            h = _down_input(inp, gateup_geglu(xe[i:i + 1], wgu))
             out[i] += w[i, j] * down_proj(h, wd)[0]
     out += shared_mlp(xe, shared_weights(inp), a4)
     return dict(logits=L, ids=ids, w=w, out=out, margin=routing_margin(L, k))

@@ -551,3 +551,113 @@ def test_nvfp4_single_expert_is_a_dense_geglu_ffn_on_decoded_weights():
     ref = (h @ torch.tensor(wd).T).numpy()
     out = oracle.forward(inp)["out"]
     assert _rel(out, ref) < 1e-12
+
+
+# ------------------------------------------------------------------ NVFP4 activations (O13)
+def _e4m3_midpoints():
+    """Every value the E4M3 rounding must decide: the finite non-negative
+    grid, the midpoints between neighbours, and values just off them."""
+    grid = oracle.e4m3_to_f64(np.arange(127))
+    mids = (grid[:-1] + grid[1:]) / 2
+    return grid, mids, np.nextafter(mids, np.inf), np.nextafter(mids, -np.inf)
+
+
+def test_e4m3_nearest_matches_torch_rounding_below_saturation():
+    """torch's float8_e4m3fn cast rounds to the nearest even code; it agrees
+    on the grid, every midpoint (ties to even) and random values up to the
+    saturation point (the cast overflows to NaN from 464 on, where E4M3
+    saturates at 448 by the OCP conversion)."""
+    grid, mids, up, down = _e4m3_midpoints()
+    rng = np.random.default_rng(1)
+    rand = np.exp(rng.uniform(np.log(2.0 ** -12), np.log(460.0), 4000))
+    v = np.concatenate([grid, mids, up, down, rand, [0.0, 2.0 ** -10, 3 * 2.0 ** -11]])
+    v = v[v < 464.0].astype(np.float32).astype(np.float64)      # the fp32 values a kernel rounds
+    ref = torch.from_numpy(v.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert (oracle.e4m3_nearest(v) == ref).all()
+
+
+def test_e4m3_nearest_saturation_and_generator_encoder():
+    assert oracle.e4m3_nearest(np.array([448.0, 460.0, 464.0, 1e6, np.inf])).tolist() == [0x7E] * 5
+    assert oracle.e4m3_nearest(np.array([0.0, 2.0 ** -9, 2.0 ** -10])).tolist() == [0, 1, 0]   # tie -> even
+    # the generator's independently written encoder (arithmetic on the
+    # exponent and mantissa) agrees everywhere it is defined
+    grid, mids, up, down = _e4m3_midpoints()
+    v = np.concatenate([grid, mids, up, down, [500.0, 1e4]])
+    assert (oracle.e4m3_nearest(v) == mi.e4m3_encode(v)).all()
+
+
+def _nv_scalar(block, g):
+    """One 16-value block by the rule written out per value: fp32 amax, scale
+    through the generator's E4M3 encoder, E2M1 through the scalar rule."""
+    from oracle import moe_oracle as om
+    f32 = np.float32
+    amax = max(abs(f32(v)) for v in block)
+    s = f32(amax) / (f32(6.0) * f32(g))
+    sc = int(mi.e4m3_encode(np.array([float(s)]))[0])
+    step = f32(oracle.e4m3_to_f64(sc)) * f32(g)
+    if step == 0:
+        return [0] * len(block), sc
+    return [om._e2m1_code(float(f32(v) / step)) for v in block], sc
+
+
+def test_nv_quantizer_matches_scalar_rule():
+    rng = np.random.default_rng(3)
+    rows = rng.standard_normal((6, 64)) * np.exp(rng.uniform(-6, 3, (6, 1)))
+    rows = mi.bf16_bits_to_f32(mi.f32_to_bf16_bits(rows.astype(np.float32))).astype(np.float64)
+    for g in (2.0 ** -8, 0.0037, 1.0):
+        codes, sc = oracle.nv_quantize(rows, g)
+        for r in range(rows.shape[0]):
+            for b in range(4):
+                c, s = _nv_scalar(rows[r, 16 * b:16 * b + 16], g)
+                assert sc[r, b] == s and codes[r, 16 * b:16 * b + 16].tolist() == c
+
+
+def test_nv_quantizer_representable_values_ties_saturation_zero():
+    g = 2.0 ** -8
+    # a block of E2M1 grid values times one E4M3 scale times g, whose amax is
+    # 6 x scale x g, comes back unchanged
+    rng = np.random.default_rng(4)
+    for sc in (1, 8, 0x38, 0x55, 0x7E):
+        s = oracle.e4m3_to_f64(sc)
+        e2m1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+        vals = rng.choice(np.concatenate([e2m1, -e2m1]), 16)
+        vals[3] = 6.0
+        block = vals * s * g
+        codes, scale = oracle.nv_quantize(block[None], g)
+        assert scale[0, 0] == sc
+        assert (oracle.nv_dequantize(codes, scale, g)[0] == block).all()
+    # E2M1 midpoints relative to the step go to the even code
+    step = 2.0 * g                                   # scale code 0x38 = 1.0 ... times 2: amax 12 g
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, -0.25, -5.0, 0, 0, 0, 0, 0, 0]) * step
+    codes, scale = oracle.nv_quantize(mids[None], g)
+    assert oracle.e4m3_to_f64(scale[0, 0]) == 2.0
+    assert codes[0, :10].tolist() == [0, 2, 2, 4, 4, 6, 6, 7, 8, 14]
+    # saturation: amax / (6 g) above 448 takes scale 448 and codes saturate at 6
+    big = np.full(16, 1e4 * g)
+    big[0] = -3e4 * g
+    codes, scale = oracle.nv_quantize(big[None], g)
+    assert scale[0, 0] == 0x7E and codes[0, 0] == 15 and (codes[0, 1:] == 7).all()
+    # an all-zero block, and negative zeros: scale code 0, all-zero codes
+    z = np.zeros((1, 16))
+    z[0, 1] = -0.0
+    codes, scale = oracle.nv_quantize(z, g)
+    assert scale.tolist() == [[0]] and (codes == 0).all()
+
+
+def test_nvfp4_w4a4_single_expert_is_a_quantised_textbook_ffn():
+    """E = 1, k = 1, NVFP4 W4A4: the torch GEGLU FFN on the decoded weights
+    and the quantised x, with h rounded to bf16 and quantised before the
+    down projection."""
+    s = mi.Shape(T=6, H=64, E=1, k=1, I=32, nvfp4=True, nv_a4=True)
+    inp = mi.make(s, seed=13)
+    r = oracle.forward(inp)
+    wgu, wd = oracle.expert_weights(inp, 0)
+    xq = torch.from_numpy(oracle.nv_round(oracle.bf16_to_f64(inp.x), inp.gu_input_scale))
+    g = torch.nn.functional.linear(xq, torch.from_numpy(wgu[:32]))
+    u = torch.nn.functional.linear(xq, torch.from_numpy(wgu[32:]))
+    h = torch.nn.functional.gelu(g, approximate="tanh") * u
+    hq = torch.from_numpy(oracle.nv_round(oracle.round_to_bf16(h.numpy()), inp.d_input_scale))
+    ref = torch.nn.functional.linear(hq, torch.from_numpy(wd)).numpy()
+    assert _rel(r["out"], ref) <= 1e-13
+    plain = oracle.forward(mi.make(mi.Shape(T=6, H=64, E=1, k=1, I=32, nvfp4=True), seed=13))["out"]
+    assert _rel(plain, ref) > 1e-4
