@@ -42,7 +42,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--config", default="decode", help="tiny|decode|prefill|skew|mxfp4|decode_shared|w4a4|mxfp4_decode|nvfp4_decode")
+    p.add_argument("--config", default="decode",
+                   help="tiny|decode|prefill|skew|mxfp4|decode_shared|w4a4|mxfp4_decode|nvfp4_decode|"
+                        "nvfp4_a4_decode|nvfp4_a4")
     p.add_argument("--rotate", type=int, default=4, help="device copies of the weights cycled per step")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle timing")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -216,6 +218,7 @@ def workload_name(config, s):
             f"hidden {s.H}, {s.E} experts, top-{s.k}, intermediate {s.I}, "
             f"GEGLU, {'MXFP4' if s.mxfp4 else ('NVFP4' if s.nvfp4 else 'bf16')} expert weights"
             f"{' and MXFP4 activations (W4A4)' if s.a4 else ''}"
+            f"{' and NVFP4 activations (W4A4)' if s.nv_a4 else ''}"
             f"{', Zipf(1.2) router bias' if s.skew else ''}"
             f"{f', plus the dense GEGLU MLP (intermediate {s.I_sh}) as a shared expert' if s.I_sh else ''}")
 
@@ -231,7 +234,7 @@ def measure(config, K, warmup, rotate, full):
     t_gen = time.perf_counter()
     inp = mi.make(config, seed=0)
     s = inp.shape
-    sh = moe.shape(s.T, s.H, s.E, s.k, s.I, mxfp4=s.mxfp4, a4=s.a4, nvfp4=s.nvfp4)
+    sh = moe.shape(s.T, s.H, s.E, s.k, s.I, mxfp4=s.mxfp4, a4=s.a4, nvfp4=s.nvfp4, nv_a4=s.nv_a4)
     x = dev.to_device(inp.x)
     wr = dev.to_device(inp.w_router)
     bias = dev.to_device(inp.router_bias) if inp.router_bias is not None else None
@@ -239,9 +242,11 @@ def measure(config, K, warmup, rotate, full):
     d0 = dev.to_device(inp.w_down)
     gus = dev.to_device(inp.gu_scales) if s.mxfp4 else None
     ds = dev.to_device(inp.d_scales) if s.mxfp4 else None
-    if s.nvfp4:   # one buffer per matrix: the fp32 expert scales, then the E4M3 codes
-        gus = dev.to_device(moe.nvfp4_scale_buffer(inp.gu_global, inp.gu_scales))
-        ds = dev.to_device(moe.nvfp4_scale_buffer(inp.d_global, inp.d_scales))
+    if s.nvfp4:   # one buffer per matrix: the fp32 expert scales (+ input scale), then the E4M3 codes
+        gus = dev.to_device(moe.nvfp4_scale_buffer(inp.gu_global, inp.gu_scales,
+                                                   inp.gu_input_scale if s.nv_a4 else 1.0))
+        ds = dev.to_device(moe.nvfp4_scale_buffer(inp.d_global, inp.d_scales,
+                                                  inp.d_input_scale if s.nv_a4 else 1.0))
     copies = [(gu0, d0)] + [(gu0.clone(), d0.clone()) for _ in range(max(0, rotate - 1))]
     if s.I_sh:   # the dense MLP's weights rotate with the experts'
         sg0, sd0 = dev.to_device(inp.w_sh_gate_up), dev.to_device(inp.w_sh_down)
@@ -318,7 +323,7 @@ def measure(config, K, warmup, rotate, full):
     torch.cuda.synchronize()
     if not torch.equal(r_ids.cpu(), ids.cpu()):
         raise RuntimeError("moe_route and moe_forward disagree on the routing")
-    if s.I_sh or s.a4:
+    if s.I_sh or s.a4 or s.nv_a4:
         # the dense-MLP tiles (and the W4A4 GEMMs) run inside moe_forward
         # only: take the gate/up stage's duration from the stage events
         # (includes the gap an event adds, and for W4A4 the quantisation of x)
@@ -388,7 +393,8 @@ def measure(config, K, warmup, rotate, full):
         "config": {"workload": workload_name(config, s),
                    "T": s.T, "H": s.H, "E": s.E, "k": s.k, "I": s.I,
                    "weights": (("mxfp4 weights and activations (W4A4)" if s.a4 else "mxfp4") if s.mxfp4
-                               else ("nvfp4" if s.nvfp4 else "bf16")),
+                               else (("nvfp4 weights and activations (W4A4)" if s.nv_a4 else "nvfp4")
+                                     if s.nvfp4 else "bf16")),
                    "weight_copies": len(copies),
                    **({"I_shared": s.I_sh} if s.I_sh else {})},
         "roofline": roof,

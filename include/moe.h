@@ -32,8 +32,9 @@
  *     same E2M1 codes with one FP8 E4M3 scale per 16 consecutive K values
  *     and one fp32 scale per expert matrix; a weight is E2M1(code) x
  *     E4M3(block scale) x matrix scale.  Their scale argument is one buffer:
- *     MOE_NVFP4_HEADER_BYTES(E) bytes holding the E fp32 matrix scales, then
- *     the E4M3 codes [E][rows][K/16].  E4M3 is the OCP 8-bit floating point
+ *     MOE_NVFP4_HEADER_BYTES(E) bytes holding the E fp32 matrix scales and
+ *     the activation input scale (NVFP4_A4), then the E4M3 codes
+ *     [E][rows][K/16].  E4M3 is the OCP 8-bit floating point
  *     format (exponent bias 7, largest value 448, no infinities); its NaN
  *     codes (0x7F, 0xFF) are undefined as scales.
  *   - Assignment a = t*k + j is slot j of token t.  A = T*k.
@@ -84,7 +85,7 @@ typedef struct moe_shape {
     int32_t E;        /* experts */
     int32_t k;        /* experts per token */
     int32_t I;        /* expert intermediate size */
-    int32_t w_format; /* MOE_W_BF16, MOE_W_MXFP4, MOE_W_MXFP4_A4 or MOE_W_NVFP4 */
+    int32_t w_format; /* MOE_W_BF16, MOE_W_MXFP4, MOE_W_MXFP4_A4, MOE_W_NVFP4 or MOE_W_NVFP4_A4 */
 } moe_shape;
 
 /* Expert weight format.  MOE_W_MXFP4_A4 (W4A4): MXFP4 weights, and the
@@ -98,12 +99,25 @@ typedef struct moe_shape {
  * (no dense MLP) and moe_quantize_mx only; the per-step GEMM entry points
  * return MOE_ERR_UNSUPPORTED for it.  MOE_W_NVFP4: NVFP4 expert weights
  * (above) with bf16 activations, through moe_forward and the per-step GEMM
- * entry points; not with a dense MLP. */
-enum { MOE_W_BF16 = 0, MOE_W_MXFP4 = 1, MOE_W_MXFP4_A4 = 2, MOE_W_NVFP4 = 3 };
+ * entry points; not with a dense MLP.  MOE_W_NVFP4_A4: NVFP4 weights and
+ * NVFP4 activations (the Gemma-4-26B-A4B-NVFP4 verification report, section
+ * 2.3: weights and activations 4-bit float in groups of 16): x, and each
+ * expert's bf16 h, are quantised per 16 consecutive K values relative to the
+ * activation's fp32 input scale g (a calibration constant, slot E of the
+ * gate/up and down scale headers): block scale = the E4M3 value nearest to
+ * amax / (6 g) (ties to the even code, 448 from 448 up), each value v /
+ * (block scale * g) to the nearest E2M1 code (ties to the even code,
+ * saturating at 6), decided in fp32 (moe_quantize_nv).  gfx950 has no FP4
+ * matrix instruction with E4M3 scales: both operands are multiplied on the
+ * bf16 matrix cores as their exact decoded values (E2M1 x E4M3 has at most
+ * six significant bits), with fp32 sums scaled by the weight's matrix scale
+ * times g.  Through moe_forward only; not with a dense MLP. */
+enum { MOE_W_BF16 = 0, MOE_W_MXFP4 = 1, MOE_W_MXFP4_A4 = 2, MOE_W_NVFP4 = 3, MOE_W_NVFP4_A4 = 4 };
 
 /* Bytes in front of the E4M3 codes of an NVFP4 scale buffer: the E fp32
- * matrix scales, padded to a multiple of 256. */
-#define MOE_NVFP4_HEADER_BYTES(E) ((((size_t)(E) * 4u + 255u) / 256u) * 256u)
+ * matrix scales and one fp32 activation input scale (slot E, read by
+ * MOE_W_NVFP4_A4 only), padded to a multiple of 256. */
+#define MOE_NVFP4_HEADER_BYTES(E) (((((size_t)(E) + 1u) * 4u + 255u) / 256u) * 256u)
 
 enum {
     MOE_OK = 0,
@@ -289,6 +303,20 @@ int moe_forward_noalloc(const moe_shape *s, const uint16_t *x, const uint16_t *w
                         const uint8_t *gu_scales, const void *w_down,
                         const uint8_t *d_scales, uint16_t *out, int32_t *topk_ids_out,
                         float *topk_w_out, moe_stream_t stream);
+
+/*
+ * moe_quantize_nv -- NVFP4 codes and E4M3 block scales of bf16 rows, per 16
+ * consecutive values, relative to an fp32 input scale (the activation
+ * conversion described with MOE_W_NVFP4_A4).
+ *   src          [rows][K] bf16, 16-byte aligned; K > 0, K % 16 == 0
+ *   input_scale  one fp32 (device), 4-byte aligned
+ *   codes        [rows][K/2] out, two E2M1 codes per byte (even index low),
+ *                8-byte aligned
+ *   scales       [rows][K/16] out, E4M3 codes
+ *   rows >= 0 (0 launches nothing)
+ */
+int moe_quantize_nv(const uint16_t *src, int64_t rows, int32_t K, const float *input_scale,
+                    uint8_t *codes, uint8_t *scales, moe_stream_t stream);
 
 /* Workspace bytes moe_forward needs for this shape; 0 for an invalid or
  * unsupported shape.  Monotone in T. */

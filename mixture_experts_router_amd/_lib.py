@@ -9,7 +9,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe.so")
 
-MOE_W_BF16, MOE_W_MXFP4, MOE_W_MXFP4_A4, MOE_W_NVFP4 = 0, 1, 2, 3
+MOE_W_BF16, MOE_W_MXFP4, MOE_W_MXFP4_A4, MOE_W_NVFP4, MOE_W_NVFP4_A4 = 0, 1, 2, 3, 4
 MOE_FORWARD_STAGES = 5
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARGUMENT", -2: "MOE_ERR_UNSUPPORTED",
           -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP", -5: "MOE_ERR_SCRATCH_TOO_SMALL"}
@@ -20,7 +20,7 @@ NOALLOC_SCRATCH_BYTES = 64 << 20
 EXPORTS = ("moe_route", "moe_permute", "moe_grouped_gemm_gateup", "moe_grouped_gemm_down",
            "moe_combine", "moe_forward", "moe_forward_shared", "moe_workspace_bytes",
            "moe_workspace_shared_bytes", "moe_route_workspace_bytes", "moe_permute_workspace_bytes",
-           "moe_quantize_mx", "moe_forward_noalloc", "moe_status_string")
+           "moe_quantize_mx", "moe_quantize_nv", "moe_forward_noalloc", "moe_status_string")
 
 
 class MoeShape(ctypes.Structure):
@@ -75,6 +75,8 @@ def load(path: str = LIB_PATH):
         f.restype = c_size
     lib.moe_quantize_mx.argtypes = [_P, ctypes.c_int64, ctypes.c_int32, _P, _P, _P]
     lib.moe_quantize_mx.restype = c_int
+    lib.moe_quantize_nv.argtypes = [_P, ctypes.c_int64, ctypes.c_int32, _P, _P, _P, _P]
+    lib.moe_quantize_nv.restype = c_int
     lib.moe_workspace_shared_bytes.argtypes = [_S, ctypes.c_int32]
     lib.moe_workspace_shared_bytes.restype = c_size
     lib.moe_status_string.argtypes = [c_int]
@@ -83,27 +85,30 @@ def load(path: str = LIB_PATH):
     return lib
 
 
-def shape(T, H, E, k, I, mxfp4=False, a4=False, nvfp4=False) -> MoeShape:
+def shape(T, H, E, k, I, mxfp4=False, a4=False, nvfp4=False, nv_a4=False) -> MoeShape:
     if nvfp4:
-        fmt = MOE_W_NVFP4
+        fmt = MOE_W_NVFP4_A4 if nv_a4 else MOE_W_NVFP4
     else:
         fmt = MOE_W_MXFP4_A4 if a4 else (MOE_W_MXFP4 if mxfp4 else MOE_W_BF16)
     return MoeShape(T, H, E, k, I, fmt)
 
 
 def nvfp4_header_bytes(E: int) -> int:
-    """MOE_NVFP4_HEADER_BYTES(E): bytes of fp32 matrix scales, padded to 256,
-    in front of the E4M3 codes of an NVFP4 scale buffer."""
-    return (E * 4 + 255) // 256 * 256
+    """MOE_NVFP4_HEADER_BYTES(E): bytes of the E fp32 matrix scales and the
+    fp32 activation input scale, padded to 256, in front of the E4M3 codes of
+    an NVFP4 scale buffer."""
+    return ((E + 1) * 4 + 255) // 256 * 256
 
 
-def nvfp4_scale_buffer(matrix_scales, block_scales):
-    """Host bytes of one NVFP4 scale argument: the E fp32 matrix scales
-    (padded to nvfp4_header_bytes(E)) followed by the E4M3 codes
-    [E][rows][K/16] (numpy arrays in, a flat uint8 numpy array out)."""
+def nvfp4_scale_buffer(matrix_scales, block_scales, input_scale=1.0):
+    """Host bytes of one NVFP4 scale argument: the E fp32 matrix scales and
+    the activation input scale (read with NVFP4 activations only), padded to
+    nvfp4_header_bytes(E), followed by the E4M3 codes [E][rows][K/16] (numpy
+    arrays in, a flat uint8 numpy array out)."""
     import numpy as np
-    g = np.ascontiguousarray(matrix_scales, dtype=np.float32).reshape(-1)
-    head = np.zeros(nvfp4_header_bytes(g.size), dtype=np.uint8)
+    g = np.concatenate([np.ascontiguousarray(matrix_scales, dtype=np.float32).reshape(-1),
+                        np.array([input_scale], dtype=np.float32)])
+    head = np.zeros(nvfp4_header_bytes(g.size - 1), dtype=np.uint8)
     head[:g.size * 4] = g.view(np.uint8)
     return np.concatenate([head, np.ascontiguousarray(block_scales, dtype=np.uint8).reshape(-1)])
 
@@ -220,6 +225,16 @@ def forward_shared(s, x, w_router, router_bias, w_gate_up, gu_scales, w_down, d_
                                   _ptr(gu_scales), _ptr(w_down), _ptr(d_scales), I_sh, _ptr(w_sh_gate_up),
                                   _ptr(sh_gu_scales), _ptr(w_sh_down), _ptr(sh_d_scales), _ptr(out),
                                   _ptr(topk_ids_out), _ptr(topk_w_out), _ptr(ws), nbytes, _stream(stream), ev))
+
+
+def quantize_nv(src, input_scale, codes, scales, stream=None):
+    """moe_quantize_nv: NVFP4 codes [rows][K/2] and E4M3 scales [rows][K/16]
+    of bf16 rows src [rows][K] relative to input_scale (a one-element fp32
+    device tensor)."""
+    lib = load()
+    rows, K = src.shape
+    _check("moe_quantize_nv", lib.moe_quantize_nv(_ptr(src), rows, K, _ptr(input_scale), _ptr(codes),
+                                                  _ptr(scales), _stream(stream)))
 
 
 def quantize_mx(src, codes, scales, stream=None):

@@ -23,12 +23,14 @@ size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 bool al16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool al4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
+bool is_nvfp4(const moe_shape *s) { return s->w_format == MOE_W_NVFP4 || s->w_format == MOE_W_NVFP4_A4; }
+
 int check_shape(const moe_shape *s) {
     if (!s) return MOE_ERR_INVALID_ARGUMENT;
     if (s->T < 1 || s->H < 1 || s->E < 1 || s->k < 1 || s->I < 1) return MOE_ERR_INVALID_ARGUMENT;
     if (s->k > s->E) return MOE_ERR_INVALID_ARGUMENT;
     if (s->w_format != MOE_W_BF16 && s->w_format != MOE_W_MXFP4 && s->w_format != MOE_W_MXFP4_A4 &&
-        s->w_format != MOE_W_NVFP4)
+        s->w_format != MOE_W_NVFP4 && s->w_format != MOE_W_NVFP4_A4)
         return MOE_ERR_UNSUPPORTED;
     if (s->H % 64 != 0 || s->I % 64 != 0) return MOE_ERR_UNSUPPORTED;
     if (s->E > 1024 || s->k > 32) return MOE_ERR_UNSUPPORTED;
@@ -73,25 +75,29 @@ int check_weights(const moe_shape *s, const void *w, const uint8_t *scales) {
         if (s->w_format == MOE_W_MXFP4_A4 && (reinterpret_cast<uintptr_t>(scales) & 1u))
             return MOE_ERR_INVALID_ARGUMENT;
         // NVFP4: the fp32 header and one 32-bit load of 4 scales per row and step
-        if (s->w_format == MOE_W_NVFP4 && !al4(scales)) return MOE_ERR_INVALID_ARGUMENT;
+        if (is_nvfp4(s) && !al4(scales)) return MOE_ERR_INVALID_ARGUMENT;
     }
     return MOE_OK;
 }
 
 // The grouped GEMMs' view of an expert weight argument: format, block
-// scales and (NVFP4) the per-expert fp32 scales in front of them.
+// scales, (NVFP4) the per-expert fp32 scales in front of them and (NVFP4
+// activations) the activations' fp32 input scale that follows those.
 struct WeightView {
     moe::WeightFormat fmt;
     const uint8_t *scales;
     const float *global;
+    const float *input;
 };
 
 WeightView weight_view(const moe_shape *s, const uint8_t *scales) {
-    if (s->w_format == MOE_W_NVFP4)
-        return {moe::WeightFormat::kNVFP4, scales + MOE_NVFP4_HEADER_BYTES(s->E),
-                reinterpret_cast<const float *>(scales)};
-    if (s->w_format == MOE_W_MXFP4) return {moe::WeightFormat::kMXFP4, scales, nullptr};
-    return {moe::WeightFormat::kBF16, scales, nullptr};
+    if (is_nvfp4(s)) {
+        const float *head = reinterpret_cast<const float *>(scales);
+        return {moe::WeightFormat::kNVFP4, scales + MOE_NVFP4_HEADER_BYTES(s->E), head,
+                s->w_format == MOE_W_NVFP4_A4 ? head + s->E : nullptr};
+    }
+    if (s->w_format == MOE_W_MXFP4) return {moe::WeightFormat::kMXFP4, scales, nullptr, nullptr};
+    return {moe::WeightFormat::kBF16, scales, nullptr, nullptr};
 }
 
 struct Workspace {
@@ -103,6 +109,7 @@ struct Workspace {
     int32_t *counts, *offsets, *block_hist, *sorted_ids, *inv;
     uint16_t *h, *y;
     uint8_t *xq, *xs, *hq, *hs;   // W4A4 only: MXFP4 codes and scales of x and h
+    uint16_t *xf;                 // NVFP4 activations only: x decoded after quantisation [T][H]
     uint16_t *h_sh;          // dense MLP (I_sh > 0 only): h rows [T][I_sh]
     float *y_sh32;           // and its down partial sums [nsplit][T][H]
     size_t bytes;
@@ -135,6 +142,7 @@ Workspace carve(const moe_shape *s, void *base, int I_sh = 0) {
     w.xs = a4 ? reinterpret_cast<uint8_t *>(take(T * (size_t)s->H / 32)) : nullptr;
     w.hq = a4 ? reinterpret_cast<uint8_t *>(take(A * (size_t)s->I / 2)) : nullptr;
     w.hs = a4 ? reinterpret_cast<uint8_t *>(take(A * (size_t)s->I / 32)) : nullptr;
+    w.xf = s->w_format == MOE_W_NVFP4_A4 ? reinterpret_cast<uint16_t *>(take(T * (size_t)s->H * 2)) : nullptr;
     w.h_sh = I_sh > 0 ? reinterpret_cast<uint16_t *>(take(T * (size_t)I_sh * sizeof(uint16_t))) : nullptr;
     w.y_sh32 = I_sh > 0 ? reinterpret_cast<float *>(take((size_t)moe::shared_splits(I_sh, s->I) * T * s->H *
                                                           sizeof(float)))
@@ -192,7 +200,7 @@ static int forward_checks(const moe_shape *s, const uint16_t *x, const uint16_t 
     if (I_sh < 0) return MOE_ERR_INVALID_ARGUMENT;
     const bool a4 = s->w_format == MOE_W_MXFP4_A4;
     if (I_sh > 0) {
-        if (a4 || s->w_format == MOE_W_NVFP4 || I_sh % 64 != 0) return MOE_ERR_UNSUPPORTED;
+        if (a4 || is_nvfp4(s) || I_sh % 64 != 0) return MOE_ERR_UNSUPPORTED;
         if ((st = check_weights(s, w_sh_gate_up, sh_gu_scales)) != MOE_OK) return st;
         if ((st = check_weights(s, w_sh_down, sh_d_scales)) != MOE_OK) return st;
     }
@@ -262,13 +270,26 @@ static int forward_launch(const moe_shape *s, const uint16_t *x, const uint16_t 
         if (st != MOE_OK) return st;
         return mark();
     }
+    // NVFP4 activations: x and h quantised to NVFP4 (relative to the input
+    // scales in the weights' scale headers) and decoded without those scales,
+    // which the GEMM epilogues apply with the weights' (both quantisations
+    // belong to the stages that multiply them; h is quantised in place)
+    const bool nv_a4 = s->w_format == MOE_W_NVFP4_A4;
+    const uint16_t *x_mm = x;
+    if (nv_a4) {
+        st = hip_status(moe::launch_quantize_nv(x, T, H, gu.input, nullptr, nullptr, w.xf, hs));
+        if (st != MOE_OK) return st;
+        x_mm = w.xf;
+    }
     // the shared expert (if any) is an extra group of the same two launches
     const moe::SharedGroup sh_gu{x, w_sh_gate_up, sh_gu_scales, w.h_sh, nullptr, T, I_sh};
     const moe::SharedGroup sh_d{w.h_sh, w_sh_down, sh_d_scales, nullptr, w.y_sh32, T, I_sh};
-    st = hip_status(moe::launch_gateup(x, w.sorted_ids, k, w.offsets, w_gate_up, gu.scales, gu.global, w.h, A, H,
-                                       E, I, gu.fmt, I_sh > 0 ? &sh_gu : nullptr, hs));
+    st = hip_status(moe::launch_gateup(x_mm, w.sorted_ids, k, w.offsets, w_gate_up, gu.scales, gu.global, gu.input,
+                                       w.h, A, H, E, I, gu.fmt, I_sh > 0 ? &sh_gu : nullptr, hs));
     if (st != MOE_OK || (st = mark()) != MOE_OK) return st;
-    st = hip_status(moe::launch_down(w.h, w.offsets, w_down, dn.scales, dn.global, w.y, A, H, E, I, dn.fmt,
+    if (nv_a4 && (st = hip_status(moe::launch_quantize_nv(w.h, A, I, dn.input, nullptr, nullptr, w.h, hs))) != MOE_OK)
+        return st;
+    st = hip_status(moe::launch_down(w.h, w.offsets, w_down, dn.scales, dn.global, dn.input, w.y, A, H, E, I, dn.fmt,
                                      I_sh > 0 ? &sh_d : nullptr, hs));
     if (st != MOE_OK || (st = mark()) != MOE_OK) return st;
     st = hip_status(moe::launch_combine(w.y, w.inv, wts, w.y_sh32, I_sh > 0 ? moe::shared_splits(I_sh, I) : 0, out,
@@ -369,9 +390,9 @@ int moe_grouped_gemm_gateup(const moe_shape *s, const uint16_t *x, const int32_t
     if (!al16(x) || !al16(h) || !al4(offsets)) return MOE_ERR_INVALID_ARGUMENT;
     if (sorted_ids && !al4(sorted_ids)) return MOE_ERR_INVALID_ARGUMENT;
     if ((st = check_weights(s, w_gate_up, gu_scales)) != MOE_OK) return st;
-    if (s->w_format == MOE_W_MXFP4_A4) return MOE_ERR_UNSUPPORTED;
+    if (s->w_format == MOE_W_MXFP4_A4 || s->w_format == MOE_W_NVFP4_A4) return MOE_ERR_UNSUPPORTED;
     const WeightView wv = weight_view(s, gu_scales);
-    return hip_status(moe::launch_gateup(x, sorted_ids, s->k, offsets, w_gate_up, wv.scales, wv.global, h,
+    return hip_status(moe::launch_gateup(x, sorted_ids, s->k, offsets, w_gate_up, wv.scales, wv.global, nullptr, h,
                                          s->T * s->k, s->H, s->E, s->I, wv.fmt, nullptr,
                                          static_cast<hipStream_t>(stream)));
 }
@@ -383,10 +404,10 @@ int moe_grouped_gemm_down(const moe_shape *s, const uint16_t *h, const int32_t *
     if (!h || !offsets || !y) return MOE_ERR_INVALID_ARGUMENT;
     if (!al16(h) || !al16(y) || !al4(offsets)) return MOE_ERR_INVALID_ARGUMENT;
     if ((st = check_weights(s, w_down, d_scales)) != MOE_OK) return st;
-    if (s->w_format == MOE_W_MXFP4_A4) return MOE_ERR_UNSUPPORTED;
+    if (s->w_format == MOE_W_MXFP4_A4 || s->w_format == MOE_W_NVFP4_A4) return MOE_ERR_UNSUPPORTED;
     const WeightView wv = weight_view(s, d_scales);
-    return hip_status(moe::launch_down(h, offsets, w_down, wv.scales, wv.global, y, s->T * s->k, s->H, s->E, s->I,
-                                       wv.fmt, nullptr, static_cast<hipStream_t>(stream)));
+    return hip_status(moe::launch_down(h, offsets, w_down, wv.scales, wv.global, nullptr, y, s->T * s->k, s->H, s->E,
+                                       s->I, wv.fmt, nullptr, static_cast<hipStream_t>(stream)));
 }
 
 int moe_combine(const moe_shape *s, const uint16_t *y, const int32_t *inv, const float *topk_w,
@@ -437,6 +458,18 @@ int moe_forward_noalloc(const moe_shape *s, const uint16_t *x, const uint16_t *w
     if ((st = noalloc_scratch(static_cast<hipStream_t>(stream), &ws)) != MOE_OK) return st;
     return forward_launch(s, x, w_router, router_bias, w_gate_up, gu_scales, w_down, d_scales, 0, nullptr, nullptr,
                           nullptr, nullptr, out, topk_ids_out, topk_w_out, ws, stream, nullptr);
+}
+
+int moe_quantize_nv(const uint16_t *src, int64_t rows, int32_t K, const float *input_scale, uint8_t *codes,
+                    uint8_t *scales, moe_stream_t stream) {
+    if (rows < 0 || K <= 0) return MOE_ERR_INVALID_ARGUMENT;
+    if (K % 16 != 0) return MOE_ERR_UNSUPPORTED;
+    if (rows == 0) return MOE_OK;
+    if (!src || !input_scale || !codes || !scales || !al16(src) || !al4(input_scale) ||
+        (reinterpret_cast<uintptr_t>(codes) & 7u))
+        return MOE_ERR_INVALID_ARGUMENT;
+    return hip_status(moe::launch_quantize_nv(src, rows, K, input_scale, codes, scales, nullptr,
+                                              static_cast<hipStream_t>(stream)));
 }
 
 size_t moe_workspace_shared_bytes(const moe_shape *s, int32_t I_sh) {

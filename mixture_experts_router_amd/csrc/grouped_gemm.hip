@@ -77,8 +77,11 @@ struct GemmArgs {
     // W4A4: `a` holds MXFP4 codes [rows][K/2] and a_scales [rows][K/32]
     const uint8_t *a_scales;
     // NVFP4 weights: `scales` holds E4M3 codes [E][rows][K/16] and w_global
-    // the fp32 scale of each expert's matrix [E]
+    // the fp32 scale of each expert's matrix [E]; with NVFP4 activations,
+    // a_global points at their fp32 input scale (the activations arrive
+    // decoded without it), else nullptr
     const float *w_global;
+    const float *a_global;
     // Row-tile groups run last to first on each XCD (large row blocks only)
     int reverse_groups;
 };
@@ -949,8 +952,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
 
     // ---- epilogue: lane holds weight rows 4*lk .. 4*lk+3 of tile j for the
     // token lrow of token tile i.  NVFP4: the expert matrix's fp32 scale
-    // multiplies the fp32 sums (before the GEGLU).
-    const float gsc = NV ? p.w_global[e] : 1.0f;
+    // (times the activations' input scale for NVFP4 activations) multiplies
+    // the fp32 sums (before the GEGLU).
+    const float gsc = NV ? p.w_global[e] * (p.a_global ? *p.a_global : 1.0f) : 1.0f;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
         const int t = wm * WTM + i * 16 + lrow;
@@ -1206,10 +1210,12 @@ hipError_t launch_down_a4(const uint8_t *hq, const uint8_t *hs, const int32_t *o
 }
 
 hipError_t launch_gateup(const uint16_t *x, const int32_t *sorted_ids, int k, const int32_t *offsets,
-                         const void *w, const uint8_t *scales, const float *w_global, uint16_t *h, int A, int H,
-                         int E, int I, WeightFormat fmt, const SharedGroup *sh, hipStream_t st) {
+                         const void *w, const uint8_t *scales, const float *w_global, const float *a_global,
+                         uint16_t *h, int A, int H, int E, int I, WeightFormat fmt, const SharedGroup *sh,
+                         hipStream_t st) {
     GemmArgs a{x, sorted_ids, k, offsets, w, scales, h, E, H, I, I, 2 * I, 0, 0, 0, nullptr, nullptr};
     a.w_global = w_global;
+    a.a_global = a_global;
     if (sh) {   // every token through the shared gate/up weights [2 I_sh][H]
         a.sh_rows = sh->rows;
         a.sh_a = x;
@@ -1228,10 +1234,11 @@ hipError_t launch_gateup(const uint16_t *x, const int32_t *sorted_ids, int k, co
 }
 
 hipError_t launch_down(const uint16_t *h, const int32_t *offsets, const void *w, const uint8_t *scales,
-                       const float *w_global, uint16_t *y, int A, int H, int E, int I, WeightFormat fmt,
-                       const SharedGroup *sh, hipStream_t st) {
+                       const float *w_global, const float *a_global, uint16_t *y, int A, int H, int E, int I,
+                       WeightFormat fmt, const SharedGroup *sh, hipStream_t st) {
     GemmArgs a{h, nullptr, 1, offsets, w, scales, y, E, I, H, I, H, 0, 0, 0, nullptr, nullptr};
     a.w_global = w_global;
+    a.a_global = a_global;
     a.reverse_groups = reverse_down_groups(A, H);
     if (sh) {   // the shared h rows [rows][I_sh] through the shared down weights [H][I_sh]
         a.sh_rows = sh->rows;

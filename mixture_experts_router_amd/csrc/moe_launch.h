@@ -65,13 +65,16 @@ inline int shared_splits(int I_sh, int I_expert) {
 // Expert weight formats of the grouped GEMMs: bf16; MXFP4 (scales: E8M0
 // [E][rows][K/32]); NVFP4 (scales: E4M3 [E][rows][K/16], w_global: the fp32
 // scale of each expert's matrix [E]; no shared group).
+// a_global (NVFP4 only, or nullptr): the fp32 input scale of activations
+// that arrive decoded without it (NVFP4 activations), applied with w_global.
 enum class WeightFormat { kBF16, kMXFP4, kNVFP4 };
 hipError_t launch_gateup(const uint16_t *x, const int32_t *sorted_ids, int k, const int32_t *offsets,
-                         const void *w, const uint8_t *scales, const float *w_global, uint16_t *h, int A, int H,
-                         int E, int I, WeightFormat fmt, const SharedGroup *sh, hipStream_t st);
+                         const void *w, const uint8_t *scales, const float *w_global, const float *a_global,
+                         uint16_t *h, int A, int H, int E, int I, WeightFormat fmt, const SharedGroup *sh,
+                         hipStream_t st);
 hipError_t launch_down(const uint16_t *h, const int32_t *offsets, const void *w, const uint8_t *scales,
-                       const float *w_global, uint16_t *y, int A, int H, int E, int I, WeightFormat fmt,
-                       const SharedGroup *sh, hipStream_t st);
+                       const float *w_global, const float *a_global, uint16_t *y, int A, int H, int E, int I,
+                       WeightFormat fmt, const SharedGroup *sh, hipStream_t st);
 // W4A4 grouped GEMMs: activations as MXFP4 codes [rows][K/2] + E8M0 scales
 // [rows][K/32] (launch_quantize_mx), weights MXFP4; K a multiple of 64.
 hipError_t launch_gateup_a4(const uint8_t *xq, const uint8_t *xs, const int32_t *sorted_ids, int k,
@@ -82,6 +85,12 @@ hipError_t launch_down_a4(const uint8_t *hq, const uint8_t *hs, const int32_t *o
 // MXFP4 codes and scales of bf16 rows [rows][K], K a multiple of 32.
 hipError_t launch_quantize_mx(const uint16_t *src, long long rows, int K, uint8_t *codes, uint8_t *scales,
                               hipStream_t st);
+// NVFP4 quantisation of bf16 rows [rows][K] (K a multiple of 16) relative
+// to the fp32 input scale *g: codes [rows][K/2] and E4M3 scales [rows][K/16]
+// (both or neither), and/or the decoded values without g as bf16 into dq
+// [rows][K] (dq may be src itself).
+hipError_t launch_quantize_nv(const uint16_t *src, long long rows, int K, const float *g, uint8_t *codes,
+                              uint8_t *scales, uint16_t *dq, hipStream_t st);
 // y_sh32 (optional, [nsplit][T][H] fp32): partial sums of a shared-expert
 // output, added (in order) with weight 1 before the routed rows.
 hipError_t launch_combine(const uint16_t *y, const int32_t *inv, const float *w, const float *y_sh32, int nsplit,

@@ -67,6 +67,106 @@ __global__ __launch_bounds__(256) void quantize_mx_kernel(const uint16_t *__rest
     scales[row * bpr + blk] = (uint8_t)(e + 127);
 }
 
+// NVFP4 quantisation of bf16 rows, per 16 consecutive values, relative to
+// the tensor's fp32 input scale g (the Gemma-4-26B-A4B-NVFP4 verification
+// report, section 2.3: 4-bit float activations in groups of 16).  In fp32:
+// s = amax / (6 g) goes to the nearest E4M3 value (ties to the even code,
+// 448 from 448 up), step = that scale * g, and each value v to the E2M1 code
+// nearest to v / step (ties to the even code, saturating at 6, v's sign
+// bit); a block whose scale is 0 gets zero codes.  Outputs: codes [rows][K/2]
+// (even index in the low nibble) and E4M3 scale codes [rows][K/16], and/or
+// the decoded values without g, E2M1 x scale, as bf16 (exact: at most six
+// significant bits), which the bf16 matrix cores multiply.
+
+// Nearest E4M3 value of s >= 0 (OCP 8-bit floating point: exponent bias 7,
+// three mantissa bits, subnormals m * 2^-9, largest finite 448): with e the
+// binade of s (at least -6, the subnormal range), s / 2^(e-3) rounded half
+// to even and scaled back; both scalings are exact, and an even rounded
+// mantissa is an even code.
+__device__ __forceinline__ float e4m3_nearest(float s) {
+    if (!(s < 448.0f)) return 448.0f;
+    const int E = (int)((__float_as_uint(s) >> 23) & 0xFFu) - 127;
+    const int e = E < -6 ? -6 : E;
+    const float up = __uint_as_float((uint32_t)(127 + 3 - e) << 23);     // 2^(3-e), normal for e >= -6
+    const float down = __uint_as_float((uint32_t)(127 - 3 + e) << 23);   // 2^(e-3)
+    return rintf(s * up) * down;
+}
+
+// E4M3 code of a value produced by e4m3_nearest (non-negative, on the grid).
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+    if (v < 0.015625f) return (uint32_t)(v * 512.0f);                   // subnormal: m * 2^-9
+    const uint32_t b = __float_as_uint(v);
+    return ((((b >> 23) & 0xFFu) - 120u) << 3) | ((b >> 20) & 7u);       // exponent + 7, three mantissa bits
+}
+
+__device__ __forceinline__ float e2m1_magnitude(uint32_t c) {
+    // 0, 0.5, 1, 1.5, 2, 3, 4, 6
+    return c < 4 ? 0.5f * (float)c : (float)(c < 6 ? c - 2 : 2 * c - 8);
+}
+
+// One thread per 16-value block.
+// (src and dq may be the same rows: each thread reads its block before it
+// writes it, and no other thread touches it.)
+__global__ __launch_bounds__(256) void quantize_nv_kernel(const uint16_t *src, long long nblocks, int K,
+                                                         const float *__restrict__ g_ptr,
+                                                         uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
+                                                         uint16_t *dq) {
+    const long long b = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= nblocks) return;
+    const int bpr = K / 16;
+    const long long row = b / bpr;
+    const int blk = (int)(b % bpr);
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(src + row * K + blk * 16);
+    const u32x4 v[2] = {p[0], p[1]};
+    uint32_t amax = 0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) amax = max(amax, max(v[i][q] & 0x7FFFu, (v[i][q] >> 16) & 0x7FFFu));
+    const float g = *g_ptr;
+    const float s = bf16_to_f32(amax) / (6.0f * g);
+    const float sq = e4m3_nearest(s);
+    const float step = sq * g;
+    uint32_t cw[2] = {0u, 0u};
+    uint32_t dw[8];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            uint32_t pair = 0;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t bits = (v[i][q] >> (16 * h)) & 0xFFFFu;
+                const uint32_t sign = (bits >> 15) & 1u;
+                uint32_t mag = 0;
+                if (step > 0.0f) mag = e2m1_code(bf16_to_f32(bits & 0x7FFFu) / step);
+                const uint32_t code = step > 0.0f ? (mag | (sign << 3)) : 0u;
+                cw[i] |= code << (4 * (2 * q + h));
+                // decoded value without g: E2M1 x scale, exact in bf16
+                const uint32_t val = __float_as_uint(e2m1_magnitude(code & 7u) * sq) >> 16;
+                pair |= (val | ((code >> 3) << 15)) << (16 * h);
+            }
+            dw[4 * i + q] = pair;
+        }
+    if (codes) {
+        *reinterpret_cast<uint2 *>(codes + row * (K / 2) + blk * 8) = make_uint2(cw[0], cw[1]);
+        scales[row * bpr + blk] = (uint8_t)e4m3_code(sq);
+    }
+    if (dq) {
+        u32x4 *o = reinterpret_cast<u32x4 *>(dq + row * K + blk * 16);
+        o[0] = u32x4{dw[0], dw[1], dw[2], dw[3]};
+        o[1] = u32x4{dw[4], dw[5], dw[6], dw[7]};
+    }
+}
+
+hipError_t launch_quantize_nv(const uint16_t *src, long long rows, int K, const float *g, uint8_t *codes,
+                              uint8_t *scales, uint16_t *dq, hipStream_t st) {
+    const long long nb = rows * (K / 16);
+    if (nb == 0) return hipSuccess;
+    quantize_nv_kernel<<<(unsigned)((nb + 255) / 256), 256, 0, st>>>(src, nb, K, g, codes, scales, dq);
+    return hipGetLastError();
+}
+
 hipError_t launch_quantize_mx(const uint16_t *src, long long rows, int K, uint8_t *codes, uint8_t *scales,
                               hipStream_t st) {
     const long long nb = rows * (K / 32);

@@ -33,10 +33,12 @@ def upload(inp):
         d_s=dev.to_device(inp.d_scales) if inp.d_scales is not None else None,
     )
     s = inp.shape
-    if s.nvfp4:   # one scale buffer per matrix: fp32 expert scales, then E4M3 codes
-        d["gu_s"] = dev.to_device(moe.nvfp4_scale_buffer(inp.gu_global, inp.gu_scales))
-        d["d_s"] = dev.to_device(moe.nvfp4_scale_buffer(inp.d_global, inp.d_scales))
-    d["shape"] = moe.shape(s.T, s.H, s.E, s.k, s.I, mxfp4=s.mxfp4, a4=s.a4, nvfp4=s.nvfp4)
+    if s.nvfp4:   # one scale buffer per matrix: fp32 expert scales (+ input scale), then E4M3 codes
+        gi = inp.gu_input_scale if s.nv_a4 else 1.0
+        di = inp.d_input_scale if s.nv_a4 else 1.0
+        d["gu_s"] = dev.to_device(moe.nvfp4_scale_buffer(inp.gu_global, inp.gu_scales, gi))
+        d["d_s"] = dev.to_device(moe.nvfp4_scale_buffer(inp.d_global, inp.d_scales, di))
+    d["shape"] = moe.shape(s.T, s.H, s.E, s.k, s.I, mxfp4=s.mxfp4, a4=s.a4, nvfp4=s.nvfp4, nv_a4=s.nv_a4)
     if s.I_sh > 0:
         d["sh_gu"] = dev.to_device(inp.w_sh_gate_up)
         d["sh_d"] = dev.to_device(inp.w_sh_down)

@@ -52,7 +52,7 @@ def S(T=16, H=256, E=8, k=2, I=128, f=0):
 
 @pytest.mark.parametrize("s,expect", [
     (S(T=0), -1), (S(H=0), -1), (S(E=0), -1), (S(k=0), -1), (S(I=0), -1), (S(k=9), -1),
-    (S(H=96), -2), (S(I=100), -2), (S(E=2000, k=8), -2), (S(E=64, k=33), -2), (S(f=4), -2),
+    (S(H=96), -2), (S(I=100), -2), (S(E=2000, k=8), -2), (S(E=64, k=33), -2), (S(f=5), -2),
     (S(T=1 << 28, k=8), -2),
 ])
 def test_bad_shapes_rejected_everywhere(lib, s, expect):
@@ -206,13 +206,16 @@ def test_nvfp4_argument_checks(lib):
 def test_nvfp4_header_size():
     text = open(HEADER).read()
     assert "#define MOE_NVFP4_HEADER_BYTES(E)" in text
-    for E, n in [(1, 256), (8, 256), (64, 256), (65, 512), (128, 512), (1024, 4096)]:
+    # E matrix scales and the activation input scale, padded to 256
+    for E, n in [(1, 256), (8, 256), (63, 256), (64, 512), (65, 512), (128, 768), (1024, 4352)]:
         assert moe.nvfp4_header_bytes(E) == n
     import numpy as np
-    buf = moe.nvfp4_scale_buffer(np.array([1.5, -2.0], np.float32), np.arange(6, dtype=np.uint8).reshape(2, 1, 3))
+    buf = moe.nvfp4_scale_buffer(np.array([1.5, -2.0], np.float32), np.arange(6, dtype=np.uint8).reshape(2, 1, 3),
+                                 0.25)
     assert buf.size == 256 + 6
-    assert buf[:8].view(np.float32).tolist() == [1.5, -2.0]
-    assert (buf[8:256] == 0).all() and buf[256:].tolist() == list(range(6))
+    assert buf[:12].view(np.float32).tolist() == [1.5, -2.0, 0.25]
+    assert (buf[12:256] == 0).all() and buf[256:].tolist() == list(range(6))
+    assert moe.nvfp4_scale_buffer(np.ones(2, np.float32), np.zeros(3, np.uint8))[8:12].view(np.float32)[0] == 1.0
 
 
 def test_forward_noalloc_argument_checks(lib):
@@ -237,3 +240,26 @@ def test_forward_noalloc_argument_checks(lib):
     assert call(too_big) == -5
     assert call(_lib.MoeShape(2048, 2816, 128, 8, 704, 1), gus=F, ds=F) == -5
     assert "scratch" in lib.moe_status_string(-5).decode()
+
+
+def test_nvfp4_activation_checks(lib):
+    """MOE_W_NVFP4_A4 runs through moe_forward only, without a dense MLP;
+    moe_quantize_nv wants K % 16 == 0 and aligned pointers."""
+    s = S(f=4)
+    b = ctypes.byref(s)
+    F = FAKE
+    big = 1 << 40
+    assert lib.moe_grouped_gemm_gateup(b, F, F, F, F, F, F, None) == -2
+    assert lib.moe_grouped_gemm_down(b, F, F, F, F, F, None) == -2
+    assert lib.moe_forward(b, F, F, None, F, None, F, F, F, None, None, F, big, None, None) == -1   # scales
+    assert lib.moe_forward_shared(b, F, F, None, F, F, F, F, 128, F, F, F, F, F, None, None, F, big, None,
+                                  None) == -2
+    # the workspace adds the quantised x: T*H bf16
+    assert lib.moe_workspace_bytes(b) >= lib.moe_workspace_bytes(ctypes.byref(S(f=3))) + 16 * 256 * 2
+    assert lib.moe_quantize_nv(F, 4, 24, F, F, F, None) == -2
+    assert lib.moe_quantize_nv(F, 4, 0, F, F, F, None) == -1
+    assert lib.moe_quantize_nv(F, -1, 32, F, F, F, None) == -1
+    assert lib.moe_quantize_nv(MIS, 4, 32, F, F, F, None) == -1
+    assert lib.moe_quantize_nv(F, 4, 32, None, F, F, None) == -1
+    assert lib.moe_quantize_nv(F, 4, 32, F, F + 4, F, None) == -1     # codes 8-byte aligned
+    assert lib.moe_quantize_nv(None, 0, 32, None, None, None, None) == 0
