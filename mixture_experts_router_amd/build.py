@@ -36,12 +36,18 @@ def asan_runtime() -> str:
     return hits[-1]
 
 
-def build(verbose: bool = False, hostsan: bool = False) -> str:
+# The bounds-checked build of the kernels (include/moe_debug.h).
+DEBUG_LIB = os.path.join(HERE, "libmoe_debug.so")
+
+
+def build(verbose: bool = False, hostsan: bool = False, debug: bool = False) -> str:
     """Compile every HIP source into mixture_experts_router_amd/libmoe.so
-    (hostsan: into libmoe_hostsan.so with sanitised host code)."""
-    out = HOSTSAN_LIB if hostsan else LIB
+    (hostsan: into libmoe_hostsan.so with sanitised host code; debug: into
+    libmoe_debug.so with the kernels' bounds checks)."""
+    out = HOSTSAN_LIB if hostsan else (DEBUG_LIB if debug else LIB)
     tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, *(HOSTSAN_FLAGS if hostsan else []), "-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
+    extra = (HOSTSAN_FLAGS if hostsan else []) + (["-DMOE_DEBUG"] if debug else [])
+    cmd = [HIPCC, *FLAGS, *extra, "-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

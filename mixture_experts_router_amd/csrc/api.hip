@@ -6,6 +6,7 @@
 #include <mutex>
 
 #include "../../include/moe.h"
+#include "../../include/moe_debug.h"
 #include "moe_launch.h"
 
 // Scratch of moe_forward_noalloc: the library's own device memory, one copy
@@ -471,6 +472,24 @@ int moe_quantize_nv(const uint16_t *src, int64_t rows, int32_t K, const float *i
     return hip_status(moe::launch_quantize_nv(src, rows, K, input_scale, codes, scales, nullptr,
                                               static_cast<hipStream_t>(stream)));
 }
+
+#ifdef MOE_DEBUG
+int moe_debug_bounds(uint32_t *violations, uint32_t *where) {
+    if (!violations || !where) return MOE_ERR_INVALID_ARGUMENT;
+    hipError_t (*const readers[])(uint32_t *) = {moe::debug_read_route, moe::debug_read_permute,
+                                                 moe::debug_read_gemm, moe::debug_read_combine,
+                                                 moe::debug_read_quant};
+    *violations = 0;
+    *where = 0;
+    for (int i = 0; i < 5; ++i) {
+        uint32_t rec[2] = {0u, 0u};
+        if (readers[i](rec) != hipSuccess) return MOE_ERR_HIP;
+        if (rec[0] && !*violations) *where = 100000u * (uint32_t)(i + 1) + rec[1];
+        *violations += rec[0];
+    }
+    return MOE_OK;
+}
+#endif
 
 size_t moe_workspace_shared_bytes(const moe_shape *s, int32_t I_sh) {
     if (check_shape(s) != MOE_OK || I_sh <= 0 || I_sh % 64 != 0) return 0;

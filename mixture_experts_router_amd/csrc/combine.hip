@@ -36,4 +36,8 @@ hipError_t launch_combine(const uint16_t *y, const int32_t *inv, const float *w,
     return hipGetLastError();
 }
 
+#ifdef MOE_DEBUG
+MOE_DEBUG_READER(debug_read_combine)
+#endif
+
 }  // namespace moe

@@ -84,6 +84,11 @@ struct GemmArgs {
     const float *a_global;
     // Row-tile groups run last to first on each XCD (large row blocks only)
     int reverse_groups;
+    // Buffer extents in bytes, for the bounds checks of the MOE_DEBUG build:
+    // the routed group's (or the router's) operands and output, then the
+    // shared group's.
+    size_t a_bytes, gather_bytes, w_bytes, s_bytes, out_bytes, a_s_bytes;
+    size_t sh_a_bytes, sh_w_bytes, sh_s_bytes, sh_out_bytes;
 };
 
 // Locate this workgroup's M tile: tile index -> (expert e, first row m0
@@ -366,6 +371,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
     const int g_I = shared ? p.sh_I : p.I;
     const int g_w_rows = shared ? p.sh_w_rows : p.w_rows;
     const int g_n_out = shared ? p.sh_n_out : p.n_out;
+    [[maybe_unused]] const size_t g_a_bytes = shared ? p.sh_a_bytes : p.a_bytes;
+    [[maybe_unused]] const size_t g_w_bytes = shared ? p.sh_w_bytes : p.w_bytes;
+    [[maybe_unused]] const size_t g_s_bytes = shared ? p.sh_s_bytes : p.s_bytes;
+    [[maybe_unused]] const size_t g_out_bytes = shared ? p.sh_out_bytes : p.out_bytes;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
@@ -444,7 +453,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
         const int g = q * NW + wave;
         const int row = RPD * (g < NA ? g : 0) + lr;
         const int rr = row < rows ? row : 0;
-        const size_t src = g_gather ? (size_t)(g_gather[seg + rr] / p.gather_k) : (size_t)(seg + rr);
+        const size_t src = g_gather ? (size_t)(*MOE_CHECKED(g_gather + seg + rr, 4, g_gather, p.gather_bytes) /
+                                               p.gather_k)
+                                    : (size_t)(seg + rr);
         if (G::WDMA) {
             a_src[q] = g_a + src * rowu + kb;
             a_ch[q] = 8 * tswz<BK>(row, lc);
@@ -521,9 +532,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
             const int g = q * NW + wave;
             if (g < na_valid) {
                 if (G::WDMA)
-                    dma16<false>(a_src[q] + min(kt * BK + a_ch[q], K - 8), As[slot] + g * 512);
+                    dma16<false>(MOE_CHECKED(a_src[q] + min(kt * BK + a_ch[q], K - 8), 16, g_a, g_a_bytes),
+                                 As[slot] + g * 512);
                 else
-                    dma16<false>(a_src[q] + col_of(kt), As[slot] + g * 512);
+                    dma16<false>(MOE_CHECKED(a_src[q] + col_of(kt), 16, g_a, g_a_bytes), As[slot] + g * 512);
             }
         }
     };
@@ -536,9 +548,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
             // Weights of an expert with one row tile are read once: stream
             // them past the caches.  Several row tiles re-read them: keep.
             if (stream)
-                dma16<true>(b_src[q] + bcol, Bs[slot] + g * 512);
+                dma16<true>(MOE_CHECKED(b_src[q] + bcol, 16, g_w, g_w_bytes), Bs[slot] + g * 512);
             else
-                dma16<false>(b_src[q] + bcol, Bs[slot] + g * 512);
+                dma16<false>(MOE_CHECKED(b_src[q] + bcol, 16, g_w, g_w_bytes), Bs[slot] + g * 512);
         }
     };
     // Weight tile (and block scales) of step kt.
@@ -549,7 +561,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
 #pragma unroll
         for (int q = 0; q < G::S_W; ++q) {
             const int g = q * NW + wave;
-            if (G::NSC % NW == 0 || g < G::NSC) dma4(s_src[q] + scol_bytes(kt), Ss[slot] + g * 256);
+            if (G::NSC % NW == 0 || g < G::NSC)
+                dma4(MOE_CHECKED(s_src[q] + scol_bytes(kt), 4, g_scales, g_s_bytes), Ss[slot] + g * 256);
         }
     };
 
@@ -607,14 +620,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
     }
     auto issue_mx = [&](int kt) {
 #pragma unroll
-        for (int i = 0; i < G::MB_PER; ++i) mb[i] = *reinterpret_cast<const u32x4 *>(mb_src[i] + kt * (BK / 2));
+        for (int i = 0; i < G::MB_PER; ++i)
+            mb[i] = *reinterpret_cast<const u32x4 *>(MOE_CHECKED(mb_src[i] + kt * (BK / 2), 16, g_w, g_w_bytes));
         // scale rows are K/32 (E8M0) or K/16 (E4M3) bytes: 2- and 4-byte
         // aligned for K % 64 == 0
 #pragma unroll
         for (int i = 0; i < G::MS_PER; ++i)
 #pragma unroll
             for (int w = 0; w < G::SCW; ++w) {
-                const uint8_t *src = ms_src[i] + kt * G::SC_PER + 4 * w;
+                const uint8_t *src = MOE_CHECKED(ms_src[i] + kt * G::SC_PER + 4 * w,
+                                                 NV || G::SC_PER >= 4 ? 4 : 2, g_scales, g_s_bytes);
                 if (NV) {
                     ms[i][w] = *reinterpret_cast<const uint32_t *>(src);
                 } else {
@@ -661,17 +676,25 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
     // wave with a single 16-row token tile reads its 16 bits alone.
     const int nblk = K / 32;
     const uint8_t *sc_src = nullptr;   // this thread's scale row
+    [[maybe_unused]] const uint8_t *sc_base = nullptr;   // its buffer and extent (bounds checks)
+    [[maybe_unused]] size_t sc_bytes = 0;
     int sc_dst = -1;                   // its LDS byte offset (blocks 0, 1 of lane block 0)
     bool sc_pair = true;
     if (A4) {
         if (tid < BN) {
             sc_src = g_scales + ((size_t)e * g_w_rows + weight_row(tid)) * nblk;
+            sc_base = g_scales;
+            sc_bytes = g_s_bytes;
             sc_dst = ((tid >> 5) * 16 + (tid & 15)) * 16 + ((tid >> 4) & 1) * 2;
         } else if (tid < BN + BM) {
             const int v = tid - BN;
             const int rr = v < rows ? v : 0;
-            const size_t src = g_gather ? (size_t)(g_gather[seg + rr] / p.gather_k) : (size_t)(seg + rr);
+            const size_t src = g_gather ? (size_t)(*MOE_CHECKED(g_gather + seg + rr, 4, g_gather, p.gather_bytes) /
+                                                   p.gather_k)
+                                        : (size_t)(seg + rr);
             sc_src = p.a_scales + src * nblk;
+            sc_base = p.a_scales;
+            sc_bytes = p.a_s_bytes;
             sc_pair = G::SC_PAIR_M;
             sc_dst = G::SC_W + (G::SC_PAIR_M ? ((v >> 5) * 16 + (v & 15)) * 16 + ((v >> 4) & 1) * 2 : v * 8);
         }
@@ -684,7 +707,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
         uint32_t h[4];
 #pragma unroll
         for (int m = 0; m < 4; ++m)
-            h[m] = *reinterpret_cast<const uint16_t *>(sc_src + min(8 * kt + 2 * m, nblk - 2));
+            h[m] = *reinterpret_cast<const uint16_t *>(
+                MOE_CHECKED(sc_src + min(8 * kt + 2 * m, nblk - 2), 2, sc_base, sc_bytes));
         sc_v[0] = h[0] | (h[1] << 16);
         sc_v[1] = h[2] | (h[3] << 16);
     };
@@ -902,7 +926,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
         uint16_t sv[MAXW];
 #pragma unroll
         for (int i = 0; i < MAXW; ++i)
-            if (TPR * i < nh) sv[i] = srow[min(w0 + TPR * i, nh - 1)];
+            if (TPR * i < nh) sv[i] = *MOE_CHECKED(srow + min(w0 + TPR * i, nh - 1), 2, g_scales, g_s_bytes);
         uint16_t *dst = reinterpret_cast<uint16_t *>(Ss[0] + v * G::SC_ROW);
 #pragma unroll
         for (int i = 0; i < MAXW; ++i)
@@ -969,7 +993,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
                     const int n = nt * BN + wn * WN + j * 16 + 4 * lk + q;
                     if (n < p.n_out) {
                         const double b = p.bias ? (double)p.bias[n] : 0.0;
-                        lrow_out[n] = (float)(acc64[j][i][q] + b);
+                        *MOE_CHECKED(lrow_out + n, 4, p.out32, p.out_bytes) = (float)(acc64[j][i][q] + b);
                     }
                 }
         } else if (GEGLU && (NI / 2) % 2 == 0) {
@@ -995,7 +1019,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
                 const int odd = lk & 1;
                 const uint4 o = pair_swap16(p[0], p[1], odd);
                 const int n = n0 + odd * 16 + 4 * (lk & ~1);
-                if (n < g_I) *reinterpret_cast<uint4 *>(orow + n) = o;
+                if (n < g_I) *reinterpret_cast<uint4 *>(MOE_CHECKED(orow + n, 16, g_out, g_out_bytes)) = o;
             }
         } else if (GEGLU) {
             constexpr int HALF_T = NI / 2;
@@ -1011,7 +1035,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
                 uint2 o;
                 o.x = pack_bf16x2(gelu_tanh(g[0]) * u[0], gelu_tanh(g[1]) * u[1]);
                 o.y = pack_bf16x2(gelu_tanh(g[2]) * u[2], gelu_tanh(g[3]) * u[3]);
-                *reinterpret_cast<uint2 *>(orow + n) = o;
+                *reinterpret_cast<uint2 *>(MOE_CHECKED(orow + n, 8, g_out, g_out_bytes)) = o;
             }
         } else if (shared && p.sh_out32) {   // dense MLP down: fp32 partial sum of this K range
             float *prow = p.sh_out32 + ((size_t)split * p.sh_rows + seg + t) * g_n_out;
@@ -1019,7 +1043,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
             for (int j = 0; j < NI; ++j) {
                 const int n = nt * BN + wn * WN + j * 16 + 4 * lk;
                 if (n >= g_n_out) continue;
-                *reinterpret_cast<f32x4 *>(prow + n) = acc[j][i];
+                *reinterpret_cast<f32x4 *>(MOE_CHECKED(prow + n, 16, p.sh_out32, p.sh_out_bytes)) = acc[j][i];
             }
         } else if (NI % 2 == 0) {
 #pragma unroll
@@ -1035,7 +1059,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
                 const int odd = lk & 1;
                 const uint4 o = pair_swap16(pr[0], pr[1], odd);
                 const int n = nt * BN + wn * WN + (j + odd) * 16 + 4 * (lk & ~1);
-                if (n < g_n_out) *reinterpret_cast<uint4 *>(orow + n) = o;
+                if (n < g_n_out) *reinterpret_cast<uint4 *>(MOE_CHECKED(orow + n, 16, g_out, g_out_bytes)) = o;
             }
         } else {
 #pragma unroll
@@ -1047,7 +1071,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
                 uint2 o;
                 o.x = pack_bf16x2(v[0], v[1]);
                 o.y = pack_bf16x2(v[2], v[3]);
-                *reinterpret_cast<uint2 *>(orow + n) = o;
+                *reinterpret_cast<uint2 *>(MOE_CHECKED(orow + n, 8, g_out, g_out_bytes)) = o;
             }
         }
     }
@@ -1188,6 +1212,13 @@ hipError_t launch_gateup_a4(const uint8_t *xq, const uint8_t *xs, const int32_t 
     GemmArgs a{reinterpret_cast<const uint16_t *>(xq), sorted_ids, k, offsets, w, scales, h, E, H, I, I, 2 * I,
                0, 0, 0, nullptr, nullptr};
     a.a_scales = xs;
+    const size_t T = (size_t)A / k;
+    a.a_bytes = T * H / 2;
+    a.a_s_bytes = T * H / 32;
+    a.gather_bytes = (size_t)A * 4;
+    a.w_bytes = (size_t)E * 2 * I * H / 2;
+    a.s_bytes = (size_t)E * 2 * I * H / 32;
+    a.out_bytes = (size_t)A * I * 2;
     return launch_sized_a4<kGateUp>(a, A, st);
 }
 
@@ -1205,6 +1236,11 @@ hipError_t launch_down_a4(const uint8_t *hq, const uint8_t *hs, const int32_t *o
     GemmArgs a{reinterpret_cast<const uint16_t *>(hq), nullptr, 1, offsets, w, scales, y, E, I, H, I, H, 0, 0, 0,
                nullptr, nullptr};
     a.a_scales = hs;
+    a.a_bytes = (size_t)A * I / 2;
+    a.a_s_bytes = (size_t)A * I / 32;
+    a.w_bytes = (size_t)E * H * I / 2;
+    a.s_bytes = (size_t)E * H * I / 32;
+    a.out_bytes = (size_t)A * H * 2;
     a.reverse_groups = reverse_down_groups(A, H);
     return launch_sized_a4<kDown>(a, A, st);
 }
@@ -1216,6 +1252,15 @@ hipError_t launch_gateup(const uint16_t *x, const int32_t *sorted_ids, int k, co
     GemmArgs a{x, sorted_ids, k, offsets, w, scales, h, E, H, I, I, 2 * I, 0, 0, 0, nullptr, nullptr};
     a.w_global = w_global;
     a.a_global = a_global;
+    // extents (bounds checks): x gathered from [T][H] or pre-permuted [A][H];
+    // weights [E][2I][H] bf16 or 4-bit codes; block scales per 32 or 16
+    const size_t wk = fmt == WeightFormat::kBF16 ? 2 * (size_t)H : (size_t)H / 2;
+    const size_t sk = fmt == WeightFormat::kMXFP4 ? H / 32 : (fmt == WeightFormat::kNVFP4 ? H / 16 : 0);
+    a.a_bytes = (sorted_ids ? (size_t)A / k : (size_t)A) * H * 2;
+    a.gather_bytes = (size_t)A * 4;
+    a.w_bytes = (size_t)E * 2 * I * wk;
+    a.s_bytes = (size_t)E * 2 * I * sk;
+    a.out_bytes = (size_t)A * I * 2;
     if (sh) {   // every token through the shared gate/up weights [2 I_sh][H]
         a.sh_rows = sh->rows;
         a.sh_a = x;
@@ -1228,6 +1273,10 @@ hipError_t launch_gateup(const uint16_t *x, const int32_t *sorted_ids, int k, co
         a.sh_n_out = sh->I;
         a.sh_splits = 1;
         a.sh_ksplit = H;
+        a.sh_a_bytes = (size_t)sh->rows * H * 2;
+        a.sh_w_bytes = 2 * (size_t)sh->I * wk;
+        a.sh_s_bytes = 2 * (size_t)sh->I * sk;
+        a.sh_out_bytes = (size_t)sh->rows * sh->I * 2;
     }
     if (fmt == WeightFormat::kNVFP4) return sh ? hipErrorInvalidValue : launch_sized<kGateUp, true, true>(a, A, st);
     return fmt == WeightFormat::kMXFP4 ? launch_sized<kGateUp, true>(a, A, st) : launch_sized<kGateUp, false>(a, A, st);
@@ -1240,6 +1289,14 @@ hipError_t launch_down(const uint16_t *h, const int32_t *offsets, const void *w,
     a.w_global = w_global;
     a.a_global = a_global;
     a.reverse_groups = reverse_down_groups(A, H);
+    // extents (bounds checks): h [A][I]; weights [E][H][I] bf16 or 4-bit
+    // codes; block scales per 32 or 16
+    const size_t wk = fmt == WeightFormat::kBF16 ? 2 * (size_t)I : (size_t)I / 2;
+    const size_t sk = fmt == WeightFormat::kMXFP4 ? I / 32 : (fmt == WeightFormat::kNVFP4 ? I / 16 : 0);
+    a.a_bytes = (size_t)A * I * 2;
+    a.w_bytes = (size_t)E * H * wk;
+    a.s_bytes = (size_t)E * H * sk;
+    a.out_bytes = (size_t)A * H * 2;
     if (sh) {   // the shared h rows [rows][I_sh] through the shared down weights [H][I_sh]
         a.sh_rows = sh->rows;
         a.sh_a = sh->a;
@@ -1256,6 +1313,11 @@ hipError_t launch_down(const uint16_t *h, const int32_t *offsets, const void *w,
         // tile takes as long as a routed one; partial sums stay fp32
         a.sh_splits = shared_splits(sh->I, I);
         a.sh_ksplit = shared_ksplit(sh->I, I);
+        const size_t swk = fmt == WeightFormat::kBF16 ? 2 * (size_t)sh->I : (size_t)sh->I / 2;
+        a.sh_a_bytes = (size_t)sh->rows * sh->I * 2;
+        a.sh_w_bytes = (size_t)H * swk;
+        a.sh_s_bytes = fmt == WeightFormat::kMXFP4 ? (size_t)H * sh->I / 32 : 0;
+        a.sh_out_bytes = (size_t)a.sh_splits * sh->rows * H * 4;
     }
     if (fmt == WeightFormat::kNVFP4) return sh ? hipErrorInvalidValue : launch_sized<kDown, true, true>(a, A, st);
     return fmt == WeightFormat::kMXFP4 ? launch_sized<kDown, true>(a, A, st) : launch_sized<kDown, false>(a, A, st);
@@ -1275,10 +1337,17 @@ hipError_t launch_down(const uint16_t *h, const int32_t *offsets, const void *w,
 hipError_t launch_router_dense(const uint16_t *x, const uint16_t *wr, const float *bias, float *logits,
                                int T, int H, int E, hipStream_t st) {
     GemmArgs a{x, nullptr, 1, nullptr, wr, nullptr, nullptr, 1, H, E, 0, E, 0, 0, T, logits, bias};
+    a.a_bytes = (size_t)T * H * 2;
+    a.w_bytes = (size_t)E * H * 2;
+    a.out_bytes = (size_t)T * E * 4;
     if (H % 128 == 0 && T >= 8192) return launch_cfg<32, 128, 2, 4, kRouter, false, 3, 128>(a, T, st);
     if (H % 256 == 0) return launch_cfg<16, 64, 1, 4, kRouter, false, 3, 256>(a, T, st);
     if (H % 128 == 0) return launch_cfg<16, 64, 1, 4, kRouter, false, 4, 128>(a, T, st);
     return launch_cfg<16, 64, 1, 4, kRouter, false, 6, 64>(a, T, st);
 }
+
+#ifdef MOE_DEBUG
+MOE_DEBUG_READER(debug_read_gemm)
+#endif
 
 }  // namespace moe

@@ -7,6 +7,34 @@
 
 namespace moe {
 
+// ---- bounds checks of the MOE_DEBUG build.  A kernel checks each global
+// address it forms from indices against the extent of the buffer it must
+// lie in: an access outside is counted (with the source line of the first
+// one, per translation unit) and redirected to the buffer's first byte, so
+// a wrong index becomes a recorded violation rather than a memory fault or a
+// silent overwrite.  moe_debug_bounds (include/moe_debug.h) reads and clears
+// the record.  In release builds MOE_CHECKED(p, ...) is p itself.
+#ifdef MOE_DEBUG
+static __device__ uint32_t moe_oob[2];   // violations, source line of the first
+template <typename T>
+__device__ __forceinline__ T *checked(T *p, size_t n, const void *base, size_t bytes, int line) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p), lo = reinterpret_cast<uintptr_t>(base);
+    if (base && a >= lo && a + n <= lo + bytes) return p;
+    if (atomicAdd(&moe_oob[0], 1u) == 0u) moe_oob[1] = (uint32_t)line;
+    return reinterpret_cast<T *>(reinterpret_cast<uintptr_t>(base));
+}
+#define MOE_CHECKED(p, n, base, bytes) ::moe::checked((p), (size_t)(n), (const void *)(base), (size_t)(bytes), __LINE__)
+// Host side: this translation unit's record into rec[2], cleared after.
+#define MOE_DEBUG_READER(fn)                                                       \
+    hipError_t fn(uint32_t *rec) {                                                 \
+        hipError_t e = hipMemcpyFromSymbol(rec, HIP_SYMBOL(moe_oob), 8);           \
+        const uint32_t zero[2] = {0u, 0u};                                         \
+        return e == hipSuccess ? hipMemcpyToSymbol(HIP_SYMBOL(moe_oob), zero, 8) : e; \
+    }
+#else
+#define MOE_CHECKED(p, n, base, bytes) (p)
+#endif
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -143,7 +171,7 @@ __device__ __forceinline__ void combine_chunk(const uint16_t *__restrict__ y, co
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[q] = 0.f;
     for (int sp = 0; y_sh32 && sp < nsplit; ++sp) {
-        const float *r = y_sh32 + ((size_t)sp * T + t) * H + c;
+        const float *r = MOE_CHECKED(y_sh32 + ((size_t)sp * T + t) * H + c, 32, y_sh32, (size_t)nsplit * T * H * 4);
         const f32x4 a = *reinterpret_cast<const f32x4 *>(r), b = *reinterpret_cast<const f32x4 *>(r + 4);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -156,7 +184,8 @@ __device__ __forceinline__ void combine_chunk(const uint16_t *__restrict__ y, co
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int j = min(j0 + u, k - 1);
-            v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(y + (size_t)ti[j] * H + c));
+            v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+                MOE_CHECKED(y + (size_t)ti[j] * H + c, 16, y, (size_t)T * k * H * 2)));
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
@@ -172,7 +201,7 @@ __device__ __forceinline__ void combine_chunk(const uint16_t *__restrict__ y, co
     u32x4 o;
 #pragma unroll
     for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
-    *reinterpret_cast<u32x4 *>(out + (size_t)t * H + c) = o;
+    *reinterpret_cast<u32x4 *>(MOE_CHECKED(out + (size_t)t * H + c, 16, out, (size_t)T * H * 2)) = o;
 }
 
 }  // namespace moe

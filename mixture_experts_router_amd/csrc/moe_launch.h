@@ -96,4 +96,14 @@ hipError_t launch_quantize_nv(const uint16_t *src, long long rows, int K, const 
 hipError_t launch_combine(const uint16_t *y, const int32_t *inv, const float *w, const float *y_sh32, int nsplit,
                           uint16_t *out, int T, int H, int k, hipStream_t st);
 
+#ifdef MOE_DEBUG
+// Bounds-check records of the MOE_DEBUG build, one per source file: rec[0]
+// violations, rec[1] source line of the first; each read clears the record.
+hipError_t debug_read_route(uint32_t *rec);
+hipError_t debug_read_permute(uint32_t *rec);
+hipError_t debug_read_gemm(uint32_t *rec);
+hipError_t debug_read_combine(uint32_t *rec);
+hipError_t debug_read_quant(uint32_t *rec);
+#endif
+
 }  // namespace moe

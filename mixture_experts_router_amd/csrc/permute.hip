@@ -89,8 +89,8 @@ __device__ __forceinline__ void scatter_chunk(const int32_t *__restrict__ ids, c
     if (valid) {
         int pos = base[e] + __popcll(m & below);
         for (int w = 0; w < wave; ++w) pos += wc[w * E + e];
-        sorted_ids[pos] = a;
-        inv[a] = pos;
+        *MOE_CHECKED(sorted_ids + pos, 4, sorted_ids, (size_t)A * 4) = a;
+        *MOE_CHECKED(inv + a, 4, inv, (size_t)A * 4) = pos;
     }
 }
 
@@ -176,7 +176,8 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t *__rest
     const int t = sorted_ids[p] / k;
     const u32x4 *src = reinterpret_cast<const u32x4 *>(x + (size_t)t * H);
     u32x4 *dst = reinterpret_cast<u32x4 *>(x_perm + (size_t)p * H);
-    for (int c = lane; c < H / 8; c += 64) dst[c] = src[c];
+    for (int c = lane; c < H / 8; c += 64)
+        *MOE_CHECKED(dst + c, 16, x_perm, (size_t)A * H * 2) = *MOE_CHECKED(src + c, 16, x, (size_t)A / k * H * 2);
 }
 
 static int bits_for(int E) {
@@ -211,5 +212,9 @@ hipError_t launch_gather_rows(const uint16_t *x, const int32_t *sorted_ids, uint
     gather_rows_kernel<<<(A + 3) / 4, 256, 0, st>>>(x, sorted_ids, x_perm, A, H, k);
     return hipGetLastError();
 }
+
+#ifdef MOE_DEBUG
+MOE_DEBUG_READER(debug_read_permute)
+#endif
 
 }  // namespace moe

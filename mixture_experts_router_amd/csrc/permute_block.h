@@ -38,7 +38,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *sh /* >= blockDi
 // advanced here.  All expert ids of the chunk are loaded first.
 __device__ __forceinline__ void rank_chunk(const int32_t *__restrict__ ids, int a0, int a1,
                                            int *cnt, int nbits, int32_t *__restrict__ sorted_ids,
-                                           int32_t *__restrict__ inv) {
+                                           int32_t *__restrict__ inv, [[maybe_unused]] int A) {
     constexpr int kSteps = kChunk / 64;
     const int lane = threadIdx.x & 63;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -65,8 +65,8 @@ __device__ __forceinline__ void rank_chunk(const int32_t *__restrict__ ids, int 
         if (valid && (m >> lane) == 1ull) cnt[e] = pos + 1;
         __builtin_amdgcn_wave_barrier();
         if (valid) {
-            sorted_ids[pos] = a;
-            inv[a] = pos;
+            *MOE_CHECKED(sorted_ids + pos, 4, sorted_ids, (size_t)A * 4) = a;
+            *MOE_CHECKED(inv + a, 4, inv, (size_t)A * 4) = pos;
         }
     }
 }
@@ -92,7 +92,7 @@ __device__ __forceinline__ void permute_in_block(const int32_t *ids, int A, int 
     if (tid == 0) offsets[E] = A;
     __syncthreads();
     if (tid < 64)
-        for (int a0 = 0; a0 < A; a0 += kChunk) rank_chunk(ids, a0, min(A, a0 + kChunk), h, nbits, sorted_ids, inv);
+        for (int a0 = 0; a0 < A; a0 += kChunk) rank_chunk(ids, a0, min(A, a0 + kChunk), h, nbits, sorted_ids, inv, A);
 }
 
 // Histogram, exclusive scan and stable scatter of A <= 64 assignments by one
@@ -119,8 +119,8 @@ __device__ __forceinline__ void permute_wave(const int32_t *ids, int A, int E, i
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     if (valid) {
         const int pos = less + __popcll(m & below);
-        sorted_ids[pos] = lane;
-        inv[lane] = pos;
+        *MOE_CHECKED(sorted_ids + pos, 4, sorted_ids, (size_t)A * 4) = lane;
+        *MOE_CHECKED(inv + lane, 4, inv, (size_t)A * 4) = pos;
         if ((m >> lane) == 1ull) h[id] = __popcll(m);   // highest lane of its expert group
     }
     __builtin_amdgcn_wave_barrier();

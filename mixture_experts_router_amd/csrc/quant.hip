@@ -35,7 +35,8 @@ __global__ __launch_bounds__(256) void quantize_mx_kernel(const uint16_t *__rest
     const int bpr = K / 32;
     const long long row = b / bpr;
     const int blk = (int)(b % bpr);
-    const u32x4 *p = reinterpret_cast<const u32x4 *>(src + row * K + blk * 32);
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(
+        MOE_CHECKED(src + row * K + blk * 32, 64, src, (size_t)nblocks * 64));
     u32x4 v[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = p[i];
@@ -63,8 +64,8 @@ __global__ __launch_bounds__(256) void quantize_mx_kernel(const uint16_t *__rest
         }
         out[i] = word;
     }
-    *reinterpret_cast<u32x4 *>(codes + row * (K / 2) + blk * 16) = out;
-    scales[row * bpr + blk] = (uint8_t)(e + 127);
+    *reinterpret_cast<u32x4 *>(MOE_CHECKED(codes + row * (K / 2) + blk * 16, 16, codes, (size_t)nblocks * 16)) = out;
+    *MOE_CHECKED(scales + row * bpr + blk, 1, scales, (size_t)nblocks) = (uint8_t)(e + 127);
 }
 
 // NVFP4 quantisation of bf16 rows, per 16 consecutive values, relative to
@@ -116,7 +117,8 @@ __global__ __launch_bounds__(256) void quantize_nv_kernel(const uint16_t *src, l
     const int bpr = K / 16;
     const long long row = b / bpr;
     const int blk = (int)(b % bpr);
-    const u32x4 *p = reinterpret_cast<const u32x4 *>(src + row * K + blk * 16);
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(
+        MOE_CHECKED(src + row * K + blk * 16, 32, src, (size_t)nblocks * 32));
     const u32x4 v[2] = {p[0], p[1]};
     uint32_t amax = 0;
 #pragma unroll
@@ -149,11 +151,12 @@ __global__ __launch_bounds__(256) void quantize_nv_kernel(const uint16_t *src, l
             dw[4 * i + q] = pair;
         }
     if (codes) {
-        *reinterpret_cast<uint2 *>(codes + row * (K / 2) + blk * 8) = make_uint2(cw[0], cw[1]);
-        scales[row * bpr + blk] = (uint8_t)e4m3_code(sq);
+        *reinterpret_cast<uint2 *>(MOE_CHECKED(codes + row * (K / 2) + blk * 8, 8, codes, (size_t)nblocks * 8)) =
+            make_uint2(cw[0], cw[1]);
+        *MOE_CHECKED(scales + row * bpr + blk, 1, scales, (size_t)nblocks) = (uint8_t)e4m3_code(sq);
     }
     if (dq) {
-        u32x4 *o = reinterpret_cast<u32x4 *>(dq + row * K + blk * 16);
+        u32x4 *o = reinterpret_cast<u32x4 *>(MOE_CHECKED(dq + row * K + blk * 16, 32, dq, (size_t)nblocks * 32));
         o[0] = u32x4{dw[0], dw[1], dw[2], dw[3]};
         o[1] = u32x4{dw[4], dw[5], dw[6], dw[7]};
     }
@@ -174,5 +177,9 @@ hipError_t launch_quantize_mx(const uint16_t *src, long long rows, int K, uint8_
     quantize_mx_kernel<<<(unsigned)((nb + 255) / 256), 256, 0, st>>>(src, nb, K, codes, scales);
     return hipGetLastError();
 }
+
+#ifdef MOE_DEBUG
+MOE_DEBUG_READER(debug_read_quant)
+#endif
 
 }  // namespace moe

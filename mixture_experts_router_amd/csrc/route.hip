@@ -40,8 +40,8 @@ __device__ __forceinline__ void router_partial_wave(const uint16_t *__restrict__
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
         const int su = u < nsteps ? u : 0;
-        a[u] = *reinterpret_cast<const u32x4 *>(arow + 32 * su);
-        b[u] = *reinterpret_cast<const u32x4 *>(brow + 32 * su);
+        a[u] = *reinterpret_cast<const u32x4 *>(MOE_CHECKED(arow + 32 * su, 16, x, (size_t)T * H * 2));
+        b[u] = *reinterpret_cast<const u32x4 *>(MOE_CHECKED(brow + 32 * su, 16, wr, (size_t)E * H * 2));
     }
     // Experts are the MFMA A operand and tokens the B operand, as in the
     // grouped GEMM engine that computes the router for many tokens: lane
@@ -55,7 +55,9 @@ __device__ __forceinline__ void router_partial_wave(const uint16_t *__restrict__
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int eo = etile * 16 + 4 * g + q;
-            if (eo < E) part[((size_t)c * T + t) * E + eo] = acc[q];
+            if (eo < E)
+                *MOE_CHECKED(part + ((size_t)c * T + t) * E + eo, 4, part,
+                             (size_t)((H + kRouteChunk - 1) / kRouteChunk) * T * E * 4) = acc[q];
         }
     }
 }
@@ -130,7 +132,8 @@ __device__ __forceinline__ void topk_token(int t, const float *__restrict__ part
                     const int e = min(lane + 64 * (i0 + i), E - 1);
 #pragma unroll
                     for (int u = 0; u < CB; ++u)
-                        pv[i][u] = part[((size_t)min(c0 + u, nchunks - 1) * T + t) * E + e];
+                        pv[i][u] = *MOE_CHECKED(part + ((size_t)min(c0 + u, nchunks - 1) * T + t) * E + e, 4, part,
+                                                (size_t)nchunks * T * E * 4);
                 }
 #pragma unroll
                 for (int i = 0; i < IB; ++i)
@@ -144,7 +147,7 @@ __device__ __forceinline__ void topk_token(int t, const float *__restrict__ part
                 key[i0 + i] = 0u;
                 if (e < E) {
                     const float v = (float)(s[i] + (double)b[i]);
-                    if (logits) logits[(size_t)t * E + e] = v;
+                    if (logits) *MOE_CHECKED(logits + (size_t)t * E + e, 4, logits, (size_t)T * E * 4) = v;
                     key[i0 + i] = order_key(v);
                 }
             }
@@ -153,7 +156,7 @@ __device__ __forceinline__ void topk_token(int t, const float *__restrict__ part
 #pragma unroll
         for (int i = 0; i < VPL; ++i) {
             const int e = lane + 64 * i;
-            key[i] = e < E ? order_key(logits[(size_t)t * E + e]) : 0u;
+            key[i] = e < E ? order_key(*MOE_CHECKED(logits + (size_t)t * E + e, 4, logits, (size_t)T * E * 4)) : 0u;
         }
     }
     // k rounds of wave argmax; lane j keeps slot j.
@@ -187,8 +190,8 @@ __device__ __forceinline__ void topk_token(int t, const float *__restrict__ part
     float sum = 0.f;
     for (int m = 0; m < k; ++m) sum += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ex), m));
     if (lane < k) {
-        ids[(size_t)t * k + lane] = my_idx;
-        wts[(size_t)t * k + lane] = ex / sum;
+        *MOE_CHECKED(ids + (size_t)t * k + lane, 4, ids, (size_t)T * k * 4) = my_idx;
+        *MOE_CHECKED(wts + (size_t)t * k + lane, 4, wts, (size_t)T * k * 4) = ex / sum;
         if (lds_ids) lds_ids[t * k + lane] = my_idx;
     }
 }
@@ -316,5 +319,9 @@ hipError_t launch_topk(const float *part, int nchunks, const float *bias, float 
 #undef MOE_TOPK
     return hipGetLastError();
 }
+
+#ifdef MOE_DEBUG
+MOE_DEBUG_READER(debug_read_route)
+#endif
 
 }  // namespace moe

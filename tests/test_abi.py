@@ -263,3 +263,20 @@ def test_nvfp4_activation_checks(lib):
     assert lib.moe_quantize_nv(F, 4, 32, None, F, F, None) == -1
     assert lib.moe_quantize_nv(F, 4, 32, F, F + 4, F, None) == -1     # codes 8-byte aligned
     assert lib.moe_quantize_nv(None, 0, 32, None, None, None, None) == 0
+
+
+def test_debug_header_and_exports():
+    """include/moe_debug.h declares the query of the bounds-checked build:
+    libmoe_debug.so exports it (and every moe.h entry point), the release
+    library does not."""
+    import subprocess
+    from mixture_experts_router_amd import build as b
+    text = open(os.path.join(ROOT, "include", "moe_debug.h")).read()
+    assert re.findall(r"^\s*int\s+(moe_\w+)\s*\(", text, re.M) == ["moe_debug_bounds"]
+    if not os.path.exists(b.DEBUG_LIB):
+        pytest.skip("libmoe_debug.so not built")
+    names = lambda path: set(subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
+                                            check=True).stdout.split())
+    dbg, rel = names(b.DEBUG_LIB), names(_lib.LIB_PATH)
+    assert "moe_debug_bounds" in dbg and "moe_debug_bounds" not in rel
+    assert set(_lib.EXPORTS) <= dbg
