@@ -161,14 +161,14 @@ struct GemmTile {
     static constexpr int SC_PER = BK / SC_BLK;                   // scale bytes per row and step
     // 4-bit weights in 256-wide steps go straight to LDS like the tokens:
     // code rows of 128 bytes (8 rows per 1 KB load) and their scale bytes
-    // (4 bytes per lane, [row][SC_PER] in LDS).  With WD_ (MXFP4, 64-wide
-    // steps) the code rows of 32 bytes go straight to LDS too (32 rows per
-    // load) and the tile's block scales, whole rows of K/32 bytes, are read
-    // into LDS once when the tile starts.  Otherwise, in 64-wide steps, they
-    // are staged through registers.
+    // (4 bytes per lane, [row][SC_PER] in LDS).  With WD_ (64-wide steps)
+    // the code rows of 32 bytes go straight to LDS too (32 rows per load)
+    // and the tile's block scales, whole rows of K/32 (MXFP4) or K/16
+    // (NVFP4) bytes, are read into LDS once when the tile starts.
+    // Otherwise, in 64-wide steps, they are staged through registers.
     static constexpr bool WDMA = MX && (BK == 256 || WD_);
     static constexpr bool SC_TILE = WDMA && BK == 64;      // scales of the whole K range, per tile
-    static constexpr int SC_ROW = 100;                     // LDS bytes per scale row (K <= 3200)
+    static constexpr int SC_ROW = NV_ ? 176 : 100;         // LDS bytes per scale row (K <= 2816 / 3200)
     static constexpr int CRB = BK / 2;                     // bytes per code row and step
     static constexpr int CCH = CRB / 16;                   // 16-byte chunks per code row
     static constexpr int CROWS = 1024 / CRB;               // code rows per 1 KB load
@@ -198,7 +198,7 @@ struct GemmTile {
     // assume at most one DMA step is issued after them.
     static_assert(!MX || WDMA || NS <= 3, "MXFP4 pipeline depth");
     static_assert(!WDMA || (BN % CROWS == 0 && (SC_TILE || (BN * SC_PER) % 256 == 0)), "whole 4-bit load groups");
-    static_assert(!WD_ || (MX && !NV_ && BK == 64), "per-tile scales: MXFP4 in 64-wide steps");
+    static_assert(!WD_ || (MX && BK == 64), "per-tile scales: 4-bit weights in 64-wide steps");
     // W4A4: both operands are MXFP4 codes loaded like bf16 tiles (128-byte
     // rows = 256 K values per stage, two 16x16x128 scaled MFMA steps).
     static_assert(!A4_ || (!MX && BK == 64), "W4A4 tiles: code rows of 128 bytes");
@@ -797,11 +797,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
                     // at physical chunk kk ^ (r & 7) (128-byte rows) or kk ^
                     // ((r >> 3) & 1) (32-byte rows); the lane's 8 codes are
                     // bytes 4 lk .. 4 lk + 3 of it; scales [row][SC_PER] of
-                    // the stage, or the tile's [row][SC_ROW] from block 2 kt
+                    // the stage, or the tile's [row][SC_ROW] from block SC_PER kt
                     const uint8_t *wrow = reinterpret_cast<const uint8_t *>(Bs[wslot]) + r * G::CRB;
                     const int pch = G::CCH == 8 ? kk ^ (r & 7) : kk ^ ((r >> 3) & 1);
                     const uint32_t codes = *reinterpret_cast<const uint32_t *>(wrow + (pch << 4) + 4 * lk);
-                    const uint8_t *srow = G::SC_TILE ? Ss[0] + r * G::SC_ROW + 2 * kt : Ss[wslot] + r * G::SC_PER;
+                    const uint8_t *srow =
+                        G::SC_TILE ? Ss[0] + r * G::SC_ROW + G::SC_PER * kt : Ss[wslot] + r * G::SC_PER;
                     if (NV) {
                         wf[j] = e2m1x8_times_scale(codes, e4m3_to_f32(srow[2 * kk + (lk >> 1)]));
                     } else {
@@ -920,9 +921,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
     if constexpr (G::SC_TILE) {
         constexpr int TPR = NT / BN, MAXW = (G::SC_ROW / 2 + TPR - 1) / TPR;
         static_assert(NT % BN == 0, "whole threads per scale row");
-        const int v = tid % BN, w0 = tid / BN, nh = K / 64;
+        const int v = tid % BN, w0 = tid / BN, nh = K / (2 * G::SC_BLK);   // 16-bit words per scale row
         const uint16_t *srow = reinterpret_cast<const uint16_t *>(
-            g_scales + ((size_t)e * g_w_rows + weight_row(v)) * (size_t)(K / 32));
+            g_scales + ((size_t)e * g_w_rows + weight_row(v)) * (size_t)(K / G::SC_BLK));
         uint16_t sv[MAXW];
 #pragma unroll
         for (int i = 0; i < MAXW; ++i)
@@ -1166,10 +1167,13 @@ static hipError_t launch_sized(const GemmArgs &a, int A, hipStream_t st) {
     // tiles, step 376 -> 295 us; 1024 tokens, 256- instead of 64-row tiles,
     // 398 -> 336 us).
     if (mean_rows <= 40) return launch_cfg<64, 128, 2, 2, MODE, MX, 2, 64, false, NV>(a, A, st);
-    if constexpr (MX && !NV) {
-        // MXFP4 codes straight to LDS (16-byte aligned rows of K/2 bytes)
-        // with the tile's scale rows (K/32 bytes, 2-byte aligned, at most
-        // SC_ROW) read into LDS once: no register staging in the K loop.
+    if constexpr (MX) {
+        // 4-bit codes straight to LDS (16-byte aligned rows of K/2 bytes)
+        // with the tile's scale rows (K/32 E8M0 or K/16 E4M3 bytes, 2-byte
+        // aligned, at most SC_ROW) read into LDS once: no register staging in
+        // the K loop (NVFP4 weights and activations at 2048 tokens: layer step
+        // 625 -> 521 us, gate/up 368 -> 289 us, down 198 -> 165 us against
+        // the register route in eight waves).
         // Waves 4 x 4: each weight fragment is expanded by four waves, but
         // two waves per SIMD multiply at <= 128 rows (2 x 8 waves, two
         // expansions per fragment: 217 us; 4 x 4: 194 us for the gate/up at
@@ -1180,12 +1184,12 @@ static hipError_t launch_sized(const GemmArgs &a, int A, hipStream_t st) {
         // gate/up 201 -> 187 us (six) and 192 us (four), down 122.5 ->
         // 120.4 us (four) and 125.5 us (six).
         constexpr int NSB = MODE == kGateUp ? 6 : 4;
-        using Tile = GemmTile<256, 256, 4, 4, MODE, MX, 2, 64, false, false, true, NSB>;
+        using Tile = GemmTile<256, 256, 4, 4, MODE, MX, 2, 64, false, NV, true, NSB>;
         const bool direct = (reinterpret_cast<uintptr_t>(a.w) & 15u) == 0 &&
                             (reinterpret_cast<uintptr_t>(a.scales) & 1u) == 0 && a.K >= 128 &&
-                            a.K / 32 <= Tile::SC_ROW;
+                            a.K / Tile::SC_BLK <= Tile::SC_ROW;
         if (direct && a.sh_rows == 0)
-            return launch_cfg<256, 256, 4, 4, MODE, MX, 2, 64, false, false, true, NSB>(a, A, st);
+            return launch_cfg<256, 256, 4, 4, MODE, MX, 2, 64, false, NV, true, NSB>(a, A, st);
     }
     if constexpr (!MX)
         return launch_cfg<256, 256, 4, 4, MODE, MX, 2, 64, false, NV, false, 3>(a, A, st);
