@@ -54,7 +54,9 @@ def parse():
     p.add_argument("--extra-steps", type=int, default=30)
     p.add_argument("--extra-warmup", type=int, default=5)
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                   help="only run a device copy of MIB mebibytes (counter calibration) and exit")
+                   help="only run a device copy of MIB mebibytes (counter calibration, copy bandwidth) and exit")
+    p.add_argument("--vendor-gemm", action="store_true",
+                   help="only time the vendor library's bf16 matmul on the layer's expert shapes (context) and exit")
     return p.parse_args()
 
 
@@ -410,6 +412,42 @@ def measure(config, K, warmup, rotate, full):
     return res, inp
 
 
+def vendor_gemm():
+    """The vendor library's bf16 matmul (torch.bmm / torch.matmul, hipBLASLt)
+    on the layer's expert shapes, for context: 128 experts x R rows each
+    (batched, contiguous operands, no gather, no GEGLU epilogue) for the
+    gate/up (K 2816 -> 1408) and down (K 704 -> 2816) products, and the same
+    totals as one dense matrix.  TFLOP/s from HIP events over 20 calls."""
+    import torch
+    out = {}
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def time(f, flops):
+        f()
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(20):
+            f()
+        end.record()
+        torch.cuda.synchronize()
+        us = start.elapsed_time(end) / 20 * 1e3
+        return {"us": round(us, 1), "tflops": round(flops / (us * 1e-6) / 1e12, 1)}
+
+    for R in (128, 512):
+        for name, K, N in (("gateup", 2816, 1408), ("down", 704, 2816)):
+            a = torch.randn(128, R, K, device="cuda", dtype=torch.bfloat16)
+            w = torch.randn(128, K, N, device="cuda", dtype=torch.bfloat16)   # [E][K][N]: contiguous right operand
+            out[f"bmm_{name}_128x{R}"] = time(lambda: torch.bmm(a, w), 2.0 * 128 * R * K * N)
+            del a, w
+    for name, K, N in (("gateup", 2816, 1408), ("down", 704, 2816)):
+        a = torch.randn(16384, K, device="cuda", dtype=torch.bfloat16)
+        w = torch.randn(K, N, device="cuda", dtype=torch.bfloat16)
+        out[f"dense_{name}_16384"] = time(lambda: torch.matmul(a, w), 2.0 * 16384 * K * N)
+        del a, w
+    torch.cuda.empty_cache()
+    return {"vendor_gemm": out}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -420,14 +458,26 @@ def main():
     import torch
 
     if args.copy_calibration:
+        # a device-to-device copy of known size: the counters' bytes per
+        # copied byte, and the bandwidth a plain copy reaches (read + write)
         n = args.copy_calibration << 20
         a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
         b = torch.empty_like(a)
         torch.cuda.synchronize()
+        b.copy_(a)
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
         for _ in range(3):
             b.copy_(a)
+        end.record()
         torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
+        ms = start.elapsed_time(end) / 3
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 4, "copy_ms": ms,
+                          "copy_read_plus_write_gbs": 2 * n / (ms * 1e-3) / 1e9}))
+        return
+    if args.vendor_gemm:
+        print(json.dumps(vendor_gemm()))
         return
 
     main_res, inp = measure(args.config, args.steps, args.warmup, args.rotate, full=not args.no_graph)
