@@ -32,6 +32,12 @@ SMALL = {
     "one-token": mi.Shape(T=1, H=256, E=8, k=2, I=128),
     "k-equals-E": mi.Shape(T=40, H=256, E=8, k=8, I=128),
     "many-experts": mi.Shape(T=130, H=256, E=300, k=6, I=64),
+    # the supported maximum of experts and of experts per token together
+    "max-E-and-k": mi.Shape(T=64, H=256, E=1024, k=32, I=64),
+    # one expert, top-1: the layer degenerates to a dense GEGLU FFN
+    "single-expert": mi.Shape(T=50, H=256, E=1, k=1, I=128),
+    # one token of the Gemma-4 layer (a single decode step)
+    "one-token-model": mi.Shape(T=1, H=2816, E=128, k=8, I=704),
 }
 
 
