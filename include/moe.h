@@ -210,8 +210,9 @@ int moe_combine(const moe_shape *s, const uint16_t *y, const int32_t *inv,
 
 /*
  * moe_forward -- the whole layer: route, permute (without materialising
- * x_perm: the gate/up GEMM gathers x rows itself), gate/up + GEGLU, down,
- * combine, all on `stream`, with a launch grid that depends only on the
+ * x_perm: the gate/up GEMM gathers x rows itself), gate/up + GEGLU, down
+ * (its rows stored in (token, slot) order, so the combine needs no inv
+ * lookup), combine, all on `stream`, with a launch grid that depends only on the
  * shape (never on routing counts), no host synchronisation and no
  * device-to-host copy.
  *   weights and scales as for the steps above

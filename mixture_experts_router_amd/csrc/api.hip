@@ -265,9 +265,10 @@ static int forward_launch(const moe_shape *s, const uint16_t *x, const uint16_t 
         if (st != MOE_OK || (st = mark()) != MOE_OK) return st;
         st = hip_status(moe::launch_quantize_mx(w.h, A, I, w.hq, w.hs, hs));
         if (st == MOE_OK)
-            st = hip_status(moe::launch_down_a4(w.hq, w.hs, w.offsets, w_down, d_scales, w.y, A, H, E, I, hs));
+            st = hip_status(
+                moe::launch_down_a4(w.hq, w.hs, w.offsets, w_down, d_scales, w.y, w.sorted_ids, A, H, E, I, hs));
         if (st != MOE_OK || (st = mark()) != MOE_OK) return st;
-        st = hip_status(moe::launch_combine(w.y, w.inv, wts, nullptr, 0, out, T, H, k, hs));
+        st = hip_status(moe::launch_combine(w.y, nullptr, wts, nullptr, 0, out, T, H, k, hs));
         if (st != MOE_OK) return st;
         return mark();
     }
@@ -290,10 +291,12 @@ static int forward_launch(const moe_shape *s, const uint16_t *x, const uint16_t 
     if (st != MOE_OK || (st = mark()) != MOE_OK) return st;
     if (nv_a4 && (st = hip_status(moe::launch_quantize_nv(w.h, A, I, dn.input, nullptr, nullptr, w.h, hs))) != MOE_OK)
         return st;
-    st = hip_status(moe::launch_down(w.h, w.offsets, w_down, dn.scales, dn.global, dn.input, w.y, A, H, E, I, dn.fmt,
-                                     I_sh > 0 ? &sh_d : nullptr, hs));
+    // y in (token, slot) order: the combine reads each token's k rows
+    // without a lookup of their positions first
+    st = hip_status(moe::launch_down(w.h, w.offsets, w_down, dn.scales, dn.global, dn.input, w.y, w.sorted_ids, A, H,
+                                     E, I, dn.fmt, I_sh > 0 ? &sh_d : nullptr, hs));
     if (st != MOE_OK || (st = mark()) != MOE_OK) return st;
-    st = hip_status(moe::launch_combine(w.y, w.inv, wts, w.y_sh32, I_sh > 0 ? moe::shared_splits(I_sh, I) : 0, out,
+    st = hip_status(moe::launch_combine(w.y, nullptr, wts, w.y_sh32, I_sh > 0 ? moe::shared_splits(I_sh, I) : 0, out,
                                         T, H, k, hs));
     if (st != MOE_OK) return st;
     return mark();
@@ -407,8 +410,8 @@ int moe_grouped_gemm_down(const moe_shape *s, const uint16_t *h, const int32_t *
     if ((st = check_weights(s, w_down, d_scales)) != MOE_OK) return st;
     if (s->w_format == MOE_W_MXFP4_A4 || s->w_format == MOE_W_NVFP4_A4) return MOE_ERR_UNSUPPORTED;
     const WeightView wv = weight_view(s, d_scales);
-    return hip_status(moe::launch_down(h, offsets, w_down, wv.scales, wv.global, nullptr, y, s->T * s->k, s->H, s->E,
-                                       s->I, wv.fmt, nullptr, static_cast<hipStream_t>(stream)));
+    return hip_status(moe::launch_down(h, offsets, w_down, wv.scales, wv.global, nullptr, y, nullptr, s->T * s->k,
+                                       s->H, s->E, s->I, wv.fmt, nullptr, static_cast<hipStream_t>(stream)));
 }
 
 int moe_combine(const moe_shape *s, const uint16_t *y, const int32_t *inv, const float *topk_w,

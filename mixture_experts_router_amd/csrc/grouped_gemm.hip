@@ -84,10 +84,14 @@ struct GemmArgs {
     const float *a_global;
     // Row-tile groups run last to first on each XCD (large row blocks only)
     int reverse_groups;
+    // Routed output rows: grouped row r is stored at out row out_rows[r]
+    // (the down GEMM of the whole layer passes sorted_ids, so y lands in
+    // (token, slot) order), or at row r when nullptr
+    const int32_t *out_rows;
     // Buffer extents in bytes, for the bounds checks of the MOE_DEBUG build:
     // the routed group's (or the router's) operands and output, then the
     // shared group's.
-    size_t a_bytes, gather_bytes, w_bytes, s_bytes, out_bytes, a_s_bytes;
+    size_t a_bytes, gather_bytes, w_bytes, s_bytes, out_bytes, a_s_bytes, out_rows_bytes;
     size_t sh_a_bytes, sh_w_bytes, sh_s_bytes, sh_out_bytes;
 };
 
@@ -902,6 +906,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
             wait_vm_lgkm0_rt(kt + NSB - 2 < KT ? dmab_per_step : 0);
         }
     };
+    // Output rows of this lane's token rows when the output is scattered
+    // (loaded before the first loads of the pipeline, so that they are older
+    // than every load its wait counts cover).
+    const bool out_map = !ROUTER && !shared && p.out_rows != nullptr;
+    int out_row[MI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+        const int t = wm * WTM + i * 16 + lrow;
+        out_row[i] = out_map && t < rows ? *MOE_CHECKED(p.out_rows + seg + t, 4, p.out_rows, p.out_rows_bytes) : 0;
+    }
     if (MX && !WDMA) issue_mx(0);
     if (A4) {
         load_scales(0);
@@ -984,7 +998,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
     for (int i = 0; i < MI; ++i) {
         const int t = wm * WTM + i * 16 + lrow;
         if (t >= rows) continue;
-        uint16_t *orow = g_out + (size_t)(seg + t) * g_n_out;
+        uint16_t *orow = g_out + (size_t)(out_map ? out_row[i] : seg + t) * g_n_out;
         if (ROUTER) {
             float *lrow_out = p.out32 + (size_t)(seg + t) * p.n_out;
 #pragma unroll
@@ -1236,9 +1250,12 @@ constexpr long long kLastLevelCacheBytes = 256LL << 20;
 static int reverse_down_groups(int A, int H) { return (long long)A * H * 2 > kLastLevelCacheBytes ? 1 : 0; }
 
 hipError_t launch_down_a4(const uint8_t *hq, const uint8_t *hs, const int32_t *offsets, const void *w,
-                          const uint8_t *scales, uint16_t *y, int A, int H, int E, int I, hipStream_t st) {
+                          const uint8_t *scales, uint16_t *y, const int32_t *out_rows, int A, int H, int E, int I,
+                          hipStream_t st) {
     GemmArgs a{reinterpret_cast<const uint16_t *>(hq), nullptr, 1, offsets, w, scales, y, E, I, H, I, H, 0, 0, 0,
                nullptr, nullptr};
+    a.out_rows = out_rows;
+    a.out_rows_bytes = (size_t)A * 4;
     a.a_scales = hs;
     a.a_bytes = (size_t)A * I / 2;
     a.a_s_bytes = (size_t)A * I / 32;
@@ -1287,9 +1304,11 @@ hipError_t launch_gateup(const uint16_t *x, const int32_t *sorted_ids, int k, co
 }
 
 hipError_t launch_down(const uint16_t *h, const int32_t *offsets, const void *w, const uint8_t *scales,
-                       const float *w_global, const float *a_global, uint16_t *y, int A, int H, int E, int I,
-                       WeightFormat fmt, const SharedGroup *sh, hipStream_t st) {
+                       const float *w_global, const float *a_global, uint16_t *y, const int32_t *out_rows, int A,
+                       int H, int E, int I, WeightFormat fmt, const SharedGroup *sh, hipStream_t st) {
     GemmArgs a{h, nullptr, 1, offsets, w, scales, y, E, I, H, I, H, 0, 0, 0, nullptr, nullptr};
+    a.out_rows = out_rows;
+    a.out_rows_bytes = (size_t)A * 4;
     a.w_global = w_global;
     a.a_global = a_global;
     a.reverse_groups = reverse_down_groups(A, H);

@@ -157,15 +157,17 @@ __device__ __forceinline__ float gelu_tanh(float z) {
 }
 
 // One 16-byte output chunk of the weighted combine: out[t][c..c+7] =
-// (sum_s y_sh32[s][t][c..c+7], if given) + sum_{j<k} w[t*k+j] *
-// y[inv[t*k+j]][c..c+7]: fp32 adds over s in order, then fp32 fmas in
-// ascending j, one bf16 rounding.  Each y row is read exactly once, so its
-// loads carry the non-temporal hint (Zipf-skewed 8192 tokens: 81 -> 78 us).
+// (sum_s y_sh32[s][t][c..c+7], if given) + sum_{j<k} w[t*k+j] * y[r_j][c..c+7]
+// with r_j = inv[t*k+j] (y in expert order) or t*k+j (inv == nullptr: y in
+// (token, slot) order, so the row loads need no index load first): fp32
+// adds over s in order, then fp32 fmas in ascending j, one bf16 rounding.
+// Each y row is read exactly once, so its loads carry the non-temporal hint
+// (Zipf-skewed 8192 tokens: 81 -> 78 us).
 __device__ __forceinline__ void combine_chunk(const uint16_t *__restrict__ y, const int32_t *__restrict__ inv,
                                               const float *__restrict__ w, const float *__restrict__ y_sh32,
                                               int nsplit, uint16_t *__restrict__ out, int t, int c, int T, int H,
                                               int k) {
-    const int32_t *ti = inv + (size_t)t * k;
+    const int32_t *ti = inv ? inv + (size_t)t * k : nullptr;
     const float *tw = w + (size_t)t * k;
     float acc[8];
 #pragma unroll
@@ -184,8 +186,9 @@ __device__ __forceinline__ void combine_chunk(const uint16_t *__restrict__ y, co
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int j = min(j0 + u, k - 1);
-            v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
-                MOE_CHECKED(y + (size_t)ti[j] * H + c, 16, y, (size_t)T * k * H * 2)));
+            const size_t row = ti ? (size_t)ti[j] : (size_t)t * k + j;
+            v[u] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4 *>(MOE_CHECKED(y + row * H + c, 16, y, (size_t)T * k * H * 2)));
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
