@@ -95,61 +95,50 @@ __device__ __forceinline__ void permute_in_block(const int32_t *ids, int A, int 
         for (int a0 = 0; a0 < A; a0 += kChunk) rank_chunk(ids, a0, min(A, a0 + kChunk), h, nbits, sorted_ids, inv, A);
 }
 
-// Histogram, exclusive scan and stable scatter of A <= 64 assignments by one
-// wave, lane a holding assignment a.  One pass over the id bits, high to
-// low, gives both the number of assignments with a smaller expert id (the
-// expert's start) and the mask of lanes with the same id (the stable rank
-// within it).  h (>= E ints of LDS, zero on entry) receives the counts.
-// Each lane then scans C = ceil(E / 64) <= 16 consecutive experts.
-template <int C>
-__device__ __forceinline__ void permute_wave(const int32_t *ids, int A, int E, int nbits, int *h,
-                                             int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
-                                             int32_t *__restrict__ sorted_ids, int32_t *__restrict__ inv) {
-    const int lane = threadIdx.x & 63;
+// Histogram, exclusive scan and stable scatter of A <= 64 assignments
+// (ids[a] for a < A, all below 2^NBITS) by a block of E or more threads, from
+// the bit planes of the ids: one ballot per bit, taken by every wave (no LDS
+// beyond the ids).  For a value v, a walk over the planes from the highest
+// bit down keeps the lanes whose ids agree with v on the bits seen so far;
+// at each bit set in v, the kept lanes with that bit clear hold smaller ids.
+// So the walk gives the number of ids below v (an expert's start) and the
+// lanes whose id equals v (its count, and an assignment's stable rank: its
+// equals in lower lanes).  Thread i walks expert i; lane a of every wave also
+// walks the id of assignment a, and wave 0 stores that rank.  The two walks
+// are independent chains without branches, so they run interleaved.
+template <int NBITS>
+__device__ __forceinline__ void permute_ids_block(const int32_t *ids, int A, int E, int32_t *__restrict__ counts,
+                                                  int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_ids,
+                                                  int32_t *__restrict__ inv) {
+    const int tid = threadIdx.x, lane = tid & 63;
     const bool valid = lane < A;
     const int id = valid ? ids[lane] : 0;
-    uint64_t m = __ballot(valid);   // valid lanes whose id agrees on the bits seen so far
-    int less = 0;
-    for (int b = nbits - 1; b >= 0; --b) {
-        const bool bit = (id >> b) & 1;
-        const uint64_t ones = __ballot(valid && bit);
-        if (bit) less += __popcll(m & ~ones);
-        m &= bit ? ones : ~ones;
+    const uint64_t all = __ballot(valid);
+    uint64_t plane[NBITS];
+#pragma unroll
+    for (int b = 0; b < NBITS; ++b) plane[b] = __ballot(valid && ((id >> b) & 1));
+    uint64_t me = all, ma = all;   // lanes agreeing with expert tid / with this lane's id
+    int less_e = 0, less_a = 0;
+#pragma unroll
+    for (int b = NBITS - 1; b >= 0; --b) {
+        const uint64_t p = plane[b];
+        const bool be = (tid >> b) & 1, ba = (id >> b) & 1;
+        less_e += be ? __popcll(me & ~p) : 0;
+        less_a += ba ? __popcll(ma & ~p) : 0;
+        me &= be ? p : ~p;
+        ma &= ba ? p : ~p;
     }
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    if (valid) {
-        const int pos = less + __popcll(m & below);
+    if (tid < E) {
+        counts[tid] = __popcll(me);
+        offsets[tid] = less_e;
+    }
+    if (tid == 0) offsets[E] = A;
+    if (tid < 64 && valid) {
+        const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+        const int pos = less_a + __popcll(ma & below);
         *MOE_CHECKED(sorted_ids + pos, 4, sorted_ids, (size_t)A * 4) = lane;
         *MOE_CHECKED(inv + lane, 4, inv, (size_t)A * 4) = pos;
-        if ((m >> lane) == 1ull) h[id] = __popcll(m);   // highest lane of its expert group
     }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    int c[C];
-    int tot = 0;
-#pragma unroll
-    for (int q = 0; q < C; ++q) {
-        const int e = lane * C + q;
-        c[q] = e < E ? h[e] : 0;
-        tot += c[q];
-    }
-    int incl = tot;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int v = __shfl_up(incl, d, 64);
-        if (lane >= d) incl += v;
-    }
-    int run = incl - tot;
-#pragma unroll
-    for (int q = 0; q < C; ++q) {
-        const int e = lane * C + q;
-        if (e < E) {
-            counts[e] = c[q];
-            offsets[e] = run;
-        }
-        run += c[q];
-    }
-    if (lane == 0) offsets[E] = A;
 }
 
 }  // namespace moe

@@ -167,14 +167,13 @@ __device__ __forceinline__ void topk_token(int t, const float *__restrict__ part
 #pragma unroll
         for (int i = 1; i < VPL; ++i) lm = max(lm, key[i]);
         const uint32_t km = wave_max_u32(lm);
+        // the lowest expert index holding km: the lowest lane of the lowest
+        // i with a hit (scalar selects, no branch per i)
         int sel = 0;
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) {
+        for (int i = VPL - 1; i >= 0; --i) {
             const uint64_t hit = __ballot(key[i] == km);
-            if (hit) {
-                sel = 64 * i + (int)__builtin_ctzll(hit);
-                break;
-            }
+            sel = hit ? 64 * i + (int)__builtin_ctzll(hit) : sel;
         }
 #pragma unroll
         for (int i = 0; i < VPL; ++i)
@@ -211,7 +210,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ par
 // expert histogram, its scan and the stable scatter of the assignments, all
 // from the routing table kept in LDS (it never makes a round trip through
 // global memory before the scatter).  Up to 64 assignments the permutation
-// is one wave's work.
+// comes from the ballots of the ids' bit planes, one expert per thread.
 template <int VPL>
 __device__ __forceinline__ void topk_permute_block(const float *__restrict__ part, int nchunks,
                                                    const float *__restrict__ bias, float *__restrict__ logits,
@@ -225,7 +224,9 @@ __device__ __forceinline__ void topk_permute_block(const float *__restrict__ par
     for (int t = wave; t < T; t += 16) topk_token<VPL>(t, part, nchunks, bias, logits, ids, wts, T, E, k, s_ids);
     __syncthreads();
     if (A <= 64) {
-        if (wave == 0) permute_wave<VPL>(s_ids, A, E, nbits, h, counts, offsets, sorted_ids, inv);
+        // ids below 64 VPL = 2^(6 + log2 VPL)
+        constexpr int NBITS = 6 + (VPL >= 2) + (VPL >= 4) + (VPL >= 8) + (VPL >= 16);
+        permute_ids_block<NBITS>(s_ids, A, E, counts, offsets, sorted_ids, inv);
     } else {
         permute_in_block(s_ids, A, E, nbits, h, sh, counts, offsets, sorted_ids, inv);
     }

@@ -23,6 +23,10 @@ SHAPES = {
     "wide-experts": mi.Shape(T=2, H=256, E=1024, k=32, I=64),        # 16 logits per lane
     "odd-experts": mi.Shape(T=40, H=768, E=300, k=6, I=64),          # 3 chunks of 256, partial expert block
     "skew-bias": mi.Shape(T=16, H=512, E=128, k=8, I=64, skew=True),
+    # one-wave permutation (A <= 64) at other expert counts
+    "one-wave-odd-experts": mi.Shape(T=9, H=256, E=300, k=7, I=64),   # A = 63, five experts per lane
+    "single-expert": mi.Shape(T=5, H=256, E=1, k=1, I=64),             # no id bits at all
+    "one-wave-hot": mi.Shape(T=8, H=256, E=16, k=8, I=64, skew=True),  # half the experts per token, skewed
 }
 
 
@@ -47,7 +51,25 @@ def _staged(d, s):
     moe.gemm_down(sh, h, offsets, d["w_d"], d["d_s"], y)
     moe.combine(sh, y, inv, w, out)
     torch.cuda.synchronize()
-    return out, ids, w
+    return out, ids, w, (counts, offsets, sorted_ids, inv)
+
+
+def _ws_tables(ws, sh, s):
+    """The fused kernel's counts, offsets, sorted_ids and inv inside the
+    moe_forward workspace.  White-box: the offsets follow the workspace carve
+    of csrc/api.hip (256-byte aligned pieces: completion counter, router
+    partials, logits, ids, weights, counts, offsets, block histograms,
+    sorted_ids, inv, ...)."""
+    up = lambda n: (n + 255) // 256 * 256
+    A = s.T * s.k
+    off = WS_ZERO_BYTES + moe.route_workspace_bytes(sh)
+    off += up(s.T * s.E * 4) + up(A * 4) + up(A * 4)          # logits, ids, weights
+    views = []
+    for n, skip in ((s.E, 0), (s.E + 1, 0), (A, moe.permute_workspace_bytes(sh)), (A, 0)):
+        off += skip
+        views.append(ws[off:off + 4 * n].view(torch.int32))
+        off += up(4 * n)
+    return views
 
 
 @pytest.mark.parametrize("name", list(SHAPES))
@@ -60,7 +82,11 @@ def test_fused_routing_matches_staged_path(gpu, name):
     for call in range(3):      # the counter must reset itself between calls
         out, ids, w = run_forward(inp, d, ws)
         assert int(ws[:WS_ZERO_BYTES].count_nonzero()) == 0, f"counter not reset after call {call}"
-    o2, i2, w2 = _staged(d, s)
+    o2, i2, w2, tables = _staged(d, s)
+    # the whole permutation of the fused kernel, bitwise (moe_forward itself
+    # reads only offsets and sorted_ids)
+    for got, want, what in zip(_ws_tables(ws, d["shape"], s), tables, ("counts", "offsets", "sorted_ids", "inv")):
+        assert torch.equal(got, want), what
     assert torch.equal(ids, i2)
     assert torch.equal(w.view(torch.int32), w2.view(torch.int32))
     assert (dev.bf16_bits(out) == dev.bf16_bits(o2)).all()
