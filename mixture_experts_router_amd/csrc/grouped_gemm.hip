@@ -778,94 +778,107 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
     // needed two steps later.
     constexpr bool SPREAD = NSB > NS;
     constexpr int GAP = (KK * MI * NI) / (B_W > 0 ? B_W : 1) > 0 ? (KK * MI * NI) / (B_W > 0 ? B_W : 1) : 1;
+    // Operand fragments of MFMA K step kk (32 values) of step kt: weight
+    // rows (expanded from 4-bit codes for 4-bit weights) and token rows.
+    auto frag_w = [&](int kt, int kk, int j) -> u32x4 {
+        const int wslot = kt % NSB;
+        const int ch = A4 ? 2 * lk + kk : kk * 4 + lk;
+        const int r = wn * WN + j * 16 + lrow;
+        if (WDMA) {
+            // code row r of the stage: logical chunk kk (32 codes)
+            // at physical chunk kk ^ (r & 7) (128-byte rows) or kk ^
+            // ((r >> 3) & 1) (32-byte rows); the lane's 8 codes are
+            // bytes 4 lk .. 4 lk + 3 of it; scales [row][SC_PER] of
+            // the stage, or the tile's [row][SC_ROW] from block SC_PER kt
+            const uint8_t *wrow = reinterpret_cast<const uint8_t *>(Bs[wslot]) + r * G::CRB;
+            const int pch = G::CCH == 8 ? kk ^ (r & 7) : kk ^ ((r >> 3) & 1);
+            const uint32_t codes = *reinterpret_cast<const uint32_t *>(wrow + (pch << 4) + 4 * lk);
+            const uint8_t *srow = G::SC_TILE ? Ss[0] + r * G::SC_ROW + G::SC_PER * kt : Ss[wslot] + r * G::SC_PER;
+            if (NV) return e2m1x8_times_scale(codes, e4m3_to_f32(srow[2 * kk + (lk >> 1)]));
+            const float sc = __uint_as_float((uint32_t)srow[kk] << 23);
+            u32x4 v;
+            v[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 0));
+            v[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 1));
+            v[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 2));
+            v[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 3));
+            return v;
+        } else if (MX && NV) {
+            // E2M1 -> bf16 at scale 1, then times the block's E4M3
+            // scale: the product has at most 6 significant bits, so
+            // it is exactly a bf16 value (the lane's 8 codes are K
+            // 8 ch .. 8 ch + 7, block 2 kk + lk / 2 of the step)
+            const uint32_t codes = reinterpret_cast<const uint32_t *>(Bs[wslot])[ch * BN + r];
+            const float sc = e4m3_to_f32(Ss[wslot][(2 * kk + (lk >> 1)) * BN + r]);
+            return e2m1x8_times_scale(codes, sc);
+        } else if (MX) {
+            const uint32_t codes = reinterpret_cast<const uint32_t *>(Bs[wslot])[ch * BN + r];
+            const float sc = __uint_as_float((uint32_t)Ss[wslot][kk * BN + r] << 23);
+            u32x4 v;
+            v[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 0));
+            v[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 1));
+            v[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 2));
+            v[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 3));
+            return v;
+        } else {
+            return *reinterpret_cast<const u32x4 *>(&Bs[wslot][r * BK + tswz<BK>(r, ch) * 8]);
+        }
+    };
+    auto frag_x = [&](int kt, int kk, int i) -> u32x4 {
+        const int ch = A4 ? 2 * lk + kk : kk * 4 + lk;
+        const int r = wm * WTM + i * 16 + lrow;
+        return *reinterpret_cast<const u32x4 *>(&As[kt % NS][r * BK + tswz<BK>(r, ch) * 8]);
+    };
+    // The MFMAs of K step kk, with this wave's spread weight loads of step
+    // kt_b (if kt_b >= 0) issued among them.
+    auto mfma_kk = [&](int kk, const u32x4 *wf, const u32x4 *xf, int kt_b) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NI; ++j) {
+                acc[j][i] = mfma16x16x32(wf[j], xf[i], acc[j][i]);
+                if constexpr (SPREAD) {
+                    const int idx = (kk * MI + i) * NI + j;
+                    if (kt_b >= 0 && idx % GAP == GAP - 1 && idx / GAP < B_W) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        issue_bq(kt_b, idx / GAP);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+            }
+    };
     auto compute = [&](int kt, int kt_b) {
-        const int slot = kt % NS, wslot = kt % NSB;
-        constexpr int NSW = A4 ? NI / 2 : 1, NSX = A4 ? (G::SC_PAIR_M ? MI / 2 : MI) : 1;
-        uint32_t sw[NSW], sx[NSX];
-        if (A4) {
+        const int slot = kt % NS;
+        if constexpr (A4) {
+            constexpr int NSW = NI / 2, NSX = G::SC_PAIR_M ? MI / 2 : MI;
+            uint32_t sw[NSW], sx[NSX];
 #pragma unroll
             for (int q = 0; q < NSW; ++q) sw[q] = read_sw(slot, q);
 #pragma unroll
             for (int q = 0; q < NSX; ++q) sx[q] = read_sx(slot, q);
-        }
-        // Per MFMA K step of 32: the fragments, then the MFMAs.
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            const int ch = A4 ? 2 * lk + kk : kk * 4 + lk;
-            u32x4 wf[NI], xf[MI];
+            for (int kk = 0; kk < KK; ++kk) {
+                u32x4 wf[NI], xf[MI];
 #pragma unroll
-            for (int j = 0; j < NI; ++j) {
-                const int r = wn * WN + j * 16 + lrow;
-                if (WDMA) {
-                    // code row r of the stage: logical chunk kk (32 codes)
-                    // at physical chunk kk ^ (r & 7) (128-byte rows) or kk ^
-                    // ((r >> 3) & 1) (32-byte rows); the lane's 8 codes are
-                    // bytes 4 lk .. 4 lk + 3 of it; scales [row][SC_PER] of
-                    // the stage, or the tile's [row][SC_ROW] from block SC_PER kt
-                    const uint8_t *wrow = reinterpret_cast<const uint8_t *>(Bs[wslot]) + r * G::CRB;
-                    const int pch = G::CCH == 8 ? kk ^ (r & 7) : kk ^ ((r >> 3) & 1);
-                    const uint32_t codes = *reinterpret_cast<const uint32_t *>(wrow + (pch << 4) + 4 * lk);
-                    const uint8_t *srow =
-                        G::SC_TILE ? Ss[0] + r * G::SC_ROW + G::SC_PER * kt : Ss[wslot] + r * G::SC_PER;
-                    if (NV) {
-                        wf[j] = e2m1x8_times_scale(codes, e4m3_to_f32(srow[2 * kk + (lk >> 1)]));
-                    } else {
-                        const float sc = __uint_as_float((uint32_t)srow[kk] << 23);
-                        u32x4 v;
-                        v[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 0));
-                        v[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 1));
-                        v[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 2));
-                        v[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 3));
-                        wf[j] = v;
-                    }
-                } else if (MX && NV) {
-                    // E2M1 -> bf16 at scale 1, then times the block's E4M3
-                    // scale: the product has at most 6 significant bits, so
-                    // it is exactly a bf16 value (the lane's 8 codes are K
-                    // 8 ch .. 8 ch + 7, block 2 kk + lk / 2 of the step)
-                    const uint32_t codes = reinterpret_cast<const uint32_t *>(Bs[wslot])[ch * BN + r];
-                    const float sc = e4m3_to_f32(Ss[wslot][(2 * kk + (lk >> 1)) * BN + r]);
-                    wf[j] = e2m1x8_times_scale(codes, sc);
-                } else if (MX) {
-                    const uint32_t codes = reinterpret_cast<const uint32_t *>(Bs[wslot])[ch * BN + r];
-                    const float sc = __uint_as_float((uint32_t)Ss[wslot][kk * BN + r] << 23);
-                    u32x4 v;
-                    v[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 0));
-                    v[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 1));
-                    v[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 2));
-                    v[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 3));
-                    wf[j] = v;
-                } else {
-                    wf[j] = *reinterpret_cast<const u32x4 *>(&Bs[wslot][r * BK + tswz<BK>(r, ch) * 8]);
-                }
-            }
+                for (int j = 0; j < NI; ++j) wf[j] = frag_w(kt, kk, j);
 #pragma unroll
-            for (int i = 0; i < MI; ++i) {
-                const int r = wm * WTM + i * 16 + lrow;
-                xf[i] = *reinterpret_cast<const u32x4 *>(&As[slot][r * BK + tswz<BK>(r, ch) * 8]);
-            }
-            if constexpr (A4) {
+                for (int i = 0; i < MI; ++i) xf[i] = frag_x(kt, kk, i);
 #pragma unroll
                 for (int i = 0; i < MI; ++i)
 #pragma unroll
                     for (int j = 0; j < NI; ++j)
                         acc[j][i] = mfma_fp4x128(wf[j], xf[i], acc[j][i], sw[j / 2], sx[G::SC_PAIR_M ? i / 2 : i],
                                                  2 * (j & 1) + kk, (G::SC_PAIR_M ? 2 * (i & 1) : 0) + kk);
-            } else {
+            }
+        } else {
+            // Per MFMA K step of 32: the fragments, then the MFMAs.
 #pragma unroll
-                for (int i = 0; i < MI; ++i)
+            for (int kk = 0; kk < KK; ++kk) {
+                u32x4 wf[NI], xf[MI];
 #pragma unroll
-                    for (int j = 0; j < NI; ++j) {
-                        acc[j][i] = mfma16x16x32(wf[j], xf[i], acc[j][i]);
-                        if constexpr (SPREAD) {
-                            const int idx = (kk * MI + i) * NI + j;
-                            if (kt_b >= 0 && idx % GAP == GAP - 1 && idx / GAP < B_W) {
-                                __builtin_amdgcn_sched_barrier(0);
-                                issue_bq(kt_b, idx / GAP);
-                                __builtin_amdgcn_sched_barrier(0);
-                            }
-                        }
-                    }
+                for (int j = 0; j < NI; ++j) wf[j] = frag_w(kt, kk, j);
+#pragma unroll
+                for (int i = 0; i < MI; ++i) xf[i] = frag_x(kt, kk, i);
+                mfma_kk(kk, wf, xf, kt_b);
             }
         }
     };
@@ -909,7 +922,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
     // Output rows of this lane's token rows when the output is scattered
     // (loaded before the first loads of the pipeline, so that they are older
     // than every load its wait counts cover).
-    const bool out_map = !ROUTER && !shared && p.out_rows != nullptr;
+    const bool out_map = MODE == kDown && !shared && p.out_rows != nullptr;
     int out_row[MI];
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
