@@ -10,6 +10,7 @@ constexpr int kChunk = 1024;           // assignments per permutation block
 constexpr int kSmallRouteMaxA = 2048;  // fused few-token top-k + permutation: T*k up to this
 
 constexpr int kRouterSplitMaxT = 64;   // split-K router (chunk partials) up to this many tokens
+constexpr int kFusedRouteMaxT = 16;    // single-launch routing up to this many tokens (one per wave)
 
 int router_chunks(int H);
 bool router_uses_partials(int T);
@@ -23,8 +24,9 @@ hipError_t launch_router_dense(const uint16_t *x, const uint16_t *wr, const floa
 // from final logits (part == nullptr).
 hipError_t launch_topk(const float *part, int nchunks, const float *bias, float *logits, int32_t *ids,
                        float *w, int T, int E, int k, hipStream_t st);
-// Few tokens (route_permute_fits): router chunk sums, top-k and the whole
-// permutation (counts, offsets, sorted_ids, inv) in one launch.  `done` is a
+// Few tokens (route_permute_fits: T <= kFusedRouteMaxT): router chunk sums,
+// top-k and the whole permutation (counts, offsets, sorted_ids, inv) in one
+// launch.  `done` is a
 // completion counter that must be zero before the launch; it is zero again
 // after it.
 bool route_permute_fits(int T, int k);

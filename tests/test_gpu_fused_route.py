@@ -1,8 +1,10 @@
-"""The single-launch few-token routing of moe_forward (router chunk sums,
-then -- in the last block to finish -- top-k and permutation) against the
-stage-by-stage C ABI path (moe_route, moe_permute, the two grouped GEMMs,
-moe_combine) on the same inputs: routing, weights and output must agree
-bitwise, and the completion counter must be back to zero after every call."""
+"""The routing inside moe_forward -- up to 16 tokens the single-launch
+routing (router chunk sums, then, in the last block to finish, top-k and
+permutation), above that the staged launches -- against the stage-by-stage C
+ABI path (moe_route, moe_permute, the two grouped GEMMs, moe_combine) on the
+same inputs: routing, weights, the permutation tables and the output must
+agree bitwise, and the completion counter must be back to zero after every
+call."""
 import numpy as np
 import pytest
 import torch
@@ -19,9 +21,10 @@ WS_ZERO_BYTES = 256   # MOE_WS_ZERO_BYTES in include/moe.h
 SHAPES = {
     "decode-like": mi.Shape(T=8, H=512, E=128, k=8, I=128),          # 64 assignments: one-wave permutation
     "one-token": mi.Shape(T=1, H=256, E=8, k=1, I=64),
-    "64-tokens": mi.Shape(T=64, H=512, E=64, k=8, I=128),            # 4 token tiles, block permutation
+    "64-tokens": mi.Shape(T=64, H=512, E=64, k=8, I=128),            # above 16 tokens: the staged routing
     "wide-experts": mi.Shape(T=2, H=256, E=1024, k=32, I=64),        # 16 logits per lane
-    "odd-experts": mi.Shape(T=40, H=768, E=300, k=6, I=64),          # 3 chunks of 256, partial expert block
+    "odd-experts": mi.Shape(T=40, H=768, E=300, k=6, I=64),          # staged: 3 chunks of 256, partial expert block
+    "odd-experts-one-launch": mi.Shape(T=12, H=768, E=300, k=6, I=64),  # A = 72: block permutation, 3 chunks
     "skew-bias": mi.Shape(T=16, H=512, E=128, k=8, I=64, skew=True),
     # one-wave permutation (A <= 64) at other expert counts
     "one-wave-odd-experts": mi.Shape(T=9, H=256, E=300, k=7, I=64),   # A = 63, five experts per lane
