@@ -224,7 +224,7 @@ struct GemmTile {
     static_assert(!A4_ || (NI % 2 == 0 && (!SC_PAIR_M || MI % 2 == 0)), "W4A4: scale rows in pairs");
     // a deeper weight ring: two token stages and three or more weight stages
     // (bf16 tiles, or 4-bit codes straight to LDS)
-    static_assert(NSB == NS || (NSB > NS && !A4_ && (!MX || WDMA)), "weight ring deeper than the token ring");
+    static_assert(NSB == NS || (NS == 2 && NSB >= 3 && !A4_ && (!MX || WDMA)), "weight ring deeper than the token ring");
     // LDS: token stages, weight stages, block scales (4-bit weights), W4A4
     // scale pairs, carved from one buffer (byte offsets, 16-byte aligned)
     static constexpr int A_OFF = 0;
@@ -907,20 +907,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
     // step s (s < NS - 1) and then the weight tile of step s (s < NSB - 1);
     // step kt issues the token tile of kt + NS - 1, then the weight tile of
     // kt + NSB - 1.  At the top of step kt the loads issued after the last
-    // one it needs are: NSB == NS: the NS - 2 later steps' loads; NSB > NS
-    // (the weight tile of kt went out in an earlier step than the token tile
-    // of kt, in step kt - NS + 1): the weight tiles of steps kt + NSB - NS ..
-    // kt + NSB - 2 and the token tiles of steps kt + 1 .. kt + NS - 2, those
-    // below KT.  (In the first NS - 1 steps this waits for more than it
-    // needs: the prologue's later weight tiles.)
+    // one it needs are: NSB == NS: the NS - 2 later steps' loads; NS = 2,
+    // NSB > 2: the weight tile of kt + NSB - 2, issued (in step kt - 1)
+    // right after the token tile of kt.  (In step 0 this waits for more than
+    // it needs: the prologue's later weight tiles.)
     auto wait_for = [&](int kt) {
         if constexpr (NSB == NS) {
             const int later = min(NS - 2, KT - 1 - kt);   // steps issued after kt
             wait_vm_lgkm0_rt(later * dma_per_step);
         } else {
-            const int na_later = max(0, min(NS - 2, KT - 1 - kt));
-            const int nb_later = max(0, min(kt + NSB - 2, KT - 1) - (kt + NSB - NS) + 1);
-            wait_vm_lgkm0_rt(na_later * (dma_per_step - dmab_per_step) + nb_later * dmab_per_step);
+            wait_vm_lgkm0_rt(kt + NSB - 2 < KT ? dmab_per_step : 0);
         }
     };
     // Output rows of this lane's token rows when the output is scattered
