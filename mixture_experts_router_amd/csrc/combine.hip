@@ -1,5 +1,6 @@
-// Weighted combine: out[t] = sum_{j<k} w[t, j] * y[inv[t*k + j]], summed in
-// fp32 in ascending j and rounded to bf16 once.  This is the local-expert sum
+// Weighted combine: out[t] = sum_{j<k} w[t, j] * y[inv[t*k + j]] (y in expert
+// order), or y[t*k + j] (y in (token, slot) order, as the whole layer stores
+// it), summed in fp32 in ascending j and rounded to bf16 once.  This is the local-expert sum
 // that the decode path of the pages all-reduces across expert-parallel
 // ranks (Gemma-4-26B-A4B optimisation report, section 6.1, MoE row).  Each
 // output element is owned by one lane, so there are no atomics and the

@@ -24,8 +24,9 @@ namespace moe {
 constexpr int kRouteChunk = 256;   // K per fp32 chunk sum (8 MFMA steps)
 
 // ---------------------------------------------------------------- few tokens
-// Split-K: one wave owns (16 experts, chunk c, 16 tokens), issues all 16
-// loads of its chunk at once and writes the fp32 chunk sums part[c][t][e].
+// Split-K: one wave owns (16 experts, chunk c, 16 tokens), issues all its
+// loads of the chunk at once (the token rows past T are not read) and
+// writes the fp32 chunk sums part[c][t][e].
 // Many small waves stream the router weight in one memory round trip.
 __device__ __forceinline__ void router_partial_wave(const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
                                                     float *__restrict__ part, int T, int H, int E, int etile,
