@@ -451,8 +451,8 @@ def vendor_gemm():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: the layer holds all experts on one device and this "
-              f"build has no multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
+        print(f"bench.py measures one GPU only: the layer holds all experts on one device and the "
+              f"library has no multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
 
     import torch
