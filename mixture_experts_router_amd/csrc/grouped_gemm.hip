@@ -1185,6 +1185,14 @@ static hipError_t launch_sized(const GemmArgs &a, int A, hipStream_t st) {
             if (a.sh_rows == 0 && aligned && a.K >= 1024)
                 return launch_cfg<16, 128, 1, 4, MODE, MX, 3, 256, false, NV>(a, A, st);
         }
+        // With the shared group (three K ranges x 22 column tiles of the
+        // dense MLP's down) the 128-column down tiles of a decode step
+        // outnumber the 1024 slots of four workgroups per CU, and the last
+        // ones run alone; 192-column tiles (three per CU) fit one round
+        // (measured, 8 tokens with the 2112-wide MLP: step 116.5 -> 111.6
+        // us, down 41.0 -> 36.3 us; without the MLP no change).
+        if constexpr (MODE == kDown && !MX)
+            if (a.sh_rows > 0) return launch_cfg<16, 192, 1, 4, MODE, MX, 2, 64, false, NV>(a, A, st);
         return launch_cfg<16, 128, 1, 4, MODE, MX, 2, 64, false, NV>(a, A, st);
     }
     // Above 16: the row tile holds a typical expert's rows whole (mean plus
