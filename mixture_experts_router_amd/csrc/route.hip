@@ -59,17 +59,16 @@ __device__ __forceinline__ void router_partial_wave(const uint16_t *__restrict__
     const int t = ttile * 16 + r;
     if (t < T) {
         const int e0 = etile * 16 + 4 * g;
-        float *dst = MOE_CHECKED(part + ((size_t)c * T + t) * E + e0, 4, part,
-                                 (size_t)((H + kRouteChunk - 1) / kRouteChunk) * T * E * 4);
+        float *row = part + ((size_t)c * T + t) * E;
+        [[maybe_unused]] const size_t ext = (size_t)((H + kRouteChunk - 1) / kRouteChunk) * T * E * 4;
         // one 16-byte store where aligned (a 16-byte aligned buffer and E a
         // multiple of 4, so every row starts at a multiple of 4 floats)
         if (E % 4 == 0 && e0 + 3 < E && (reinterpret_cast<uintptr_t>(part) & 15u) == 0) {
-            *reinterpret_cast<f32x4 *>(MOE_CHECKED(dst, 16, part,
-                                                   (size_t)((H + kRouteChunk - 1) / kRouteChunk) * T * E * 4)) = acc;
+            *reinterpret_cast<f32x4 *>(MOE_CHECKED(row + e0, 16, part, ext)) = acc;
         } else {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                if (e0 + q < E) dst[q] = acc[q];
+                if (e0 + q < E) *MOE_CHECKED(row + e0 + q, 4, part, ext) = acc[q];
         }
     }
 }
