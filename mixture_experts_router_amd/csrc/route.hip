@@ -184,7 +184,9 @@ __device__ __forceinline__ void topk_token(int t, const float *__restrict__ part
 #pragma unroll
         for (int i = VPL - 1; i >= 0; --i) {
             const uint64_t hit = __ballot(key[i] == km);
-            sel = hit ? 64 * i + (int)__builtin_ctzll(hit) : sel;
+            // (bit 63 keeps the count defined for an empty mask, whose
+            // result is not selected, and changes no nonzero one)
+            sel = hit ? 64 * i + (int)__builtin_ctzll(hit | (1ull << 63)) : sel;
         }
 #pragma unroll
         for (int i = 0; i < VPL; ++i)
