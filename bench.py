@@ -55,6 +55,8 @@ def parse():
     p.add_argument("--extra-warmup", type=int, default=5)
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a device copy of MIB mebibytes (counter calibration, copy bandwidth) and exit")
+    p.add_argument("--stream-probe", action="store_true",
+                   help="only time the load-only streaming probes (libmoe_probe.so) and exit")
     p.add_argument("--vendor-gemm", action="store_true",
                    help="only time the vendor library's bf16 matmul on the layer's expert shapes (context) and exit")
     return p.parse_args()
@@ -448,6 +450,66 @@ def vendor_gemm():
     return {"vendor_gemm": out}
 
 
+def stream_probe(launches=20):
+    """The load-only streaming probes of libmoe_probe.so: a plain stream and
+    the byte streams of the decode GEMMs' launch shapes, with no arithmetic,
+    and the LDS read rate (16 waves per CU, conflict-free 16-byte reads).
+    Each probe reads its bytes from one of four regions of a device buffer in
+    turn (each region at least as large as the 256 MB Infinity Cache, so no
+    launch finds its bytes there); us per launch from HIP events around
+    `launches` back-to-back launches on the launch stream."""
+    import ctypes
+
+    import torch
+    path = os.path.join(ROOT, "mixture_experts_router_amd", "libmoe_probe.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built (python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(path)
+    lib.moe_probe_name.restype = ctypes.c_char_p
+    lib.moe_probe_name.argtypes = [ctypes.c_int]
+    lib.moe_probe_bytes.restype = ctypes.c_size_t
+    lib.moe_probe_bytes.argtypes = [ctypes.c_int]
+    lib.moe_probe_footprint.restype = ctypes.c_size_t
+    lib.moe_probe_footprint.argtypes = [ctypes.c_int]
+    lib.moe_probe_launch.restype = ctypes.c_int
+    lib.moe_probe_launch.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                     ctypes.c_void_p]
+    kinds = range(lib.moe_probe_count())
+    region = max(max(lib.moe_probe_footprint(k) for k in kinds), 256 << 20)
+    region = (region + (1 << 20) - 1) >> 20 << 20
+    buf = torch.ones(4 * region, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def launch(k, i):
+        rc = lib.moe_probe_launch(k, buf.data_ptr() + (i % 4) * region, region, sink.data_ptr(),
+                                  stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"moe_probe_launch({k}) returned {rc}")
+
+    out = []
+    for k in kinds:
+        for i in range(4):
+            launch(k, i)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(launches):
+            launch(k, i)
+        end.record(stream)
+        torch.cuda.synchronize()
+        us = start.elapsed_time(end) / launches * 1e3
+        nbytes = lib.moe_probe_bytes(k)
+        out.append({"probe": lib.moe_probe_name(k).decode(), "bytes": nbytes, "us": round(us, 2),
+                    "tb_per_s": round(nbytes / (us * 1e-6) / 1e12, 3)})
+        if lib.moe_probe_footprint(k) == 0:   # the LDS probe: bytes per clock and CU at 2.4 GHz
+            out[-1]["bytes_per_clk_per_cu_at_2p4ghz"] = round(nbytes / (us * 1e-6) / 2.4e9 / 256, 1)
+        print(json.dumps(out[-1]), flush=True)
+    del buf, sink
+    torch.cuda.empty_cache()
+    return {"stream_probe": out, "launches": launches}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -478,6 +540,9 @@ def main():
         return
     if args.vendor_gemm:
         print(json.dumps(vendor_gemm()))
+        return
+    if args.stream_probe:
+        print(json.dumps(stream_probe()))
         return
 
     main_res, inp = measure(args.config, args.steps, args.warmup, args.rotate, full=not args.no_graph)

@@ -39,15 +39,22 @@ def asan_runtime() -> str:
 # The bounds-checked build of the kernels (include/moe_debug.h).
 DEBUG_LIB = os.path.join(HERE, "libmoe_debug.so")
 
+# The load-only streaming probes (csrc/stream_probe.hip), a library of their
+# own that the layer never loads; bench.py --stream-probe times them.
+PROBE_LIB = os.path.join(HERE, "libmoe_probe.so")
+PROBE_SOURCES = ["stream_probe.hip"]
 
-def build(verbose: bool = False, hostsan: bool = False, debug: bool = False) -> str:
+
+def build(verbose: bool = False, hostsan: bool = False, debug: bool = False, probe: bool = False) -> str:
     """Compile every HIP source into mixture_experts_router_amd/libmoe.so
     (hostsan: into libmoe_hostsan.so with sanitised host code; debug: into
-    libmoe_debug.so with the kernels' bounds checks)."""
-    out = HOSTSAN_LIB if hostsan else (DEBUG_LIB if debug else LIB)
+    libmoe_debug.so with the kernels' bounds checks; probe: the streaming
+    probes into libmoe_probe.so)."""
+    out = PROBE_LIB if probe else (HOSTSAN_LIB if hostsan else (DEBUG_LIB if debug else LIB))
     tmp = out + ".tmp"
     extra = (HOSTSAN_FLAGS if hostsan else []) + (["-DMOE_DEBUG"] if debug else [])
-    cmd = [HIPCC, *FLAGS, *extra, "-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
+    srcs = PROBE_SOURCES if probe else SOURCES
+    cmd = [HIPCC, *FLAGS, *extra, "-o", tmp] + [os.path.join(CSRC, s) for s in srcs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -280,3 +280,41 @@ def test_debug_header_and_exports():
     dbg, rel = names(b.DEBUG_LIB), names(_lib.LIB_PATH)
     assert "moe_debug_bounds" in dbg and "moe_debug_bounds" not in rel
     assert set(_lib.EXPORTS) <= dbg
+
+
+def test_probe_header_and_exports():
+    """include/moe_probe.h declares the streaming probes of libmoe_probe.so:
+    the library exports exactly those, names and sizes every kind, and
+    rejects bad arguments before any HIP call."""
+    from mixture_experts_router_amd import build as b
+    text = open(os.path.join(ROOT, "include", "moe_probe.h")).read()
+    decl = sorted(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(moe_\w+)\s*\(", text, re.M))
+    assert decl == ["moe_probe_bytes", "moe_probe_count", "moe_probe_footprint", "moe_probe_launch",
+                    "moe_probe_name"]
+    if not os.path.exists(b.PROBE_LIB):
+        pytest.skip("libmoe_probe.so not built")
+    p = ctypes.CDLL(b.PROBE_LIB)
+    for n in decl:
+        assert hasattr(p, n)
+    p.moe_probe_name.restype = ctypes.c_char_p
+    p.moe_probe_bytes.restype = ctypes.c_size_t
+    p.moe_probe_footprint.restype = ctypes.c_size_t
+    p.moe_probe_launch.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+    n = p.moe_probe_count()
+    assert n >= 1
+    for k in range(n):
+        assert p.moe_probe_name(k) and p.moe_probe_bytes(k) >= p.moe_probe_footprint(k)
+        assert p.moe_probe_bytes(k) > 0
+    assert p.moe_probe_name(n) is None and p.moe_probe_bytes(n) == 0 and p.moe_probe_bytes(-1) == 0
+    assert p.moe_probe_footprint(n) == 0
+    big = p.moe_probe_footprint(0)
+    assert big == p.moe_probe_bytes(0)
+    assert p.moe_probe_launch(n, FAKE, big, FAKE, None) == -1          # unknown kind
+    assert p.moe_probe_launch(0, None, big, FAKE, None) == -1          # no buffer
+    assert p.moe_probe_launch(0, FAKE, big, None, None) == -1          # no sink
+    assert p.moe_probe_launch(0, FAKE, big - 1, FAKE, None) == -1      # short buffer
+    assert p.moe_probe_launch(0, MIS, big, FAKE, None) == -1           # misaligned buffer
+    # the layer library does not carry the probes
+    rel = ctypes.CDLL(_lib.LIB_PATH)
+    assert not hasattr(rel, "moe_probe_launch")
