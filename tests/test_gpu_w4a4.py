@@ -63,6 +63,10 @@ A4 = {
     "mid-tiles-a4": mi.Shape(T=120, H=512, E=16, k=4, I=192, mxfp4=True, a4=True),    # mean 30: 64-row tiles
     "ragged-a4": mi.Shape(T=300, H=512, E=16, k=4, I=192, mxfp4=True, a4=True),      # mean 75: 256-row tiles
     "big-tiles-a4": mi.Shape(T=600, H=512, E=16, k=4, I=320, mxfp4=True, a4=True),   # 256-row tiles
+    # 256-row tiles with half a 256-wide K step in all (K = 128) and a gate/up
+    # that ends in a half step (H = 576)
+    "short-k-a4": mi.Shape(T=400, H=128, E=8, k=2, I=64, mxfp4=True, a4=True),       # mean 100
+    "odd-k-a4": mi.Shape(T=600, H=576, E=16, k=4, I=320, mxfp4=True, a4=True),
     "decode-like-a4": mi.Shape(T=8, H=768, E=64, k=8, I=704, mxfp4=True, a4=True),   # the model's I
     # the Gemma-4 layer at 300 tokens (mean 19): 64-row tiles with the model's
     # K (gate/up 2816 = 11 steps of 256, down 704 = 2.75 steps)
