@@ -726,8 +726,21 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
         }
     }
     uint32_t sc_v[2];   // the step's 8 bytes, in flight between load and store
+    // Scale rows of whole 8-byte words (K % 256 == 0, so no partial stage;
+    // both scale buffers 8-byte aligned) take one 8-byte load per row and
+    // step, others four 2-byte loads: one load instruction of a wave touches
+    // up to 64 rows' cache lines, so the narrow form quadruples the requests
+    // (measured, W4A4 gate/up at 2048 tokens: 94.1 -> 83.2 us).
+    const bool sc_wide = (nblk & 7) == 0 &&
+                         ((reinterpret_cast<uintptr_t>(g_scales) | reinterpret_cast<uintptr_t>(p.a_scales)) & 7u) == 0;
     auto load_scales = [&](int kt) {
         if (sc_dst < 0) return;
+        if (sc_wide) {
+            const uint2 v = *reinterpret_cast<const uint2 *>(MOE_CHECKED(sc_src + 8 * kt, 8, sc_base, sc_bytes));
+            sc_v[0] = v.x;
+            sc_v[1] = v.y;
+            return;
+        }
         // blocks past the row (last, partial stage) re-read its last pair;
         // they only scale zeros.  nblk = K/32 is even (K % 64 == 0).
         uint32_t h[4];
