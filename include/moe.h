@@ -67,7 +67,9 @@
  *     E <= 1024, T*k < 2^30.  Pointers to bf16 arrays, x_perm, h and y must
  *     be 16-byte aligned (W4A4 weight codes too), the other arrays 4-byte
  *     aligned (MXFP4 scales: any address, 2-byte aligned for W4A4; NVFP4
- *     scale buffers 4-byte aligned).
+ *     scale buffers 4-byte aligned).  W4A4 gate/up weight scales that are
+ *     8-byte aligned, with H % 256 == 0, are read 8 bytes per row and step
+ *     (faster; the results are the same bits).
  */
 #ifndef MOE_H
 #define MOE_H
